@@ -1,0 +1,215 @@
+"""Pins of the CPU oracle's building blocks against facts fixed outside it.
+
+Each test checks one oracle function against something other than itself:
+the format's bit-field definition, IEEE bit patterns, hand-worked examples
+stored under tests/golden/ (with the passage they come from), library routines
+(torch's bf16 cast, scipy's softmax/expit) or brute force.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import bruteforce as bf
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _e2m1_bitfields(code):
+    # OCP E2M1: 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit; exponent 0 is subnormal.
+    s, e, m = (code >> 3) & 1, (code >> 1) & 3, code & 1
+    mag = m / 2 if e == 0 else 2.0 ** (e - 1) * (1 + m / 2)
+    return -mag if s else mag
+
+
+def test_e2m1_table_matches_bit_fields():
+    for code in range(16):
+        v = float(oracle.e2m1_to_float(np.array([code]))[0])
+        assert v == _e2m1_bitfields(code)
+        assert math.copysign(1.0, v) == (-1.0 if code & 8 else 1.0), code
+    mags = np.abs(oracle.e2m1_to_float(np.arange(16)))
+    assert mags.max() == 6.0  # the encoder section: everything above 6.0 clamps
+
+
+def test_e8m0_matches_ieee_exponent_field():
+    s = np.arange(256)
+    got = oracle.e8m0_to_float(s)
+    # IEEE binary32 with exponent field s and zero fraction is 2**(s-127) for 1 <= s <= 254;
+    # s = 0 is below the normal range: 2**-127 is the subnormal with fraction bit 22 set.
+    want = (s[1:255].astype(np.uint32) << 23).view(np.float32)
+    assert np.array_equal(got[1:255], want)
+    assert got[0] == np.array([0x00400000], dtype=np.uint32).view(np.float32)[0]
+    assert got[0] == 2.0 ** -127
+    assert np.isnan(got[255])
+
+
+def test_dequant_exhaustive_codes_scales_nibble_positions():
+    # row s carries scale s; byte i holds code i in the low nibble and code 15-i in the high nibble
+    byte_row = np.array([(i & 0xF) | ((15 - i) << 4) for i in range(16)], dtype=np.uint8)
+    packed = np.tile(byte_row, (256, 1))
+    scales = np.arange(256, dtype=np.uint8).reshape(256, 1)
+    got = oracle.dequantize(packed, scales)
+    assert got.shape == (256, 32) and got.dtype == np.float32
+    for s in range(256):
+        for col in range(32):
+            code = (col // 2) if col % 2 == 0 else 15 - col // 2
+            v = got[s, col]
+            if s == 255:
+                assert np.isnan(v)
+                continue
+            want = np.float32(math.ldexp(_e2m1_bitfields(code), s - 127)) if abs(
+                math.ldexp(_e2m1_bitfields(code), s - 127)) < 3.5e38 else np.float32(
+                math.copysign(math.inf, _e2m1_bitfields(code)))
+            assert v == want and np.signbit(v) == np.signbit(want), (s, col, v, want)
+
+
+def test_nibble_order_golden(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "mxfp4_format.json")))
+    for ex in g["nibble_examples"]:
+        row = np.zeros((1, 16), dtype=np.uint8)
+        row[0, 0] = ex["byte"]
+        got = oracle.dequantize(row, np.array([[ex["scale"]]], dtype=np.uint8))[0, :2]
+        for v, w in zip(got, ex["values"]):
+            assert v == w and np.signbit(v) == np.signbit(np.float32(w)), ex
+
+
+def test_nibble_order_agrees_with_lane_map(golden_dir):
+    # The pages' lane map: nibble plane p of 16-bit lane i carries element 4i+p of the chunk.
+    g = json.load(open(os.path.join(golden_dir, "mxfp4_format.json")))["lane_map"]
+    rng = np.random.default_rng(3)
+    chunk = rng.integers(0, 256, size=g["chunk"] // 2, dtype=np.uint8)
+    codes = oracle.unpack_codes(chunk)
+    lanes = chunk.view("<u2")
+    for i, lane in enumerate(lanes):
+        for p in range(g["planes"]):
+            assert (int(lane) >> (4 * p)) & 0xF == codes[4 * i + p]
+
+
+def test_scale_indexing_one_block_per_row():
+    rng = np.random.default_rng(5)
+    rows, cols = 6, 128
+    packed = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    base = np.full((rows, cols // 32), 127, dtype=np.uint8)
+    ref = oracle.dequantize(packed, base)
+    for n in range(rows):
+        blk = (n * 3 + 1) % (cols // 32)
+        sc = base.copy()
+        sc[n, blk] = 129
+        got = oracle.dequantize(packed, sc)
+        changed = got != ref
+        expect = np.zeros_like(changed)
+        expect[n, blk * 32:(blk + 1) * 32] = ref[n, blk * 32:(blk + 1) * 32] != 0
+        assert np.array_equal(changed, expect)
+        assert np.array_equal(got[n, blk * 32:(blk + 1) * 32], ref[n, blk * 32:(blk + 1) * 32] * 4)
+
+
+def test_bf16_rounding_matches_torch_cast():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal(20000).astype(np.float32) * np.float32(1000)
+    bits = rng.integers(0, 2 ** 32, size=20000, dtype=np.uint64).astype(np.uint32)
+    v2 = bits.view(np.float32)
+    v2 = v2[np.isfinite(v2)]
+    # exact ties: low 16 bits = 0x8000, with even and odd kept parts
+    ties = ((rng.integers(0x3F00, 0x4100, size=2000, dtype=np.uint32) << 16) | 0x8000).view(np.float32)
+    special = np.array([0.0, -0.0, np.inf, -np.inf, 3.3961776e38, -3.3961776e38, 1e-40, -1e-40,
+                        1.17549435e-38, 2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -135], dtype=np.float32)
+    allv = np.concatenate([v, v2, ties, special]).astype(np.float32)
+    got = oracle.round_to_bf16(allv)
+    want = torch.from_numpy(allv).to(torch.bfloat16).to(torch.float32).numpy()
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all(), allv[~same][:10]
+    assert np.array_equal(np.signbit(got[np.isfinite(got)]), np.signbit(want[np.isfinite(want)]))
+
+
+def test_bf16_rounding_float64_is_direct():
+    # fp64 input rounds once: 1 + 2^-8 + 2^-30 lies just above the tie and must round up,
+    # whereas rounding through fp32 first would land on the tie and round to even (down).
+    v = np.array([1.0 + 2.0 ** -8 + 2.0 ** -30], dtype=np.float64)
+    assert oracle.round_to_bf16(v)[0] == 1.0 + 2.0 ** -7
+    assert oracle.round_to_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
+
+
+def test_routing_golden(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "routing_examples.json")))
+    for case in g["cases"]:
+        l = np.array([case["logits"]], dtype=np.float32)
+        ids, w = oracle.route_topk(l, case["top_k"], case["scoring"], dtype=np.float64)
+        assert ids.dtype == np.int32
+        assert ids[0].tolist() == case["ids"], case
+        if "weights" in case:
+            assert np.allclose(w[0], case["weights"], rtol=1e-12, atol=0)
+    ids, w = oracle.route_topk(np.array([[1.0, 3.0, 2.0]], np.float32), 2, "softmax", dtype=np.float64)
+    e = math.exp(-1.0)
+    assert np.allclose(w[0], [1 / (1 + e), e / (1 + e)], rtol=1e-14)
+
+
+def test_routing_against_library_and_bruteforce():
+    sp = pytest.importorskip("scipy.special")
+    rng = np.random.default_rng(11)
+    for scoring in ("softmax", "sigmoid"):
+        for E, k in ((8, 2), (32, 4), (128, 4), (256, 8), (384, 8)):
+            # quantise to force ties
+            logits = (np.round(rng.standard_normal((16, E)) * 4) / 4).astype(np.float32)
+            ids, w = oracle.route_topk(logits, k, scoring, dtype=np.float64)
+            for t in range(16):
+                assert ids[t].tolist() == bf.topk_by_argmax([float(v) for v in logits[t]], k)
+                assert len(set(ids[t].tolist())) == k
+                sel = logits[t, ids[t]].astype(np.float64)
+                rest = np.delete(logits[t], ids[t])
+                assert sel.min() >= rest.max()
+                if scoring == "softmax":
+                    want = sp.softmax(sel)
+                else:
+                    want = sp.expit(sel) / sp.expit(sel).sum()
+                assert np.allclose(w[t], want, rtol=1e-12)
+                assert abs(w[t].sum() - 1) < 1e-12
+            # float32 weights are within a few ulps of the fp64 ones and sum to 1
+            _, w32 = oracle.route_topk(logits, k, scoring, dtype=np.float32)
+            assert np.allclose(w32, w, rtol=2e-6)
+            assert np.all(np.abs(w32.sum(axis=1, dtype=np.float64) - 1) < 1e-6)
+
+
+def test_bucketing_against_bruteforce():
+    rng = np.random.default_rng(13)
+    for E_g, E_l, off, k, T in ((8, 8, 0, 2, 4), (256, 32, 64, 8, 32), (384, 48, 336, 8, 257),
+                                (128, 128, 0, 4, 1), (32, 32, 0, 4, 0)):
+        ids = np.stack([rng.choice(E_g, size=k, replace=False) for _ in range(T)]).astype(np.int32) \
+            if T else np.zeros((0, k), np.int32)
+        if T:
+            ids[rng.random(ids.shape) < 0.1] = -1
+        counts, offsets, routes = oracle.bucket_routes(ids, E_l, off)
+        flat = ids.reshape(-1)
+        bf_routes = []
+        for e in range(E_l):  # O(E * R) scan
+            mine = [r for r in range(flat.size) if flat[r] == e + off]
+            assert counts[e] == len(mine)
+            bf_routes += mine
+        assert routes.tolist() == bf_routes
+        assert offsets[0] == 0 and offsets[-1] == len(routes)
+        assert np.array_equal(np.diff(offsets), counts)
+        assert routes.dtype == np.int32 and counts.dtype == np.int32
+
+
+def test_activation_closed_forms():
+    f32 = np.float32
+    # SwiGLU-OAI: gate capped at 7 (upper only), up clamped to +-7, then g*sigmoid(1.702 g)*(u+1)
+    a = oracle.activation(np.array([10.0]), np.array([-9.0]), "swiglu_oai")[0]
+    assert a == pytest.approx(7 * (1 / (1 + math.exp(-1.702 * 7))) * (-6), rel=1e-14)
+    a = oracle.activation(np.array([-3.0]), np.array([2.5]), "swiglu_oai")[0]
+    assert a == pytest.approx(-3 / (1 + math.exp(1.702 * 3)) * 3.5, rel=1e-14)
+    a = oracle.activation(np.array([1.0]), np.array([9.0]), "swiglu_oai", alpha=1.702, limit=7.0)[0]
+    assert a == pytest.approx(1 / (1 + math.exp(-1.702)) * 8, rel=1e-14)
+    # SiLU * up
+    assert oracle.activation(np.array([0.0]), np.array([5.0]), "silu_mul")[0] == 0.0
+    a = oracle.activation(np.array([2.0]), np.array([-0.5]), "silu_mul")[0]
+    assert a == pytest.approx(2 / (1 + math.exp(-2)) * -0.5, rel=1e-14)
+    # sigmoid saturates to exactly 1 in fp32 above ~17: SiLU(g) == g exactly
+    g = np.array([64.0, 96.0, 17.5], dtype=f32)
+    assert np.array_equal(oracle.activation(g, np.ones(3, f32), "silu_mul"), g)
+    # a very negative gate gives -0 / 0, never NaN
+    assert np.isfinite(oracle.activation(np.array([-200.0], f32), np.array([3.0], f32), "silu_mul")).all()
