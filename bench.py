@@ -1,0 +1,275 @@
+"""Benchmark of the MXFP4 MoE decode layer on one MI355X.
+
+Metric: MoE decode us/call and achieved HBM GB/s on the bytes of the touched
+experts, at T = 1..32 tokens per call.  Default workload: the gpt-oss-20b-shaped
+layer (K = I = 2880, 32 experts, top-4 softmax, biases, clamped SwiGLU), one
+call at each of T = 1, 4, 16, 32; a "step" is that sweep of four calls.
+
+Method (the pages' per-call method, made robust to the 256 MB Infinity Cache):
+each T gets a HIP graph of `--steps` back-to-back layer calls that rotate over
+L distinct weight replicas and input sets (L chosen so that one rotation moves
+more than 512 MB), replayed once untimed per warmup step and once timed,
+bracketed by HIP events on the launch stream and device synchronisation.
+The same chains of the three steps alone (plan, gate_up, down) give the
+per-kernel times; the gate/up kernel is the dominant one and feeds `roofline`.
+
+Algorithmic bytes of one call: for every touched local expert its packed
+weights and scales (3*I*K*17/32 bytes) plus biases, plus x (2TK), the router
+logits (4*T*E_global) and the output (2TK).  Touched experts and local routes
+are read back from the plan the library writes, so they are the realised ones.
+
+Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--config", default="gptoss20b")
+    p.add_argument("--tokens", default=None, help="comma-separated T values (default: the layer's decode sweep)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--rotate-mb", type=float, default=512.0, help="bytes one replica rotation must exceed")
+    return p.parse_args()
+
+
+class Replica:
+    def __init__(self, torch, cfg, idx, w_np=None):
+        dev = "cuda"
+        K, I, E = cfg.K, cfg.I, cfg.E_local
+        if w_np is not None:
+            def u8(a):
+                return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+            self.w13p, self.w13s = u8(w_np.w13_packed), u8(w_np.w13_scales)
+            self.w2p, self.w2s = u8(w_np.w2_packed), u8(w_np.w2_scales)
+            self.b13 = self.b2 = None
+            if w_np.b13 is not None:
+                self.b13 = torch.from_numpy(w_np.b13.view(np.int16)).to(dev).view(torch.bfloat16)
+                self.b2 = torch.from_numpy(w_np.b2.view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            g = torch.Generator(device=dev)
+            g.manual_seed(1000 * cfg.index + idx)
+            self.w13p = torch.randint(0, 256, (E, 2 * I, K // 2), dtype=torch.uint8, device=dev, generator=g)
+            self.w13s = torch.randint(cfg.scale_lo, cfg.scale_hi + 1, (E, 2 * I, K // 32), dtype=torch.uint8,
+                                      device=dev, generator=g)
+            self.w2p = torch.randint(0, 256, (E, K, I // 2), dtype=torch.uint8, device=dev, generator=g)
+            self.w2s = torch.randint(cfg.scale_lo, cfg.scale_hi + 1, (E, K, I // 32), dtype=torch.uint8,
+                                     device=dev, generator=g)
+            self.b13 = self.b2 = None
+            if cfg.bias:
+                self.b13 = torch.randn((E, 2 * I), device=dev, generator=g).to(torch.bfloat16)
+                self.b2 = torch.randn((E, K), device=dev, generator=g).to(torch.bfloat16)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this layer slice runs on a single MI355X "
+              f"(--gpus {args.gpus} is not supported; expert-parallel sharding is described in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mxfp4_mixture_experts_router_amd as moe
+    from workloads import get_config, make_inputs, make_weights
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = get_config(args.config)
+    tokens = [int(t) for t in args.tokens.split(",")] if args.tokens else [t for t in cfg.tokens if t <= 32] or list(cfg.tokens)
+    K, I = cfg.K, cfg.I
+    per_expert = cfg.bytes_per_expert()
+    w13_per_expert = 2 * I * (K // 2) + 2 * I * (K // 32) + (4 * I if cfg.bias else 0)
+
+    # number of distinct replicas: one rotation must move > rotate_mb of expert bytes at the smallest T
+    t_min = min(tokens)
+    exp_touched = cfg.E_local * (1 - (1 - cfg.top_k / cfg.E_global) ** t_min)
+    L = max(4, math.ceil(args.rotate_mb * 1e6 / max(1.0, exp_touched * per_expert)))
+    L = min(L, args.steps)
+    log(f"config {cfg.name}: tokens {tokens}, replicas {L}, steps {args.steps}, warmup {args.warmup}")
+
+    t0 = time.time()
+    w0 = make_weights(cfg, replica=0)
+    reps = [Replica(torch, cfg, 0, w0)] + [Replica(torch, cfg, i) for i in range(1, L)]
+    torch.cuda.synchronize()
+    log(f"weights ready ({L} x {cfg.E_local} experts) in {time.time() - t0:.1f}s")
+
+    stream = torch.cuda.Stream()
+    results = {}
+    for T in tokens:
+        d = moe.make_desc(T=T, K=K, I=I, E_global=cfg.E_global, E_local=cfg.E_local, top_k=cfg.top_k,
+                          expert_offset=cfg.expert_offset, scoring=cfg.scoring, activation=cfg.activation,
+                          swiglu_alpha=cfg.swiglu_alpha, swiglu_limit=cfg.swiglu_limit)
+        ws_bytes = moe.moe_mxfp4_workspace_bytes(d)
+        inputs = [make_inputs(cfg, T, call=i) for i in range(L)]
+        xs = [torch.from_numpy(inp.x.view(np.int16)).cuda().view(torch.bfloat16) for inp in inputs]
+        lg = [torch.from_numpy(inp.logits).cuda() for inp in inputs]
+        wss = [torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") for _ in range(L)]
+        outs = [torch.empty((T, K), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+
+        def call_decode(i, s):
+            r = reps[i % L]
+            moe.moe_mxfp4_decode(d, xs[i % L], r.w13p, r.w13s, r.w2p, r.w2s, outs[i % L], router_logits=lg[i % L],
+                                 w13_bias=r.b13, w2_bias=r.b2, workspace=wss[i % L], stream=s)
+
+        def call_plan(i, s):
+            moe.moe_mxfp4_plan(d, router_logits=lg[i % L], workspace=wss[i % L], stream=s)
+
+        def call_gate_up(i, s):
+            r = reps[i % L]
+            moe.moe_mxfp4_gate_up(d, xs[i % L], r.w13p, r.w13s, wss[i % L], w13_bias=r.b13, stream=s)
+
+        def call_down(i, s):
+            r = reps[i % L]
+            moe.moe_mxfp4_down(d, r.w2p, r.w2s, outs[i % L], wss[i % L], w2_bias=r.b2, stream=s)
+
+        with torch.cuda.stream(stream):
+            for i in range(L):
+                call_decode(i, stream)
+        stream.synchronize()
+        plan_hdr = [wss[i][:8].view(torch.int32).cpu().tolist() for i in range(L)]
+        touched = [h[0] for h in plan_hdr]
+        routes = [h[1] for h in plan_hdr]
+
+        def chain(fn):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(args.steps):
+                    fn(i, stream)
+            return g
+
+        graphs = {name: chain(fn) for name, fn in
+                  (("decode", call_decode), ("plan", call_plan), ("gate_up", call_gate_up), ("down", call_down))}
+        timing = {}
+        for name, g in graphs.items():
+            with torch.cuda.stream(stream):
+                for _ in range(args.warmup):
+                    g.replay()
+                stream.synchronize()
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            timing[name] = e0.elapsed_time(e1) * 1000.0 / args.steps   # us per call
+        # bytes per call, averaged over the calls of the chain (call i uses replica i % L)
+        calls = [i % L for i in range(args.steps)]
+        bytes_call = np.mean([touched[c] * per_expert + 4 * T * K + 4 * T * cfg.E_global for c in calls])
+        w13_bytes = np.mean([touched[c] * w13_per_expert + 2 * T * K + 2 * routes[c] * I for c in calls])
+        us = timing["decode"]
+        results[T] = dict(
+            us_per_call=round(us, 2), calls_per_s=round(1e6 / us, 1),
+            touched_experts=round(float(np.mean([touched[c] for c in calls])), 2),
+            local_routes=round(float(np.mean([routes[c] for c in calls])), 2),
+            bytes_per_call=int(bytes_call), gbs=round(bytes_call / us / 1e3, 1),
+            pct_peak=round(100 * bytes_call / us / 1e3 / HBM_PEAK_GBS, 1),
+            us_plan=round(timing["plan"], 2), us_gate_up=round(timing["gate_up"], 2),
+            us_down=round(timing["down"], 2), w13_bytes=int(w13_bytes),
+            w13_gbs=round(w13_bytes / timing["gate_up"] / 1e3, 1))
+        log(f"T={T}: {json.dumps(results[T])}")
+        for g in graphs.values():
+            del g
+        del graphs
+        torch.cuda.synchronize()
+
+    step_us = sum(r["us_per_call"] for r in results.values())
+    step_bytes = sum(r["bytes_per_call"] for r in results.values())
+    value = step_bytes / step_us / 1e3
+    # dominant kernel: the gate/up GEMV; one launch per call, same launch count per T
+    w13_avg_us = float(np.mean([r["us_gate_up"] for r in results.values()]))
+    w13_avg_bytes = float(np.mean([r["w13_bytes"] for r in results.values()]))
+    achieved = w13_avg_bytes / w13_avg_us / 1e3
+    line = {
+        "metric": "MoE decode us/call and achieved HBM GB/s (% peak) at T=1..32 tokens",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_us / 1000.0, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4 weights, bf16 activations, fp32 accumulate",
+        "data": "synthetic (seeded random E2M1 codes, E8M0 scales, Gaussian x and logits)",
+        "config": {"workload": f"{cfg.description}; one call at each T in {tokens} per step",
+                   "K": K, "I": I, "E_global": cfg.E_global, "E_local": cfg.E_local, "top_k": cfg.top_k,
+                   "tokens": tokens, "replicas": L, "parallelism": "single GPU"},
+        "pct_peak": round(100 * value / HBM_PEAK_GBS, 1),
+        "per_T": {str(k): v for k, v in results.items()},
+        "roofline": {"kernel": "moe::w13_gemv_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(w13_avg_us, 2),
+                     "algorithmic_bytes_per_launch": int(w13_avg_bytes)},
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, w0, reps[0], torch, moe)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cfg, w0, rep0, torch, moe):
+    """The CPU oracle, as it stands, on a bounded sample: one call at T=1 and one at T=4."""
+    import oracle
+    from workloads import make_inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    total_s, total_bytes, checks = 0.0, 0, {}
+    for T in (1, 4):
+        inp = make_inputs(cfg, T, call=0)
+        t0 = time.perf_counter()
+        ref = oracle.moe_forward_cfg(cfg, w0, inp)
+        dt = time.perf_counter() - t0
+        total_s += dt
+        touched = int((ref["counts"] > 0).sum())
+        total_bytes += touched * cfg.bytes_per_expert() + 4 * T * cfg.K + 4 * T * cfg.E_global
+        # the same call on the device, compared with the oracle
+        d = moe.make_desc(T=T, K=cfg.K, I=cfg.I, E_global=cfg.E_global, E_local=cfg.E_local, top_k=cfg.top_k,
+                          expert_offset=cfg.expert_offset, scoring=cfg.scoring, activation=cfg.activation,
+                          swiglu_alpha=cfg.swiglu_alpha, swiglu_limit=cfg.swiglu_limit)
+        out = torch.empty((T, cfg.K), dtype=torch.bfloat16, device="cuda")
+        moe.moe_mxfp4_decode(d, torch.from_numpy(inp.x.view(np.int16)).cuda().view(torch.bfloat16), rep0.w13p,
+                             rep0.w13s, rep0.w2p, rep0.w2s, out, router_logits=torch.from_numpy(inp.logits).cuda(),
+                             w13_bias=rep0.b13, w2_bias=rep0.b2)
+        torch.cuda.synchronize()
+        y = (out.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+        checks[str(T)] = {"rel_l2": float(f"{oracle.rel_l2(y, ref['y']):.3e}"),
+                          "cosine": float(f"{oracle.cosine(y, ref['y']):.7f}")}
+    return {"value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "us_per_call": round(total_s / 2 * 1e6, 1),
+            "sample": f"numpy oracle (fp32, full dequantise of touched experts, BLAS {cores} threads), "
+                      f"one call at T=1 and one at T=4 of replica 0: {total_s:.1f} s",
+            "parity_vs_gpu": checks}
+
+
+if __name__ == "__main__":
+    main()

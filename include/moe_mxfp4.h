@@ -1,0 +1,215 @@
+/*
+ * moe_mxfp4.h - C ABI of the MI355X (gfx950) routed-expert MXFP4 MoE decode layer.
+ *
+ * One call computes, for one expert-parallel slice of a mixture-of-experts
+ * layer, top-k routing, the fused gate/up projection with its activation, the
+ * down projection and the routing-weighted combine, reading every weight
+ * straight from packed OCP MXFP4.
+ *
+ * Sources (page, section):
+ *  - "MXFP4 MoE decode kernels", Design, Read the served layout: the tensor
+ *    layouts below; The bottleneck: E2M1 values two per byte, one E8M0 scale
+ *    per 32 values; Design, Fused epilogues: bias and activation in fp32, bf16
+ *    intermediate, routing-weighted bias added once per route, fp32 per-token
+ *    sums, bf16 output; Design, Routing inside the kernel: routes are counting
+ *    sorted by local expert and routes to other ranks are skipped; Limitations
+ *    and pitfalls: unsupported inputs are refused with a reason, and unexpected
+ *    dtypes must be rejected.
+ *  - "GLM-5.2 and GLM-5.3 (744B) in MXFP4 on Gaudi 2", What was built,
+ *    Byte-exact repack: E2M1 low nibble first, E8M0 scales, blocks of 32; Why it
+ *    needed a port, items 1, 2 and 4: w13 rows are [gate; up], experts are
+ *    sliced by expert-parallel rank, routing ids are int32.
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers, row-major and contiguous, owned by
+ *    the caller; the library allocates nothing, never synchronises and never
+ *    logs.  Work is enqueued on `stream` (a hipStream_t; NULL is the default
+ *    stream) and runs asynchronously, like a kernel launch.
+ *  - bf16 tensors are passed as uint16_t bit patterns.
+ *  - Every argument check runs on the host before anything is enqueued: on a
+ *    non-zero status nothing has been launched and no output has been written.
+ *  - Status codes are the MOE_* values below; moe_mxfp4_status_string() names
+ *    them.
+ */
+#ifndef MOE_MXFP4_H
+#define MOE_MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define MOE_OK             0
+#define MOE_ERR_NULL      (-1)  /* a required pointer is NULL                          */
+#define MOE_ERR_SHAPE     (-2)  /* a size is out of range (see moe_mxfp4_desc)        */
+#define MOE_ERR_MODE      (-3)  /* both or neither routing input; bad enum value       */
+#define MOE_ERR_ALIGN     (-4)  /* a tensor pointer is not 16-byte aligned             */
+#define MOE_ERR_WORKSPACE (-5)  /* workspace NULL or smaller than the query says       */
+#define MOE_ERR_HIP       (-6)  /* the HIP runtime reported a launch error             */
+
+/* ---- enums ------------------------------------------------------------- */
+#define MOE_SCORING_SOFTMAX 0   /* softmax over the top_k selected logits             */
+#define MOE_SCORING_SIGMOID 1   /* sigmoid(logit) renormalised over the top_k selected */
+
+#define MOE_ACT_SILU_MUL    0   /* a = silu(gate) * up                                 */
+#define MOE_ACT_SWIGLU_OAI  1   /* g = min(gate, L), u = clamp(up, -L, L),
+                                   a = g * sigmoid(alpha * g) * (u + 1)                */
+
+#define MOE_DTYPE_F32  0
+#define MOE_DTYPE_BF16 1
+
+/* ---- layer descriptor --------------------------------------------------- */
+typedef struct moe_mxfp4_desc {
+    int32_t T;              /* tokens in the call, >= 0 (T = 0 is a no-op)               */
+    int32_t K;              /* hidden size, multiple of 32, 32..8192                      */
+    int32_t I;              /* intermediate size per expert, multiple of 32, 32..8192     */
+    int32_t E_global;       /* experts the router scores, >= 1 (<= 1024 with logits)     */
+    int32_t E_local;        /* experts held in w13/w2, 1..512                             */
+    int32_t expert_offset;  /* global id of local expert 0; the slice is
+                               [expert_offset, expert_offset + E_local) within E_global */
+    int32_t top_k;          /* routes per token, 1..min(64, E_global)                    */
+    int32_t scoring;        /* MOE_SCORING_*  (used in router-logits mode only)          */
+    int32_t activation;     /* MOE_ACT_*                                                  */
+    float   swiglu_alpha;   /* 1.702 for gpt-oss  (MOE_ACT_SWIGLU_OAI only)              */
+    float   swiglu_limit;   /* 7.0 for gpt-oss    (MOE_ACT_SWIGLU_OAI only)              */
+} moe_mxfp4_desc;
+
+/*
+ * Device workspace needed by moe_mxfp4_decode / _gate_up / _down / _bucket for
+ * this descriptor (host-only query, nothing is launched).  It holds the routing
+ * table, the bucketing plan, the bf16 intermediate and the per-route fp32 down
+ * projection, each sized for the worst case T*top_k local routes.
+ * Returns MOE_OK and writes *bytes, or MOE_ERR_NULL / MOE_ERR_SHAPE / MOE_ERR_MODE.
+ */
+int moe_mxfp4_workspace_bytes(const moe_mxfp4_desc* desc, size_t* bytes);
+
+/*
+ * The layer call ("MXFP4 MoE decode kernels", Design: gate/up GEMV + bias +
+ * activation, then down GEMV + routing-weighted bias + weighted sum per token).
+ *
+ *  x            bf16 [T, K]
+ *  router_logits fp32 [T, E_global], or NULL  (router-logits mode: top_k by
+ *               logit descending, ties to the lower id; weights per `scoring`)
+ *  topk_ids     int32 [T, top_k] global expert ids, or NULL   (ids mode:
+ *  topk_weights fp32 [T, top_k], or NULL       weights are used as given)
+ *               Exactly one of router_logits and (topk_ids, topk_weights)
+ *               must be given, else MOE_ERR_MODE.  Ids outside the local
+ *               slice (including -1 padding) are skipped; a repeated id is a
+ *               separate route.
+ *  w13_packed   u8 [E_local, 2I, K/2]: row n < I is gate row n, row I+n is
+ *               up row n; byte c of a row holds element 2c in its low nibble
+ *               and element 2c+1 in its high nibble (E2M1 codes)
+ *  w13_scales   u8 [E_local, 2I, K/32]: E8M0 scale of elements 32b..32b+31
+ *  w13_bias     bf16 [E_local, 2I], or NULL (added to the fp32 projection
+ *               before the activation)
+ *  w2_packed    u8 [E_local, K, I/2]: row k is output feature k
+ *  w2_scales    u8 [E_local, K, I/32]
+ *  w2_bias      bf16 [E_local, K], or NULL (added once per route, before the
+ *               routing weight multiplies)
+ *  out          bf16 [T, K], fully overwritten; a token with no local route
+ *               gets zeros (the slice's partial sum; an expert-parallel caller
+ *               sums the slices)
+ *  workspace    device buffer of at least moe_mxfp4_workspace_bytes() bytes,
+ *               16-byte aligned; contents on entry are ignored
+ *
+ * Pointers to x, the packed weights, the scales, out and workspace must be
+ * 16-byte aligned (MOE_ERR_ALIGN).  Preconditions not checked: finite x and
+ * logits, buffers of the stated sizes.  Results are deterministic: no
+ * floating-point atomics; a call repeated on the same inputs is bit-identical.
+ */
+int moe_mxfp4_decode(const moe_mxfp4_desc* desc,
+                     const uint16_t* x,
+                     const float* router_logits,
+                     const int32_t* topk_ids, const float* topk_weights,
+                     const uint8_t* w13_packed, const uint8_t* w13_scales, const uint16_t* w13_bias,
+                     const uint8_t* w2_packed, const uint8_t* w2_scales, const uint16_t* w2_bias,
+                     uint16_t* out,
+                     void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
+ * The three steps of moe_mxfp4_decode, callable one by one on the same
+ * workspace (decode = plan, then gate_up, then down, with identical launches).
+ *
+ * moe_mxfp4_plan: routing and bucketing.  With router_logits (fp32
+ * [T, E_global]) it runs the top-k router; with topk_ids + topk_weights it
+ * takes them as given (exactly one mode, else MOE_ERR_MODE).  It then
+ * counting-sorts the local routes by local expert into the workspace ("MXFP4
+ * MoE decode kernels", Design, Routing inside the kernel) and keeps a copy of
+ * the routing weights there, so later steps read nothing else of the caller's
+ * routing inputs.
+ */
+int moe_mxfp4_plan(const moe_mxfp4_desc* desc, const float* router_logits,
+                   const int32_t* topk_ids, const float* topk_weights,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_mxfp4_gate_up: for every local route of the plan, the gate/up projection
+ * of its token with bias and activation, rounded to bf16 ("MXFP4 MoE decode
+ * kernels", Design, Fused epilogues).  Writes the intermediate a
+ * [T*top_k, I] bf16 whose row p (p < local routes) belongs to the p-th route
+ * of the plan's order (see moe_mxfp4_bucket); rows past the local routes are
+ * not written.  a == NULL writes the workspace's own copy (what
+ * moe_mxfp4_down reads when its a is NULL).  Needs moe_mxfp4_plan first.
+ */
+int moe_mxfp4_gate_up(const moe_mxfp4_desc* desc, const uint16_t* x,
+                      const uint8_t* w13_packed, const uint8_t* w13_scales, const uint16_t* w13_bias,
+                      uint16_t* a, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_mxfp4_down: down projection of every local route's intermediate row
+ * (a [>= local routes, I] bf16 in plan order, or NULL for the workspace copy),
+ * plus the w2 bias, then out [T, K] bf16 = per token, the sum over its local
+ * routes in route order of weight * (W2 a + b2) ("MXFP4 MoE decode kernels",
+ * Design, Fused epilogues).  Tokens without a local route get zeros.  Needs
+ * moe_mxfp4_plan first.
+ */
+int moe_mxfp4_down(const moe_mxfp4_desc* desc, const uint16_t* a,
+                   const uint8_t* w2_packed, const uint8_t* w2_scales, const uint16_t* w2_bias,
+                   uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Routing step alone (test hook): router logits fp32 [T, E_global] ->
+ * ids int32 [T, top_k] (logit descending, ties to the lower id) and
+ * weights fp32 [T, top_k] (softmax over the selected logits, or sigmoid
+ * renormalised over the selected, per desc->scoring).
+ */
+int moe_mxfp4_route(const moe_mxfp4_desc* desc, const float* router_logits,
+                    int32_t* topk_ids, float* topk_weights, void* stream);
+
+/*
+ * Bucketing step alone (test hook): ids int32 [T, top_k] -> per local expert
+ * counts int32 [E_local], exclusive offsets int32 [E_local + 1], and
+ * routes int32 [T*top_k] whose first offsets[E_local] entries are the local
+ * route indices r = t*top_k + j grouped by local expert, ascending r inside
+ * each group (a stable counting sort); the remaining entries are -1.
+ * Needs the workspace of moe_mxfp4_workspace_bytes().
+ */
+int moe_mxfp4_bucket(const moe_mxfp4_desc* desc, const int32_t* topk_ids,
+                     int32_t* counts, int32_t* offsets, int32_t* routes,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * MXFP4 -> dense dequantisation (test hook, and the unpack a prefill path
+ * would use): packed u8 [rows, cols/2] + scales u8 [rows, cols/32] ->
+ * out [rows, cols] as fp32 (out_dtype MOE_DTYPE_F32) or bf16 bits
+ * (MOE_DTYPE_BF16).  Value = E2M1(code) * 2^(scale - 127), scale 255 -> NaN,
+ * computed with the same decode the layer kernels use.  cols % 32 == 0.
+ */
+int moe_mxfp4_dequant(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t cols,
+                      int32_t out_dtype, void* out, void* stream);
+
+/* Static string naming a status code. */
+const char* moe_mxfp4_status_string(int status);
+
+/* Static version string of the library build. */
+const char* moe_mxfp4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MXFP4_H */

@@ -1,0 +1,238 @@
+"""MI355X (gfx950) routed-expert MXFP4 MoE decode layer.
+
+Python binding of ``libmoe_mxfp4.so`` with the same entry points as the C ABI
+in ``include/moe_mxfp4.h``.  It only marshals arguments: it checks dtypes,
+shapes, devices and contiguity of torch tensors (refusing anything unexpected
+rather than re-typing it) and passes their device pointers and the stream
+handle to the library, where every step of the layer runs.  PyTorch supplies
+device memory and streams.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    MOE_ACT_SILU_MUL,
+    MOE_ACT_SWIGLU_OAI,
+    MOE_DTYPE_BF16,
+    MOE_DTYPE_F32,
+    MOE_ERR_ALIGN,
+    MOE_ERR_HIP,
+    MOE_ERR_MODE,
+    MOE_ERR_NULL,
+    MOE_ERR_SHAPE,
+    MOE_ERR_WORKSPACE,
+    MOE_OK,
+    MOE_SCORING_SIGMOID,
+    MOE_SCORING_SOFTMAX,
+    MoeDesc,
+)
+
+__all__ = [
+    "MoeDesc", "MoeError", "make_desc", "moe_mxfp4_workspace_bytes", "moe_mxfp4_decode",
+    "moe_mxfp4_plan", "moe_mxfp4_gate_up", "moe_mxfp4_down", "moe_mxfp4_route", "moe_mxfp4_bucket",
+    "moe_mxfp4_dequant", "moe_mxfp4_status_string", "moe_mxfp4_version",
+]
+
+_SCORING = {"softmax": MOE_SCORING_SOFTMAX, "sigmoid": MOE_SCORING_SIGMOID}
+_ACT = {"silu_mul": MOE_ACT_SILU_MUL, "swiglu_oai": MOE_ACT_SWIGLU_OAI}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {moe_mxfp4_status_string(status)} ({status})")
+
+
+def make_desc(T: int, K: int, I: int, E_global: int, E_local: int, top_k: int, expert_offset: int = 0,
+              scoring="softmax", activation="silu_mul", swiglu_alpha: float = 1.702,
+              swiglu_limit: float = 7.0) -> MoeDesc:
+    sc = _SCORING[scoring] if isinstance(scoring, str) else int(scoring)
+    ac = _ACT[activation] if isinstance(activation, str) else int(activation)
+    return MoeDesc(T, K, I, E_global, E_local, expert_offset, top_k, sc, ac, swiglu_alpha, swiglu_limit)
+
+
+def moe_mxfp4_status_string(status: int) -> str:
+    return _lib.lib().moe_mxfp4_status_string(int(status)).decode()
+
+
+def moe_mxfp4_version() -> str:
+    return _lib.lib().moe_mxfp4_version().decode()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t, dtype, shape, name, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def moe_mxfp4_workspace_bytes(desc: MoeDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.lib().moe_mxfp4_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)), "moe_mxfp4_workspace_bytes")
+    return n.value
+
+
+def _workspace(desc, workspace, device):
+    torch = _torch()
+    need = moe_mxfp4_workspace_bytes(desc)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    if workspace.dtype != torch.uint8 or workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 device tensor")
+    return workspace, workspace.data_ptr(), workspace.numel()
+
+
+def _weights_shapes(d: MoeDesc, E: Optional[int] = None):
+    E = d.E_local if E is None else E
+    return ((E, 2 * d.I, d.K // 2), (E, 2 * d.I, d.K // 32), (E, 2 * d.I),
+            (E, d.K, d.I // 2), (E, d.K, d.I // 32), (E, d.K))
+
+
+def moe_mxfp4_decode(desc: MoeDesc, x, w13_packed, w13_scales, w2_packed, w2_scales, out,
+                     router_logits=None, topk_ids=None, topk_weights=None, w13_bias=None, w2_bias=None,
+                     workspace=None, stream=None):
+    """One layer call; ``out`` (bf16 [T, K]) is overwritten.  Returns the workspace used."""
+    torch = _torch()
+    d = desc
+    s13p, s13s, s13b, s2p, s2s, s2b = _weights_shapes(d)
+    ws, wsp, wsn = _workspace(d, workspace, x.device)
+    _check(_lib.lib().moe_mxfp4_decode(
+        ctypes.byref(d),
+        _ptr(x, torch.bfloat16, (d.T, d.K), "x"),
+        _ptr(router_logits, torch.float32, (d.T, d.E_global), "router_logits", True),
+        _ptr(topk_ids, torch.int32, (d.T, d.top_k), "topk_ids", True),
+        _ptr(topk_weights, torch.float32, (d.T, d.top_k), "topk_weights", True),
+        _ptr(w13_packed, torch.uint8, s13p, "w13_packed"),
+        _ptr(w13_scales, torch.uint8, s13s, "w13_scales"),
+        _ptr(w13_bias, torch.bfloat16, s13b, "w13_bias", True),
+        _ptr(w2_packed, torch.uint8, s2p, "w2_packed"),
+        _ptr(w2_scales, torch.uint8, s2s, "w2_scales"),
+        _ptr(w2_bias, torch.bfloat16, s2b, "w2_bias", True),
+        _ptr(out, torch.bfloat16, (d.T, d.K), "out"),
+        wsp, wsn, _stream(stream)), "moe_mxfp4_decode")
+    return ws
+
+
+def moe_mxfp4_plan(desc: MoeDesc, router_logits=None, topk_ids=None, topk_weights=None, workspace=None,
+                   stream=None, device=None):
+    """Routing + bucketing into the workspace (returned)."""
+    torch = _torch()
+    d = desc
+    dev = next((t.device for t in (router_logits, topk_ids, topk_weights) if t is not None), device)
+    ws, wsp, wsn = _workspace(d, workspace, dev)
+    _check(_lib.lib().moe_mxfp4_plan(
+        ctypes.byref(d),
+        _ptr(router_logits, torch.float32, (d.T, d.E_global), "router_logits", True),
+        _ptr(topk_ids, torch.int32, (d.T, d.top_k), "topk_ids", True),
+        _ptr(topk_weights, torch.float32, (d.T, d.top_k), "topk_weights", True),
+        wsp, wsn, _stream(stream)), "moe_mxfp4_plan")
+    return ws
+
+
+def moe_mxfp4_gate_up(desc: MoeDesc, x, w13_packed, w13_scales, workspace, a=None, w13_bias=None, stream=None):
+    """Gate/up step on the plan held in ``workspace``; writes ``a`` [T*top_k, I] bf16 (or the workspace copy)."""
+    torch = _torch()
+    d = desc
+    s13p, s13s, s13b, _, _, _ = _weights_shapes(d)
+    ws, wsp, wsn = _workspace(d, workspace, x.device)
+    _check(_lib.lib().moe_mxfp4_gate_up(
+        ctypes.byref(d),
+        _ptr(x, torch.bfloat16, (d.T, d.K), "x"),
+        _ptr(w13_packed, torch.uint8, s13p, "w13_packed"),
+        _ptr(w13_scales, torch.uint8, s13s, "w13_scales"),
+        _ptr(w13_bias, torch.bfloat16, s13b, "w13_bias", True),
+        _ptr(a, torch.bfloat16, (d.T * d.top_k, d.I), "a", True),
+        wsp, wsn, _stream(stream)), "moe_mxfp4_gate_up")
+
+
+def moe_mxfp4_down(desc: MoeDesc, w2_packed, w2_scales, out, workspace, a=None, w2_bias=None, stream=None):
+    """Down + combine step on the plan held in ``workspace``; ``a`` None reads the workspace copy."""
+    torch = _torch()
+    d = desc
+    _, _, _, s2p, s2s, s2b = _weights_shapes(d)
+    ws, wsp, wsn = _workspace(d, workspace, out.device)
+    _check(_lib.lib().moe_mxfp4_down(
+        ctypes.byref(d),
+        _ptr(a, torch.bfloat16, (d.T * d.top_k, d.I), "a", True),
+        _ptr(w2_packed, torch.uint8, s2p, "w2_packed"),
+        _ptr(w2_scales, torch.uint8, s2s, "w2_scales"),
+        _ptr(w2_bias, torch.bfloat16, s2b, "w2_bias", True),
+        _ptr(out, torch.bfloat16, (d.T, d.K), "out"),
+        wsp, wsn, _stream(stream)), "moe_mxfp4_down")
+
+
+def moe_mxfp4_route(desc: MoeDesc, router_logits, topk_ids, topk_weights, stream=None):
+    torch = _torch()
+    d = desc
+    _check(_lib.lib().moe_mxfp4_route(
+        ctypes.byref(d),
+        _ptr(router_logits, torch.float32, (d.T, d.E_global), "router_logits"),
+        _ptr(topk_ids, torch.int32, (d.T, d.top_k), "topk_ids"),
+        _ptr(topk_weights, torch.float32, (d.T, d.top_k), "topk_weights"),
+        _stream(stream)), "moe_mxfp4_route")
+
+
+def moe_mxfp4_bucket(desc: MoeDesc, topk_ids, counts, offsets, routes, workspace=None, stream=None):
+    torch = _torch()
+    d = desc
+    ws, wsp, wsn = _workspace(d, workspace, topk_ids.device)
+    _check(_lib.lib().moe_mxfp4_bucket(
+        ctypes.byref(d),
+        _ptr(topk_ids, torch.int32, (d.T, d.top_k), "topk_ids"),
+        _ptr(counts, torch.int32, (d.E_local,), "counts"),
+        _ptr(offsets, torch.int32, (d.E_local + 1,), "offsets"),
+        _ptr(routes, torch.int32, (d.T * d.top_k,), "routes"),
+        wsp, wsn, _stream(stream)), "moe_mxfp4_bucket")
+    return ws
+
+
+def moe_mxfp4_dequant(packed, scales, out, stream=None):
+    """packed u8 [rows, cols/2] + scales u8 [rows, cols/32] -> out fp32 or bf16 [rows, cols]."""
+    torch = _torch()
+    rows, half = packed.shape
+    cols = 2 * half
+    if out.dtype == torch.float32:
+        code = MOE_DTYPE_F32
+    elif out.dtype == torch.bfloat16:
+        code = MOE_DTYPE_BF16
+    else:
+        raise TypeError(f"out must be float32 or bfloat16, got {out.dtype}")
+    _check(_lib.lib().moe_mxfp4_dequant(
+        _ptr(packed, torch.uint8, (rows, half), "packed"),
+        _ptr(scales, torch.uint8, (rows, cols // 32), "scales"),
+        rows, cols, code, _ptr(out, out.dtype, (rows, cols), "out"), _stream(stream)), "moe_mxfp4_dequant")

@@ -1,0 +1,155 @@
+"""The C-ABI library loads, exports what include/*.h declares, and refuses bad
+arguments on the host before any launch (no GPU needed: every call here
+returns during argument checking)."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from mxfp4_mixture_experts_router_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="library not built")
+
+
+def _declared():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(moe_mxfp4_\w+)\s*\(", text))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    decl = _declared()
+    assert decl == set(_lib.EXPORTED), decl ^ set(_lib.EXPORTED)
+    handle = _lib.lib()
+    for name in decl:
+        assert getattr(handle, name) is not None
+
+
+def test_version_and_status_strings():
+    L = _lib.lib()
+    assert b"gfx950" in L.moe_mxfp4_version()
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert L.moe_mxfp4_status_string(st).startswith(b"MOE_")
+    assert L.moe_mxfp4_status_string(12345) == b"unknown status"
+
+
+def _desc(**kw):
+    d = dict(T=4, K=256, I=256, E_global=8, E_local=8, expert_offset=0, top_k=2, scoring=0,
+             activation=0, swiglu_alpha=1.702, swiglu_limit=7.0)
+    d.update(kw)
+    return _lib.MoeDesc(**d)
+
+
+def _ws_bytes(d):
+    n = ctypes.c_size_t(0)
+    st = _lib.lib().moe_mxfp4_workspace_bytes(ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_query():
+    st, n = _ws_bytes(_desc())
+    assert st == 0 and n > 0 and n % 256 == 0
+    st2, n2 = _ws_bytes(_desc(T=8))
+    assert n2 > n
+    assert _lib.lib().moe_mxfp4_workspace_bytes(None, ctypes.byref(ctypes.c_size_t())) == _lib.MOE_ERR_NULL
+    assert _lib.lib().moe_mxfp4_workspace_bytes(ctypes.byref(_desc()), None) == _lib.MOE_ERR_NULL
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(K=250), _lib.MOE_ERR_SHAPE),
+    (dict(K=0), _lib.MOE_ERR_SHAPE),
+    (dict(K=8192 + 32), _lib.MOE_ERR_SHAPE),
+    (dict(I=48), _lib.MOE_ERR_SHAPE),
+    (dict(T=-1), _lib.MOE_ERR_SHAPE),
+    (dict(E_local=9), _lib.MOE_ERR_SHAPE),
+    (dict(E_local=4, expert_offset=5), _lib.MOE_ERR_SHAPE),
+    (dict(expert_offset=-1), _lib.MOE_ERR_SHAPE),
+    (dict(top_k=0), _lib.MOE_ERR_SHAPE),
+    (dict(top_k=9), _lib.MOE_ERR_SHAPE),
+    (dict(E_global=600, E_local=513), _lib.MOE_ERR_SHAPE),
+    (dict(scoring=2), _lib.MOE_ERR_MODE),
+    (dict(activation=-1), _lib.MOE_ERR_MODE),
+])
+def test_bad_descriptors_are_refused(bad, code):
+    st, _ = _ws_bytes(_desc(**bad))
+    assert st == code
+
+
+# fake, never-dereferenced addresses: every call below must fail in the host checks
+A = 0x10000
+A_MIS = 0x10008
+
+
+def _decode(d, **kw):
+    args = dict(x=A, logits=A, ids=None, wts=None, w13p=A, w13s=A, b13=None, w2p=A, w2s=A, b2=None,
+                out=A, ws=A, ws_bytes=1 << 40)
+    args.update(kw)
+    return _lib.lib().moe_mxfp4_decode(
+        ctypes.byref(d), args["x"], args["logits"], args["ids"], args["wts"], args["w13p"], args["w13s"],
+        args["b13"], args["w2p"], args["w2s"], args["b2"], args["out"], args["ws"], args["ws_bytes"], None)
+
+
+def test_decode_error_paths():
+    d = _desc()
+    E = _lib
+    assert _decode(d, logits=None) == E.MOE_ERR_MODE                      # neither routing input
+    assert _decode(d, ids=A, wts=A) == E.MOE_ERR_MODE                     # both
+    assert _decode(d, logits=None, ids=A) == E.MOE_ERR_MODE               # ids without weights
+    assert _decode(d, x=None) == E.MOE_ERR_NULL
+    assert _decode(d, w2s=None) == E.MOE_ERR_NULL
+    assert _decode(d, out=None) == E.MOE_ERR_NULL
+    assert _decode(d, x=A_MIS) == E.MOE_ERR_ALIGN
+    assert _decode(d, w13p=A_MIS) == E.MOE_ERR_ALIGN
+    assert _decode(d, out=A_MIS) == E.MOE_ERR_ALIGN
+    assert _decode(d, ws=None) == E.MOE_ERR_WORKSPACE
+    assert _decode(d, ws=A_MIS) == E.MOE_ERR_ALIGN
+    _, need = _ws_bytes(d)
+    assert _decode(d, ws_bytes=need - 1) == E.MOE_ERR_WORKSPACE
+    assert _decode(_desc(E_global=2048, E_local=8)) == E.MOE_ERR_SHAPE   # too many experts to route
+    assert _decode(_desc(T=0)) == E.MOE_OK                               # T = 0: nothing to do
+    assert _decode(_desc(T=0), x=None, out=None) == E.MOE_OK
+
+
+def test_hook_error_paths():
+    L = _lib.lib()
+    d = _desc()
+    E = _lib
+    assert L.moe_mxfp4_route(ctypes.byref(d), None, A, A, None) == E.MOE_ERR_NULL
+    assert L.moe_mxfp4_route(ctypes.byref(_desc(E_global=1100, E_local=8)), A, A, A, None) == E.MOE_ERR_SHAPE
+    assert L.moe_mxfp4_bucket(ctypes.byref(d), A, A, A, None, A, 1 << 40, None) == E.MOE_ERR_NULL
+    assert L.moe_mxfp4_bucket(ctypes.byref(d), A, A, A, A, A, 16, None) == E.MOE_ERR_WORKSPACE
+    assert L.moe_mxfp4_plan(ctypes.byref(d), None, None, None, A, 1 << 40, None) == E.MOE_ERR_MODE
+    assert L.moe_mxfp4_plan(ctypes.byref(d), A, A, A, A, 1 << 40, None) == E.MOE_ERR_MODE
+    assert L.moe_mxfp4_plan(ctypes.byref(d), None, A, None, A, 1 << 40, None) == E.MOE_ERR_MODE
+    assert L.moe_mxfp4_plan(ctypes.byref(d), A, None, None, A, 16, None) == E.MOE_ERR_WORKSPACE
+    assert L.moe_mxfp4_plan(ctypes.byref(_desc(T=0)), A, None, None, None, 0, None) == E.MOE_OK
+    assert L.moe_mxfp4_gate_up(ctypes.byref(d), A, A, A, None, A_MIS, A, 1 << 40, None) == E.MOE_ERR_ALIGN
+    assert L.moe_mxfp4_gate_up(ctypes.byref(d), None, A, A, None, None, A, 1 << 40, None) == E.MOE_ERR_NULL
+    assert L.moe_mxfp4_gate_up(ctypes.byref(d), A, A, A, None, None, None, 1 << 40, None) == E.MOE_ERR_WORKSPACE
+    assert L.moe_mxfp4_down(ctypes.byref(d), None, A, None, None, A, A, 1 << 40, None) == E.MOE_ERR_NULL
+    assert L.moe_mxfp4_down(ctypes.byref(d), A_MIS, A, A, None, A, A, 1 << 40, None) == E.MOE_ERR_ALIGN
+    assert L.moe_mxfp4_down(ctypes.byref(d), None, A, A, None, A, A, 8, None) == E.MOE_ERR_WORKSPACE
+    assert L.moe_mxfp4_dequant(A, A, 4, 48, 0, A, None) == E.MOE_ERR_SHAPE
+    assert L.moe_mxfp4_dequant(A, A, 4, 64, 7, A, None) == E.MOE_ERR_MODE
+    assert L.moe_mxfp4_dequant(A_MIS, A, 4, 64, 0, A, None) == E.MOE_ERR_ALIGN
+    assert L.moe_mxfp4_dequant(None, A, 4, 64, 0, A, None) == E.MOE_ERR_NULL
+    assert L.moe_mxfp4_dequant(A, A, 0, 64, 0, A, None) == E.MOE_OK
+
+
+def test_binding_rejects_unexpected_dtypes():
+    torch = pytest.importorskip("torch")
+    import mxfp4_mixture_experts_router_amd as m
+    with pytest.raises(TypeError):
+        m._ptr(torch.zeros(4, 256, dtype=torch.float16), torch.bfloat16, (4, 256), "x")
+    with pytest.raises(ValueError):
+        m._ptr(torch.zeros(4, 255, dtype=torch.bfloat16), torch.bfloat16, (4, 256), "x")
+    with pytest.raises(ValueError):
+        m._ptr(torch.zeros(4, 256, dtype=torch.bfloat16), torch.bfloat16, (4, 256), "x")  # host tensor

@@ -1,0 +1,336 @@
+"""Parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bit-exact: dequantised values, top-k ids, the bucketing permutation, and a
+closed-form dyadic chain.  Floating-point outputs: rel_l2 <= 3e-3 and
+cosine >= 0.9999 against the fp32 oracle (the acceptance bar of the layer;
+the bf16 rounding of the output alone costs about 1.7e-3), no non-finite
+values.  Small shapes are compared element by element; the full workload
+shapes are run in the launch configuration the benchmark uses and compared
+on sampled tokens, which the oracle computes on their own (its output for a
+token does not depend on the other tokens of the batch).
+"""
+
+import numpy as np
+import pytest
+
+import mxfp4_mixture_experts_router_amd as moe
+import oracle
+from workloads import LayerConfig, get_config, make_inputs, make_topk_inputs, make_weights
+
+from gpu_util import (DeviceLayer, bf16_bits_np, bf16_to_np, desc_for, dev_bf16, dev_f32, dev_i32, dev_u8,
+                      run_decode, torch)
+
+pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
+
+REL_L2 = 3e-3
+COSINE = 0.9999
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    t = torch()
+    assert t.cuda.is_available(), "GPU tests need a GPU"
+    print("device:", t.cuda.get_device_name(0), "|", moe.moe_mxfp4_version(), flush=True)
+
+
+def _cfg(**kw):
+    base = dict(name="case", description="case", K=256, I=256, E_global=8, E_local=8, expert_offset=0,
+                top_k=2, scoring="softmax", activation="silu_mul", bias=False, tokens=(4,),
+                scale_lo=118, scale_hi=130, index=90)
+    base.update(kw)
+    return LayerConfig(**base)
+
+
+def _assert_close(y_gpu, y_ref, what):
+    assert np.isfinite(y_gpu).all(), f"{what}: {np.count_nonzero(~np.isfinite(y_gpu))} non-finite outputs"
+    if not np.any(y_ref):
+        assert not np.any(y_gpu), f"{what}: expected all zeros"
+        return
+    r = oracle.rel_l2(y_gpu, y_ref)
+    c = oracle.cosine(y_gpu, y_ref)
+    print(f"{what}: rel_l2 {r:.3e} cosine {c:.7f}", flush=True)
+    assert r <= REL_L2 and c >= COSINE, (what, r, c)
+
+
+# --------------------------------------------------------------------------
+# dequantisation: bit-exact over every (code, scale, nibble position)
+# --------------------------------------------------------------------------
+
+def test_dequant_exhaustive_bit_exact():
+    t = torch()
+    byte_row = np.array([(i & 0xF) | ((15 - i) << 4) for i in range(16)], dtype=np.uint8)
+    packed = np.tile(byte_row, (256, 4))            # 256 rows x 128 values (4 blocks)
+    scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 4, axis=1)
+    scales[:, 1] = scales[:, 0][::-1]               # vary the scale per block too
+    want = oracle.dequantize(packed, scales)
+    out32 = t.empty((256, 128), dtype=t.float32, device="cuda")
+    moe.moe_mxfp4_dequant(dev_u8(packed), dev_u8(scales), out32)
+    got = out32.cpu().numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))  # sign of -0 included
+    out16 = t.empty((256, 128), dtype=t.bfloat16, device="cuda")
+    moe.moe_mxfp4_dequant(dev_u8(packed), dev_u8(scales), out16)
+    got16 = bf16_to_np(out16)
+    # every finite E2M1 * 2^k value is a bf16 value, so the bf16 output is exact too
+    assert np.array_equal(np.isnan(got16), nan)
+    assert np.array_equal(got16[~nan].view(np.uint32), want[~nan].view(np.uint32))
+
+
+def test_dequant_random_large():
+    t = torch()
+    rng = np.random.default_rng(1)
+    rows, cols = 1000, 2880
+    packed = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(100, 140, size=(rows, cols // 32), dtype=np.uint8)
+    out = t.empty((rows, cols), dtype=t.float32, device="cuda")
+    moe.moe_mxfp4_dequant(dev_u8(packed), dev_u8(scales), out)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), oracle.dequantize(packed, scales).view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# routing and bucketing: bit-exact ids and permutation
+# --------------------------------------------------------------------------
+
+ROUTE_CASES = [("tiny", 4), ("gptoss20b", 32), ("gptoss120b", 32), ("glm5_ep", 32), ("widek", 2048)]
+
+
+@pytest.mark.parametrize("name,T", ROUTE_CASES)
+def test_route_topk(name, T):
+    t = torch()
+    cfg = get_config(name)
+    inp = make_inputs(cfg, T)
+    d = desc_for(cfg, T)
+    ids = t.empty((T, cfg.top_k), dtype=t.int32, device="cuda")
+    w = t.empty((T, cfg.top_k), dtype=t.float32, device="cuda")
+    moe.moe_mxfp4_route(d, dev_f32(inp.logits), ids, w)
+    t.cuda.synchronize()
+    ids_ref, w_ref = oracle.route_topk(inp.logits, cfg.top_k, cfg.scoring, dtype=np.float64)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert np.allclose(w.cpu().numpy(), w_ref, rtol=2e-6, atol=1e-7)
+
+
+def test_route_ties_break_to_lower_id():
+    t = torch()
+    cfg = _cfg(E_global=200, E_local=8, top_k=8, scoring="sigmoid")
+    rng = np.random.default_rng(2)
+    logits = (np.round(rng.standard_normal((64, 200)) * 2) / 2).astype(np.float32)  # many ties
+    logits[0] = 1.0
+    d = desc_for(cfg, 64)
+    ids = t.empty((64, 8), dtype=t.int32, device="cuda")
+    w = t.empty((64, 8), dtype=t.float32, device="cuda")
+    moe.moe_mxfp4_route(d, dev_f32(logits), ids, w)
+    ids_ref, w_ref = oracle.route_topk(logits, 8, "sigmoid", dtype=np.float64)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert ids.cpu().numpy()[0].tolist() == list(range(8))
+    assert np.allclose(w.cpu().numpy(), w_ref, rtol=2e-6)
+
+
+BUCKET_CASES = [
+    (8, 8, 0, 2, 4, 0.0), (32, 32, 0, 4, 1, 0.0), (128, 128, 0, 4, 32, 0.0), (256, 32, 64, 8, 32, 0.1),
+    (384, 48, 336, 8, 2048, 0.05), (384, 48, 0, 8, 2047, 0.0), (512, 512, 0, 8, 300, 0.0), (16, 4, 12, 16, 3, 0.3),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BUCKET_CASES)))
+def test_bucket_permutation_bit_exact(case):
+    t = torch()
+    E_g, E_l, off, k, T, pad = BUCKET_CASES[case]
+    cfg = _cfg(E_global=E_g, E_local=E_l, expert_offset=off, top_k=k)
+    inp = make_topk_inputs(cfg, T, seed=100 + case, pad_fraction=pad)
+    d = desc_for(cfg, T)
+    counts = t.empty(E_l, dtype=t.int32, device="cuda")
+    offsets = t.empty(E_l + 1, dtype=t.int32, device="cuda")
+    routes = t.empty(T * k, dtype=t.int32, device="cuda")
+    moe.moe_mxfp4_bucket(d, dev_i32(inp.topk_ids), counts, offsets, routes)
+    t.cuda.synchronize()
+    c_ref, o_ref, r_ref = oracle.bucket_routes(inp.topk_ids, E_l, off)
+    assert np.array_equal(counts.cpu().numpy(), c_ref)
+    assert np.array_equal(offsets.cpu().numpy(), o_ref)
+    r = routes.cpu().numpy()
+    assert np.array_equal(r[:len(r_ref)], r_ref)
+    assert (r[len(r_ref):] == -1).all()
+
+
+def test_bucket_duplicate_ids_are_separate_routes():
+    t = torch()
+    cfg = _cfg(E_global=8, E_local=8, top_k=4)
+    ids = np.array([[3, 3, 1, 3], [0, 7, 7, -1]], np.int32)
+    d = desc_for(cfg, 2)
+    counts = t.empty(8, dtype=t.int32, device="cuda")
+    offsets = t.empty(9, dtype=t.int32, device="cuda")
+    routes = t.empty(8, dtype=t.int32, device="cuda")
+    moe.moe_mxfp4_bucket(d, dev_i32(ids), counts, offsets, routes)
+    c_ref, o_ref, r_ref = oracle.bucket_routes(ids, 8, 0)
+    assert np.array_equal(counts.cpu().numpy(), c_ref)
+    assert np.array_equal(routes.cpu().numpy()[:len(r_ref)], r_ref)
+
+
+# --------------------------------------------------------------------------
+# gate/up and down steps alone
+# --------------------------------------------------------------------------
+
+STEP_CASES = [
+    dict(),                                                                    # tiny
+    dict(K=2880, I=2880, E_global=32, E_local=4, expert_offset=8, top_k=4, activation="swiglu_oai",
+         bias=True, scale_lo=115, scale_hi=127),                               # ragged 90-block rows
+    dict(K=6144, I=2048, E_global=16, E_local=2, top_k=8, scoring="sigmoid", scale_lo=115, scale_hi=127),
+    dict(K=96, I=160, E_global=3, E_local=3, top_k=2, bias=True, activation="swiglu_oai"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(STEP_CASES)))
+@pytest.mark.parametrize("T", [1, 5, 19])
+def test_gate_up_step(case, T):
+    t = torch()
+    cfg = _cfg(**STEP_CASES[case])
+    w = make_weights(cfg)
+    inp = make_inputs(cfg, T, t_index=T, x_scale=4.0 if case == 1 else 1.0)
+    ref = oracle.moe_forward_cfg(cfg, w, inp)
+    layer = DeviceLayer(w)
+    d = desc_for(cfg, T)
+    ws = moe.moe_mxfp4_plan(d, topk_ids=dev_i32(ref["ids"]), topk_weights=dev_f32(ref["weights"]))
+    a = t.zeros((T * cfg.top_k, cfg.I), dtype=t.bfloat16, device="cuda")
+    moe.moe_mxfp4_gate_up(d, dev_bf16(inp.x), layer.w13p, layer.w13s, ws, a=a, w13_bias=layer.b13)
+    t.cuda.synchronize()
+    Rl = len(ref["routes"])
+    got = bf16_to_np(a)[:Rl]
+    _assert_close(got, ref["a"], f"a case{case} T{T}")
+    assert np.mean(got == ref["a"]) > 0.98   # bf16 values agree except rare rounding-boundary cases
+
+
+@pytest.mark.parametrize("case", range(len(STEP_CASES)))
+@pytest.mark.parametrize("T", [1, 5, 19])
+def test_down_step(case, T):
+    t = torch()
+    cfg = _cfg(**STEP_CASES[case])
+    w = make_weights(cfg)
+    inp = make_inputs(cfg, T, t_index=T)
+    ref = oracle.moe_forward_cfg(cfg, w, inp)
+    layer = DeviceLayer(w)
+    d = desc_for(cfg, T)
+    R = T * cfg.top_k
+    a_bits = np.zeros((R, cfg.I), np.uint16)
+    a_bits[:len(ref["routes"])] = (ref["a"].astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    ws = moe.moe_mxfp4_plan(d, router_logits=dev_f32(inp.logits))
+    out = t.full((T, cfg.K), float("nan"), dtype=t.bfloat16, device="cuda")
+    moe.moe_mxfp4_down(d, layer.w2p, layer.w2s, out, ws, a=dev_bf16(a_bits), w2_bias=layer.b2)
+    t.cuda.synchronize()
+    _assert_close(bf16_to_np(out), ref["y"], f"down case{case} T{T}")
+
+
+def test_steps_compose_to_decode():
+    t = torch()
+    cfg = _cfg(**STEP_CASES[1])
+    w = make_weights(cfg)
+    inp = make_inputs(cfg, 6, t_index=3)
+    layer = DeviceLayer(w)
+    d = desc_for(cfg, 6)
+    logits = dev_f32(inp.logits)
+    ws = moe.moe_mxfp4_plan(d, router_logits=logits)
+    moe.moe_mxfp4_gate_up(d, dev_bf16(inp.x), layer.w13p, layer.w13s, ws, w13_bias=layer.b13)
+    out1 = t.empty((6, cfg.K), dtype=t.bfloat16, device="cuda")
+    moe.moe_mxfp4_down(d, layer.w2p, layer.w2s, out1, ws, w2_bias=layer.b2)
+    out2 = run_decode(cfg, layer, inp)
+    assert np.array_equal(bf16_bits_np(out1), bf16_bits_np(out2))
+
+
+# --------------------------------------------------------------------------
+# the whole layer
+# --------------------------------------------------------------------------
+
+LAYER_CASES = [
+    ("tiny", dict(), 4, 1.0),
+    ("tiny", dict(), 1, 4.0),
+    ("swiglu-slice", dict(K=2880, I=2880, E_global=32, E_local=6, expert_offset=20, top_k=4,
+                          activation="swiglu_oai", bias=True, scale_lo=115, scale_hi=127), 7, 4.0),
+    ("sigmoid-slice", dict(K=6144, I=2048, E_global=64, E_local=4, expert_offset=4, top_k=8,
+                           scoring="sigmoid", scale_lo=115, scale_hi=127), 9, 1.0),
+    ("many-tokens-per-expert", dict(K=512, I=768, E_global=2, E_local=2, top_k=2), 37, 1.0),
+    ("odd-blocks", dict(K=96, I=224, E_global=5, E_local=5, top_k=3, activation="swiglu_oai", bias=True), 11, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(LAYER_CASES)))
+def test_layer_elementwise(case):
+    name, kw, T, xs = LAYER_CASES[case]
+    cfg = _cfg(**kw)
+    w = make_weights(cfg)
+    inp = make_inputs(cfg, T, t_index=case, x_scale=xs)
+    ref = oracle.moe_forward_cfg(cfg, w, inp)
+    out = run_decode(cfg, DeviceLayer(w), inp)
+    _assert_close(bf16_to_np(out), ref["y"], f"layer {name} T{T}")
+
+
+def test_layer_ids_mode_with_padding_and_foreign_ids():
+    cfg = _cfg(K=2880, I=2880, E_global=32, E_local=5, expert_offset=3, top_k=4, activation="swiglu_oai",
+               bias=True, scale_lo=115, scale_hi=127)
+    w = make_weights(cfg)
+    inp = make_topk_inputs(cfg, 12, seed=7, pad_fraction=0.2)
+    ref = oracle.moe_forward_cfg(cfg, w, inp)
+    y = bf16_to_np(run_decode(cfg, DeviceLayer(w), inp))
+    _assert_close(y, ref["y"], "ids mode")
+    no_route = ~np.any((inp.topk_ids >= 3) & (inp.topk_ids < 8), axis=1)
+    assert not y[no_route].any()
+
+
+def test_layer_no_local_route_writes_zeros():
+    cfg = _cfg(E_global=16, E_local=4, expert_offset=12, top_k=2)
+    w = make_weights(cfg)
+    inp = make_topk_inputs(cfg, 6, seed=8)
+    inp.topk_ids[:] = np.array([0, 1], np.int32)
+    y = bf16_to_np(run_decode(cfg, DeviceLayer(w), inp))
+    assert np.array_equal(y, np.zeros_like(y)) and not np.signbit(y).any()
+
+
+def test_layer_exact_chain_bit_exact():
+    from test_oracle_layer import build_exact_chain
+    t = torch()
+    for c0 in (37, 70):
+        arrays, want = build_exact_chain(c0, False)
+        d = moe.make_desc(T=2, K=arrays["K"], I=arrays["I"], E_global=2, E_local=2, top_k=2)
+        out = t.empty((2, arrays["K"]), dtype=t.bfloat16, device="cuda")
+        moe.moe_mxfp4_decode(d, dev_bf16(arrays["x_bits"]), dev_u8(arrays["w13_packed"]),
+                             dev_u8(arrays["w13_scales"]), dev_u8(arrays["w2_packed"]),
+                             dev_u8(arrays["w2_scales"]), out, topk_ids=dev_i32(arrays["topk_ids"]),
+                             topk_weights=dev_f32(arrays["topk_weights"]))
+        t.cuda.synchronize()
+        assert np.array_equal(bf16_to_np(out).astype(np.float64), want)
+
+
+def test_layer_repeat_calls_bit_identical():
+    t = torch()
+    cfg = get_config("gptoss20b")
+    w = make_weights(cfg, E_local=8)
+    cfg2 = LayerConfig(**{**cfg.__dict__, "E_global": 8, "E_local": 8})
+    inp = make_inputs(cfg2, 16)
+    layer = DeviceLayer(w)
+    ws = t.empty(moe.moe_mxfp4_workspace_bytes(desc_for(cfg2, 16)), dtype=t.uint8, device="cuda")
+    first = bf16_bits_np(run_decode(cfg2, layer, inp, workspace=ws))
+    for _ in range(3):
+        assert np.array_equal(bf16_bits_np(run_decode(cfg2, layer, inp, workspace=ws)), first)
+
+
+# --------------------------------------------------------------------------
+# full workload shapes, sampled tokens
+# --------------------------------------------------------------------------
+
+FULL_CASES = [("gptoss20b", 1), ("gptoss20b", 32), ("gptoss120b", 32), ("glm5_ep", 1), ("glm5_ep", 32),
+              ("widek", 256), ("widek", 2048)]
+
+
+@pytest.mark.parametrize("name,T", FULL_CASES)
+def test_full_shape_sampled_tokens(name, T):
+    cfg = get_config(name)
+    print(f"full shape {name} T={T}: generating", flush=True)
+    w = make_weights(cfg)
+    inp = make_inputs(cfg, T)
+    out = bf16_to_np(run_decode(cfg, DeviceLayer(w), inp))
+    assert np.isfinite(out).all()
+    rng = np.random.default_rng(T)
+    sample = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, size=4)]))
+    sub = make_inputs(cfg, T)
+    sub.x = inp.x[sample]
+    sub.logits = inp.logits[sample]
+    ref = oracle.moe_forward_cfg(cfg, w, sub)
+    _assert_close(out[sample], ref["y"], f"{name} T={T} tokens {sample.tolist()}")
