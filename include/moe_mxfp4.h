@@ -116,7 +116,7 @@ int moe_mxfp4_workspace_bytes(const moe_mxfp4_desc* desc, size_t* bytes);
  *               16-byte aligned; contents on entry are ignored
  *
  * Pointers to x, the packed weights, the scales, out and workspace must be
- * 16-byte aligned (MOE_ERR_ALIGN).  Preconditions not checked: finite x and
+ * 16-byte aligned (MOE_ERR_ALIGN); the same holds for every entry point below.  Preconditions not checked: finite x and
  * logits, buffers of the stated sizes.  Results are deterministic: no
  * floating-point atomics; a call repeated on the same inputs is bit-identical.
  */

@@ -21,14 +21,6 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int kWave = 64;
 
-// Device-side plan written by the bucketing kernel and read by the expert
-// kernels.  Lives at the start of the workspace.
-struct Plan {
-  int32_t n_touched;   // local experts with at least one route
-  int32_t R_local;     // local routes
-  int32_t pad[62];
-};
-
 // E8M0 byte -> fp32 2^(s-127), built from the IEEE exponent field;
 // s = 0 is the subnormal 2^-127, s = 255 is NaN.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {

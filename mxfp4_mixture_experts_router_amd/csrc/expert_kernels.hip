@@ -1,0 +1,517 @@
+// Grouped expert kernels: the gate/up projection with its activation, the
+// down projection, the routing-weighted combine, and the dequantisation hook.
+//
+// What they compute: "MXFP4 MoE decode kernels", Design (x -> gate/up GEMV +
+// bias + activation -> bf16 intermediate; intermediate -> down GEMV +
+// routing-weighted bias + weighted sum per token) and Design, Fused
+// epilogues.  Weights are read once, straight from the packed layout (Design,
+// Read the served layout), and decoded in registers with gfx950's scaled FP4
+// converts; one 16-byte load of a packed row is exactly one 32-value MX block
+// and needs one scale byte.
+//
+// Two regimes, two kernels, each serving both projections (a template flag
+// selects [gate; up] row pairs with the activation, or single rows):
+//  * GEMV (experts with Te <= kGemvMaxTokens routes): kLanesPerRow lanes
+//    stream one row (pair); lane q loads MX blocks q, q + kLanesPerRow, ...
+//    with 128-bit loads through a register ring so that several blocks per
+//    row are in flight, multiplies with v_dot2_f32_bf16 against the
+//    activations staged once in LDS, and the partial sums are combined with
+//    DPP row operations.
+//  * MFMA (Te > kGemvMaxTokens): 4 waves x 16 rows, tokens in groups of 16.
+//    Each lane decodes one MX block of its row per step into four 8-value
+//    bf16 operands of v_mfma_f32_16x16x32_bf16; the activation chunk of the
+//    tokens is shared by the 4 waves through LDS.  The reduction index inside
+//    one MFMA is permuted (lane group q carries block q of the chunk),
+//    identically for both operands.
+// A work item (one workgroup) is a tile of rows of one expert from the
+// plan's list for its regime; blocks past the list exit at once, so the grid
+// only needs a host-side upper bound.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ bf16x8 decode_dword_bf16x8(uint32_t d, float s) {
+  const bf16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 0);
+  const bf16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 1);
+  const bf16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 2);
+  const bf16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 3);
+  bf16x8 r;
+  r[0] = v0[0]; r[1] = v0[1]; r[2] = v1[0]; r[3] = v1[1];
+  r[4] = v2[0]; r[5] = v2[1]; r[6] = v3[0]; r[7] = v3[1];
+  return r;
+}
+
+__device__ __forceinline__ float dot_block(const bf16x2 (&w)[16], const uint4* __restrict__ xp, float acc) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint4 xv = xp[c];
+    acc = dot2(w[4 * c + 0], xv.x, acc);
+    acc = dot2(w[4 * c + 1], xv.y, acc);
+    acc = dot2(w[4 * c + 2], xv.z, acc);
+    acc = dot2(w[4 * c + 3], xv.w, acc);
+  }
+  return acc;
+}
+
+// Copy nbytes (a multiple of 4, 4-byte aligned source) from global memory to
+// LDS with direct global->LDS loads of one dword per lane; every thread of the
+// 256-lane workgroup takes part.  A wave's copy fills 256 contiguous LDS bytes.
+__device__ __forceinline__ void dma_strip(const uint8_t* __restrict__ src, unsigned char* dst, int nbytes) {
+  const int n = nbytes >> 2;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(src) + i,
+                                     reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                         reinterpret_cast<uintptr_t>(dst + 4 * (i & ~63))),
+                                     4, 0, 0);
+  }
+}
+
+template <int kLanesPerRow>
+__device__ __forceinline__ float row_sum(float v) {
+  v = row16_sum(v);
+  if (kLanesPerRow == 32) v += __shfl_xor(v, 16);
+  return v;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// GEMV regime
+// ---------------------------------------------------------------------------
+// The hot loop is branch-free so that the compiler keeps the register ring of
+// weight loads in flight: block indices are clamped to the row (the surplus
+// loads of the ragged tail hit the same row) and tail contributions are
+// dropped with selects.
+template <bool kGateUp, int kLanesPerRow>
+__global__ __launch_bounds__(256, 4) void gemv_kernel(ExpertArgs A) {
+  constexpr int kRowsPerWG = 256 / kLanesPerRow;
+  constexpr int kRing = kGateUp ? 4 : (kLanesPerRow == 16 ? 6 : 4);
+  extern __shared__ uint4 xs[];  // [kGemvMaxTokens][red / 8], then the scale strips
+
+  const int tiles = A.rows / kRowsPerWG;
+  const int item = blockIdx.x / tiles;         // < E_local: the entry load is always in bounds
+  const int n_items = A.plan->n_gemv;
+  const WorkEntry we = A.list[item];
+  if (item >= n_items) return;
+  const int tile = blockIdx.x - item * tiles;
+  const int tid = threadIdx.x, g = tid / kLanesPerRow, q = tid % kLanesPerRow;
+  const int red = A.red, RB = red >> 5, RV = red >> 3;
+  const int n = tile * kRowsPerWG + g;
+  // wave-uniform expert base pointers + 32-bit per-lane row offsets
+  const int rows_e = kGateUp ? 2 * A.rows : A.rows;
+  const uint8_t* __restrict__ wbase = A.wp + static_cast<size_t>(we.e) * rows_e * (red >> 1);
+  const uint8_t* __restrict__ sbase = A.ws + static_cast<size_t>(we.e) * rows_e * RB;
+  const uint32_t wo0 = static_cast<uint32_t>(n) * (red >> 1), wo1 = static_cast<uint32_t>(n + A.rows) * (red >> 1);
+  const size_t row0 = static_cast<size_t>(we.e) * rows_e + n;  // bias index of the gate (or single) row
+  const size_t row1 = row0 + A.rows;                             // bias index of the up row
+  auto ldw = [&](uint32_t off, int b) { return *reinterpret_cast<const uint4*>(wbase + off + 16u * b); };
+  // scale strips of the tile's rows, staged in LDS: [kRowsPerWG][RB] (gate/single), then up
+  unsigned char* sstrip = reinterpret_cast<unsigned char*>(xs) + kGemvMaxTokens * red * 2;
+  const int strip = kRowsPerWG * RB;
+  const uint8_t* ss0 = sbase + static_cast<size_t>(tile * kRowsPerWG) * RB;
+  const uint8_t* ss1 = sbase + static_cast<size_t>(tile * kRowsPerWG + A.rows) * RB;
+  auto lds_scale = [&](int which, int b) -> uint32_t { return sstrip[which * strip + g * RB + b]; };
+  const int nmax = (RB + kLanesPerRow - 1) / kLanesPerRow;  // ring steps (uniform)
+  const int Te = we.Te;
+
+  // Token passes of up to kGemvMaxTokens routes; one pass unless repeated ids
+  // gave the expert more routes while the MFMA regime is off.
+  for (int t0 = 0; t0 < Te; t0 += kGemvMaxTokens) {
+    const int nt = min(kGemvMaxTokens, Te - t0);
+    const int n_stage = nt * RV;
+
+    // 1. activation rows of the pass: direct global -> LDS copies (16 B per
+    //    lane; a wave's copy fills 1 KB of LDS contiguously), no registers
+    // activation row of each token of the pass (uniform)
+    const uint4* src_row[kGemvMaxTokens];
+#pragma unroll
+    for (int t = 0; t < kGemvMaxTokens; ++t) {
+      const int tt = min(t0 + t, Te - 1);
+      int row = we.p0 + tt;  // down projection: row of the intermediate
+      if (kGateUp) {
+        int tok = we.tok[0];
+#pragma unroll
+        for (int u = 1; u < kGemvMaxTokens; ++u) tok = tt == u ? we.tok[u] : tok;
+        row = tt < kGemvMaxTokens ? tok : A.routes[we.p0 + tt] / A.top_k;
+      }
+      src_row[t] = reinterpret_cast<const uint4*>(A.in + static_cast<size_t>(row) * red);
+    }
+#pragma unroll 1
+    for (int i = tid; i < n_stage; i += 256) {
+      {
+        int t = 0, c = i;
+#pragma unroll
+        for (int u = 1; u < kGemvMaxTokens; ++u) {
+          const bool next = c >= RV;
+          t = next ? u : t;
+          c = next ? c - RV : c;
+        }
+        const uint4* src = src_row[0];
+#pragma unroll
+        for (int u = 1; u < kGemvMaxTokens; ++u) src = t == u ? src_row[u] : src;
+        __builtin_amdgcn_global_load_lds(src + c,
+                                         reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                             reinterpret_cast<uintptr_t>(xs + (i & ~63))),
+                                         16, 0, 0);
+      }
+    }
+    if (t0 == 0) {
+      dma_strip(ss0, sstrip, strip);
+      if (kGateUp) dma_strip(ss1, sstrip + strip, strip);
+    }
+    // 2. weight ring, unconditional (indices clamped to the row)
+    uint4 r0[kRing], r1[kRing];
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) {
+      const int b = min(q + kLanesPerRow * j, RB - 1);
+      r0[j] = ldw(wo0, b);
+      if (kGateUp) r1[j] = ldw(wo1, b);
+    }
+    __syncthreads();
+
+    float acc0[kGemvMaxTokens], acc1[kGemvMaxTokens];
+#pragma unroll
+    for (int t = 0; t < kGemvMaxTokens; ++t) acc0[t] = acc1[t] = 0.0f;
+
+    for (int j0 = 0; j0 < nmax; j0 += kRing) {
+#pragma unroll
+      for (int s = 0; s < kRing; ++s) {
+        const int b = q + kLanesPerRow * (j0 + s);
+        const bool valid = b < RB;             // also false past the last ring step
+        const int bc = min(b, RB - 1);
+        // a zero scale turns a ragged-tail block into zeros
+        const float sc0 = valid ? e8m0_to_f32(lds_scale(0, bc)) : 0.0f;
+        const float sc1 = kGateUp && valid ? e8m0_to_f32(lds_scale(1, bc)) : 0.0f;
+        const uint32_t d0[4] = {r0[s].x, r0[s].y, r0[s].z, r0[s].w};
+        uint32_t d1[4] = {0, 0, 0, 0};
+        if (kGateUp) {
+          d1[0] = r1[s].x;
+          d1[1] = r1[s].y;
+          d1[2] = r1[s].z;
+          d1[3] = r1[s].w;
+        }
+        const int bn = min(b + kLanesPerRow * kRing, RB - 1);
+        r0[s] = ldw(wo0, bn);
+        if (kGateUp) r1[s] = ldw(wo1, bn);
+#pragma unroll
+        for (int dw = 0; dw < 4; ++dw) {
+          const bf16x2 g0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d0[dw], sc0, 0);
+          const bf16x2 g1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d0[dw], sc0, 1);
+          const bf16x2 g2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d0[dw], sc0, 2);
+          const bf16x2 g3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d0[dw], sc0, 3);
+          bf16x2 u0, u1, u2, u3;
+          if (kGateUp) {
+            u0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d1[dw], sc1, 0);
+            u1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d1[dw], sc1, 1);
+            u2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d1[dw], sc1, 2);
+            u3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d1[dw], sc1, 3);
+          }
+#pragma unroll
+          for (int t = 0; t < kGemvMaxTokens; ++t) {
+            if (t < nt) {
+              const uint4 xv = xs[t * RV + bc * 4 + dw];
+              acc0[t] = dot2(g3, xv.w, dot2(g2, xv.z, dot2(g1, xv.y, dot2(g0, xv.x, acc0[t]))));
+              if (kGateUp) acc1[t] = dot2(u3, xv.w, dot2(u2, xv.z, dot2(u1, xv.y, dot2(u0, xv.x, acc1[t]))));
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep live ranges per ring slot
+      }
+    }
+
+#pragma unroll
+    for (int t = 0; t < kGemvMaxTokens; ++t) {
+      acc0[t] = row_sum<kLanesPerRow>(acc0[t]);
+      if (kGateUp) acc1[t] = row_sum<kLanesPerRow>(acc1[t]);
+    }
+    if (q == 0) {
+      const float b0 = A.bias != nullptr ? bf16_bits_to_f32(A.bias[row0]) : 0.0f;
+      const float b1 = (kGateUp && A.bias != nullptr) ? bf16_bits_to_f32(A.bias[row1]) : 0.0f;
+#pragma unroll
+      for (int t = 0; t < kGemvMaxTokens; ++t) {
+        if (t < nt) {
+          const size_t p = static_cast<size_t>(we.p0 + t0 + t);
+          if (kGateUp) {
+            A.a_out[p * A.rows + n] =
+                f32_to_bf16_rne(activate(acc0[t] + b0, acc1[t] + b1, A.act_kind, A.alpha, A.limit));
+          } else {
+            A.o_out[p * A.rows + n] = acc0[t] + b0;
+          }
+        }
+      }
+    }
+    if (t0 + kGemvMaxTokens < Te) __syncthreads();  // xs is restaged by the next pass
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA regime
+// ---------------------------------------------------------------------------
+// Work item: 64 rows (row pairs) of one expert, 4 waves x 16 rows.  The
+// reduction runs in chunks of 4 MX blocks (128 values).  Per chunk, lane
+// (r, q) of a wave decodes block q of its row r (A operand) and reads 64 bytes
+// of token r's activations for the same block from LDS (B operand).  The
+// activation chunk of the pass's tokens is shared by the 4 waves through an
+// LDS double buffer; both it and the weights stream through register rings
+// kRing chunks deep, with the loop unrolled by the ring depth so every slot
+// stays in its own registers and the compiler can count outstanding loads
+// exactly.  One LDS-only barrier per chunk; no branches inside the ring.
+namespace {
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+}  // namespace
+
+template <bool kGateUp, int kGroups>
+__global__ __launch_bounds__(256, 2) void mfma_kernel(ExpertArgs A) {
+  constexpr int kTokens = 16 * kGroups;
+  constexpr int kBuf = kTokens * kXRowBytes;
+  constexpr int kRing = 4;
+  extern __shared__ __align__(16) unsigned char lds[];  // [2][kTokens][kXRowBytes], then the scale strips
+
+  const int tiles = (A.rows + kMfmaRows - 1) / kMfmaRows;
+  const int item = blockIdx.x / tiles;         // < E_local: the entry load is always in bounds
+  const int n_items = A.plan->n_mfma;
+  const WorkEntry we = A.list[item];
+  if (item >= n_items) return;  // whole workgroup
+  const int tile = blockIdx.x - item * tiles;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, q = lane >> 4;
+  const int wrow0 = tile * kMfmaRows + wave * 16;
+  const bool wave_ok = wrow0 < A.rows;              // rows past the end: staging and barriers only
+  const int wrow = min(wrow0 + r, A.rows - 1);      // clamped so that every load stays in the expert
+  const int red = A.red, RB = red >> 5;
+  const int NC = (RB + kChunkBlocks - 1) / kChunkBlocks;
+  const int rows_e = kGateUp ? 2 * A.rows : A.rows;
+  const uint8_t* __restrict__ wbase = A.wp + static_cast<size_t>(we.e) * rows_e * (red >> 1);
+  const uint8_t* __restrict__ sbase = A.ws + static_cast<size_t>(we.e) * rows_e * RB;
+  const uint32_t wo0 = static_cast<uint32_t>(wrow) * (red >> 1);
+  const uint32_t wo1 = static_cast<uint32_t>(wrow + A.rows) * (red >> 1);
+  // scale strips of the tile's rows (clamped to the expert), staged in LDS once:
+  // [kMfmaRows][RB] (gate/single), then up
+  const int srows = min(kMfmaRows, A.rows - tile * kMfmaRows);
+  unsigned char* sstrip = lds + 2 * kBuf;
+  const int strip = kMfmaRows * RB;
+  dma_strip(sbase + static_cast<size_t>(tile * kMfmaRows) * RB, sstrip, srows * RB);
+  if (kGateUp) dma_strip(sbase + static_cast<size_t>(tile * kMfmaRows + A.rows) * RB, sstrip + strip, srows * RB);
+  const int srow_l = min(wave * 16 + r, srows - 1);  // this lane's row in the strips
+
+  for (int tp0 = 0; tp0 < we.Te; tp0 += kTokens) {
+    const int nt = min(kTokens, we.Te - tp0);
+    const int NG = (nt + 15) >> 4;
+
+    // staging role: uint4 piece u = tid + 256*k of the chunk's [kTokens][16]
+    // pieces.  Loads are unconditional (tokens past the pass read the first
+    // token's row, chunks past the row read the last chunk); the mask is
+    // applied when the piece is written to LDS.
+    const uint4* srow[kGroups];
+    int spiece[kGroups];
+    bool stok[kGroups];
+#pragma unroll
+    for (int k = 0; k < kGroups; ++k) {
+      const int u = tid + 256 * k;
+      const int st = u >> 4;
+      spiece[k] = u & 15;
+      stok[k] = st < nt;
+      const int p = we.p0 + tp0 + (st < nt ? st : 0);
+      const int row = A.routes != nullptr ? A.routes[p] / A.top_k : p;
+      srow[k] = reinterpret_cast<const uint4*>(A.in + static_cast<size_t>(row) * red);
+    }
+    const int last_piece = (red >> 3) - 1;  // last uint4 of an activation row
+    auto xload = [&](int c, uint4 (&dst)[kGroups]) {
+#pragma unroll
+      for (int k = 0; k < kGroups; ++k) dst[k] = srow[k][min(c * 16 + spiece[k], last_piece)];
+    };
+    auto xstore = [&](int c, const uint4 (&src)[kGroups]) {
+#pragma unroll
+      for (int k = 0; k < kGroups; ++k) {
+        const int u = tid + 256 * k;
+        const bool ok = stok[k] && c * kChunkBlocks + (spiece[k] >> 2) < RB;
+        *reinterpret_cast<uint4*>(lds + (c & 1) * kBuf + (u >> 4) * kXRowBytes + (u & 15) * 16) =
+            ok ? src[k] : make_uint4(0, 0, 0, 0);
+      }
+    };
+
+    f32x4 acc0[kGroups], acc1[kGroups];
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      acc0[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      acc1[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    uint4 rw0[kRing], rw1[kRing], rx[kRing][kGroups];
+    auto wload = [&](int c, int slot) {
+      const int b = min(c * kChunkBlocks + q, RB - 1);
+      rw0[slot] = *reinterpret_cast<const uint4*>(wbase + wo0 + 16u * b);
+      if (kGateUp) rw1[slot] = *reinterpret_cast<const uint4*>(wbase + wo1 + 16u * b);
+    };
+
+    // prologue: chunks 0..kRing-1 in flight, chunk 0 staged in LDS
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) {
+      wload(s, s);
+      xload(s, rx[s]);
+    }
+    xstore(0, rx[0]);
+    xload(kRing, rx[0]);
+    lds_barrier();
+
+    const int rounds = (NC + kRing - 1) / kRing;
+    for (int c0 = 0; c0 < rounds * kRing; c0 += kRing) {
+#pragma unroll
+      for (int s = 0; s < kRing; ++s) {
+        const int c = c0 + s;
+        const bool valid = c * kChunkBlocks + q < RB;  // false past the row and past the last chunk
+        // a zero scale turns a ragged-tail block into zeros
+        bf16x8 a0[4], a1[4];
+        const int bs = min(c * kChunkBlocks + q, RB - 1);
+        const float sc0 = valid ? e8m0_to_f32(sstrip[srow_l * RB + bs]) : 0.0f;
+        a0[0] = decode_dword_bf16x8(rw0[s].x, sc0);
+        a0[1] = decode_dword_bf16x8(rw0[s].y, sc0);
+        a0[2] = decode_dword_bf16x8(rw0[s].z, sc0);
+        a0[3] = decode_dword_bf16x8(rw0[s].w, sc0);
+        if (kGateUp) {
+          const float sc1 = valid ? e8m0_to_f32(sstrip[strip + srow_l * RB + bs]) : 0.0f;
+          a1[0] = decode_dword_bf16x8(rw1[s].x, sc1);
+          a1[1] = decode_dword_bf16x8(rw1[s].y, sc1);
+          a1[2] = decode_dword_bf16x8(rw1[s].z, sc1);
+          a1[3] = decode_dword_bf16x8(rw1[s].w, sc1);
+        }
+        wload(c + kRing, s);
+        const unsigned char* xb = lds + (c & 1) * kBuf + q * 64;
+#pragma unroll
+        for (int tg = 0; tg < kGroups; ++tg) {
+          if (tg < NG) {
+            const unsigned char* xrow = xb + (tg * 16 + r) * kXRowBytes;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const bf16x8 bx = *reinterpret_cast<const bf16x8*>(xrow + g * 16);
+              acc0[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[g], bx, acc0[tg], 0, 0, 0);
+              if (kGateUp) acc1[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[g], bx, acc1[tg], 0, 0, 0);
+            }
+          }
+        }
+        // stage chunk c+1 (loaded kRing-1 chunks ago) and refill its register slot
+        const int sn = (s + 1) % kRing;  // compile-time after unrolling
+        xstore(c + 1, rx[sn]);
+        xload(c + 1 + kRing, rx[sn]);
+        lds_barrier();
+      }
+    }
+
+    // epilogue: lane holds rows wrow0 + 4q + i (i < 4) of token tg*16 + r
+    if (wave_ok) {
+      const int rowbase = wrow0 + 4 * q;
+      float b0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, b1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (A.bias != nullptr) {
+        const size_t bb = static_cast<size_t>(we.e) * rows_e + rowbase;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          b0[i] = bf16_bits_to_f32(A.bias[bb + i]);
+          if (kGateUp) b1[i] = bf16_bits_to_f32(A.bias[bb + A.rows + i]);
+        }
+      }
+#pragma unroll
+      for (int tg = 0; tg < kGroups; ++tg) {
+        const int tt = tg * 16 + r;
+        if (tg < NG && tt < nt) {
+          const size_t p = static_cast<size_t>(we.p0 + tp0 + tt);
+          if (kGateUp) {
+            uint16_t h[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              h[i] = f32_to_bf16_rne(
+                  activate(acc0[tg][i] + b0[i], acc1[tg][i] + b1[i], A.act_kind, A.alpha, A.limit));
+            uint2 pk;
+            pk.x = static_cast<uint32_t>(h[0]) | (static_cast<uint32_t>(h[1]) << 16);
+            pk.y = static_cast<uint32_t>(h[2]) | (static_cast<uint32_t>(h[3]) << 16);
+            *reinterpret_cast<uint2*>(A.a_out + p * A.rows + rowbase) = pk;
+          } else {
+            *reinterpret_cast<float4*>(A.o_out + p * A.rows + rowbase) =
+                make_float4(acc0[tg][0] + b0[0], acc0[tg][1] + b0[1], acc0[tg][2] + b0[2], acc0[tg][3] + b0[3]);
+          }
+        }
+      }
+    }
+    if (tp0 + kTokens < we.Te) lds_barrier();  // the next pass restages the buffers
+  }
+}
+
+template __global__ void gemv_kernel<true, 16>(ExpertArgs);
+template __global__ void gemv_kernel<true, 32>(ExpertArgs);
+template __global__ void gemv_kernel<false, 16>(ExpertArgs);
+template __global__ void gemv_kernel<false, 32>(ExpertArgs);
+template __global__ void mfma_kernel<true, 1>(ExpertArgs);
+template __global__ void mfma_kernel<true, 2>(ExpertArgs);
+template __global__ void mfma_kernel<true, 4>(ExpertArgs);
+template __global__ void mfma_kernel<false, 1>(ExpertArgs);
+template __global__ void mfma_kernel<false, 2>(ExpertArgs);
+template __global__ void mfma_kernel<false, 4>(ExpertArgs);
+
+// y[t, :] = sum over j (ascending) of w[t, j] * o[pos(t, j), :] for the
+// token's local routes; zeros for a token without one.  Fixed order, no
+// atomics, so the result is reproducible bit for bit.
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs A) {
+  const int t = blockIdx.y;
+  const int k4 = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (k4 >= A.K) return;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int j = 0; j < A.top_k; ++j) {
+    const int r = t * A.top_k + j;
+    const int p = A.pos[r];
+    if (p < 0) continue;
+    const float wt = A.weights[r];
+    const float4 o = *reinterpret_cast<const float4*>(A.o + static_cast<size_t>(p) * A.K + k4);
+    acc.x = __fadd_rn(acc.x, __fmul_rn(wt, o.x));
+    acc.y = __fadd_rn(acc.y, __fmul_rn(wt, o.y));
+    acc.z = __fadd_rn(acc.z, __fmul_rn(wt, o.z));
+    acc.w = __fadd_rn(acc.w, __fmul_rn(wt, o.w));
+  }
+  uint2 packed;
+  packed.x = static_cast<uint32_t>(f32_to_bf16_rne(acc.x)) | (static_cast<uint32_t>(f32_to_bf16_rne(acc.y)) << 16);
+  packed.y = static_cast<uint32_t>(f32_to_bf16_rne(acc.z)) | (static_cast<uint32_t>(f32_to_bf16_rne(acc.w)) << 16);
+  *reinterpret_cast<uint2*>(A.out + static_cast<size_t>(t) * A.K + k4) = packed;
+}
+
+// One thread per 32-value MX block: 16 packed bytes + 1 scale byte.
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ packed,
+                                                      const uint8_t* __restrict__ scales, int64_t n_blocks,
+                                                      int out_bf16, void* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n_blocks) return;
+  const uint4 q = reinterpret_cast<const uint4*>(packed)[i];
+  const float s = e8m0_to_f32(scales[i]);
+  if (out_bf16) {
+    bf16x2 v[16];
+    decode_block_bf16(q, s, v);
+    uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + i * 32);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint4 u;
+      u.x = __builtin_bit_cast(uint32_t, v[4 * c + 0]);
+      u.y = __builtin_bit_cast(uint32_t, v[4 * c + 1]);
+      u.z = __builtin_bit_cast(uint32_t, v[4 * c + 2]);
+      u.w = __builtin_bit_cast(uint32_t, v[4 * c + 3]);
+      o[c] = u;
+    }
+  } else {
+    float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + i * 32);
+    const uint32_t d[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      f32x2 v[4];
+      decode_dword_f32(d[c], s, v);
+      o[2 * c + 0] = make_float4(v[0][0], v[0][1], v[1][0], v[1][1]);
+      o[2 * c + 1] = make_float4(v[2][0], v[2][1], v[3][0], v[3][1]);
+    }
+  }
+}
+
+}  // namespace moe

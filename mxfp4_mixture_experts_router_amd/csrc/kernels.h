@@ -1,4 +1,5 @@
-// Kernel declarations and the size limits the host checks before launching.
+// Kernel declarations, the device plan layout, and the size limits the host
+// checks before launching.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,46 +12,72 @@ namespace moe {
 constexpr int kRouteMaxPerLane = 16;                    // E_global <= 1024 in logits mode
 constexpr int kMaxGlobalExpertsRouted = 64 * kRouteMaxPerLane;
 constexpr int kMaxTopK = 64;
-constexpr int kBucketSegments = 16;                     // waves of the bucketing workgroup
+constexpr int kPlanWaves = 16;                          // waves of the planning workgroup
 constexpr int kMaxLocalExperts = 512;
-constexpr int kMaxDim = 8192;                           // K and I (4 staged rows of bf16 fit 64 KB of LDS)
+constexpr int kMaxDim = 8192;                           // K and I
+constexpr int kFusedRouteTokens = 64;                   // T up to this: routing runs inside the plan kernel
 
-// Rows per expert-kernel work item: 16 lane-groups of 16 lanes each own one
-// row (w2) or one [gate; up] row pair (w13).
-constexpr int kRowsPerTile = 16;
-// Tokens whose activations are staged in LDS at once by the GEMV kernels.
-constexpr int kGemvTokens = 4;
+// Regime per touched expert, decided on the device from its route count:
+// up to kGemvMaxTokens routes -> VALU GEMV (gemv_kernel); more -> bf16 MFMA
+// (mfma_kernel), 4 waves x 16 rows per work item, tokens in groups of 16.
+constexpr int kGemvMaxTokens = 2;
+constexpr int kMfmaRows = 64;
+constexpr int kChunkBlocks = 4;                         // MX blocks (of 32 values) per MFMA step
+constexpr int kXRowBytes = kChunkBlocks * 64 + 16;      // LDS row of one staged chunk, padded
 
-__global__ void route_topk_kernel(const float* logits, int T, int E, int k, int scoring, int32_t* ids,
-                                  float* weights);
-__global__ void bucket_kernel(const int32_t* ids, int R, int E_l, int offset, int32_t* counts,
-                              int32_t* offsets, int32_t* routes, int32_t* pos, int32_t* touched,
-                              Plan* plan, int32_t* routes_out, const float* w_in, float* w_out);
+// One touched local expert, written by the plan kernel into the list of its
+// regime.
+struct WorkEntry {
+  int32_t e;        // local expert
+  int32_t p0;       // first route position of the expert in plan order
+  int32_t Te;       // routes of the expert
+  int32_t tok[kGemvMaxTokens];  // token of the first routes (GEMV entries)
+  int32_t pad[8 - 3 - kGemvMaxTokens];
+};
+static_assert(sizeof(WorkEntry) == 32, "WorkEntry is 32 bytes");
 
-struct W13Args {
-  const uint16_t* x;
-  const uint8_t* w13p;
-  const uint8_t* w13s;
-  const uint16_t* b13;
-  const int32_t* offsets;
-  const int32_t* routes;
-  const int32_t* touched;
-  const Plan* plan;
-  uint16_t* a;
-  int K, I, top_k, act;
-  float alpha, limit;
+// Header of the device plan, at the start of the workspace.
+struct Plan {
+  int32_t n_touched;   // local experts with at least one route
+  int32_t R_local;     // local routes
+  int32_t n_gemv;      // experts in the GEMV list
+  int32_t n_mfma;      // experts in the MFMA list
+  int32_t pad[60];
 };
 
-struct W2Args {
-  const uint16_t* a;
-  const uint8_t* w2p;
-  const uint8_t* w2s;
-  const uint16_t* b2;
-  const int32_t* offsets;
-  const int32_t* touched;
+struct PlanArgs {
+  const float* logits;     // router-logits mode, or nullptr
+  const int32_t* ids_in;   // ids (caller's, or written by route_topk_kernel), used when logits == nullptr
+  const float* w_in;       // caller's weights to copy into the workspace (ids mode), or nullptr
+  int T, top_k, E_global, E_local, offset, scoring;
+  int mfma_enabled;        // the MFMA kernels run for this call (T > kGemvMaxTokens); else all experts go to GEMV
+  int32_t* ids_ws;         // [R] routed ids (logits mode)
+  float* weights_ws;       // [R] routing weights
+  int32_t* counts;         // [E_l]
+  int32_t* offsets;        // [E_l + 1]
+  int32_t* routes;         // [R] route index by plan position
+  int32_t* pos;            // [R] plan position by route index, -1 if not local
+  WorkEntry* gemv_list;    // [E_l]
+  WorkEntry* mfma_list;    // [E_l]
+  Plan* plan;
+  int32_t* routes_out;     // bucket hook: copy of routes padded with -1, or nullptr
+};
+
+struct ExpertArgs {
+  const uint16_t* in;      // gate/up: x [T, K]; down: a [R, I]  (bf16)
+  const int32_t* routes;   // gate/up: activation row of position p is routes[p] / top_k; down: nullptr (row p)
+  int top_k;
+  const uint8_t* wp;       // packed weights
+  const uint8_t* ws;       // scales
+  const uint16_t* bias;    // bf16 bias or nullptr
+  const WorkEntry* list;   // the kernel's expert list
   const Plan* plan;
-  float* o;      // [R, K] fp32 per-route output
-  int K, I;
+  int red;                 // reduction length: K (gate/up) or I (down)
+  int rows;                // output rows per expert: I row pairs (gate/up) or K (down)
+  uint16_t* a_out;         // gate/up output [R, I] bf16
+  float* o_out;            // down output [R, K] fp32
+  int act_kind;
+  float alpha, limit;
 };
 
 struct CombineArgs {
@@ -61,9 +88,17 @@ struct CombineArgs {
   int T, K, top_k;
 };
 
-__global__ void w13_gemv_kernel(W13Args args);
-__global__ void w2_gemv_kernel(W2Args args);
-__global__ void combine_kernel(CombineArgs args);
+__global__ void route_topk_kernel(const float* logits, int T, int E, int k, int scoring, int32_t* ids,
+                                  float* weights);
+__global__ void plan_kernel(PlanArgs P);
+// GEMV regime: kLanesPerRow lanes stream one row (or [gate; up] row pair);
+// a workgroup of 256 lanes covers 256 / kLanesPerRow rows of one expert.
+template <bool kGateUp, int kLanesPerRow>
+__global__ void gemv_kernel(ExpertArgs A);
+// MFMA regime: 64 rows of one expert per workgroup, kGroups groups of 16 tokens per pass.
+template <bool kGateUp, int kGroups>
+__global__ void mfma_kernel(ExpertArgs A);
+__global__ void combine_kernel(CombineArgs A);
 __global__ void dequant_kernel(const uint8_t* packed, const uint8_t* scales, int64_t n_blocks, int out_bf16,
                                void* out);
 

@@ -18,10 +18,9 @@ namespace {
 
 using moe::Plan;
 
-constexpr int kMaxGrid = 16384;
 
 struct Layout {
-  size_t plan, ids, weights, counts, offsets, touched, routes, pos, a, o, total;
+  size_t plan, ids, weights, counts, offsets, gemv_list, mfma_list, routes, pos, a, o, total;
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -40,7 +39,8 @@ Layout make_layout(const moe_mxfp4_desc& d) {
   L.weights = take(R * 4);
   L.counts = take(static_cast<size_t>(d.E_local) * 4);
   L.offsets = take((static_cast<size_t>(d.E_local) + 1) * 4);
-  L.touched = take(static_cast<size_t>(d.E_local) * 4);
+  L.gemv_list = take(static_cast<size_t>(d.E_local) * sizeof(moe::WorkEntry));
+  L.mfma_list = take(static_cast<size_t>(d.E_local) * sizeof(moe::WorkEntry));
   L.routes = take(R * 4);
   L.pos = take(R * 4);
   L.a = take(R * d.I * 2);
@@ -85,74 +85,146 @@ int tokens_bound(const moe_mxfp4_desc& d) {
   return static_cast<int>(std::min<int64_t>(d.E_local, static_cast<int64_t>(d.T) * d.top_k));
 }
 
-void enqueue_bucket(const moe_mxfp4_desc& d, const int32_t* ids, const float* w_in, void* ws, hipStream_t s,
-                    int32_t* counts_out, int32_t* offsets_out, int32_t* routes_out) {
+// The MFMA regime is used only when an expert can hold more than
+// kGemvMaxTokens routes of distinct tokens, i.e. T > kGemvMaxTokens; the plan
+// kernel and the launches below apply the same rule.
+bool mfma_enabled(const moe_mxfp4_desc& d) { return d.T > moe::kGemvMaxTokens; }
+
+moe::PlanArgs plan_args(const moe_mxfp4_desc& d, void* ws) {
   const Layout L = make_layout(d);
-  const int R = d.T * d.top_k;
-  hipLaunchKernelGGL(moe::bucket_kernel, dim3(1), dim3(1024), 0, s, ids, R, d.E_local, d.expert_offset,
-                     counts_out ? counts_out : at<int32_t>(ws, L.counts),
-                     offsets_out ? offsets_out : at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.routes),
-                     at<int32_t>(ws, L.pos), at<int32_t>(ws, L.touched), at<Plan>(ws, L.plan), routes_out, w_in,
-                     at<float>(ws, L.weights));
+  moe::PlanArgs P{};
+  P.T = d.T;
+  P.top_k = d.top_k;
+  P.E_global = d.E_global;
+  P.E_local = d.E_local;
+  P.offset = d.expert_offset;
+  P.scoring = d.scoring;
+  P.mfma_enabled = mfma_enabled(d) ? 1 : 0;
+  P.ids_ws = at<int32_t>(ws, L.ids);
+  P.weights_ws = at<float>(ws, L.weights);
+  P.counts = at<int32_t>(ws, L.counts);
+  P.offsets = at<int32_t>(ws, L.offsets);
+  P.routes = at<int32_t>(ws, L.routes);
+  P.pos = at<int32_t>(ws, L.pos);
+  P.gemv_list = at<moe::WorkEntry>(ws, L.gemv_list);
+  P.mfma_list = at<moe::WorkEntry>(ws, L.mfma_list);
+  P.plan = at<Plan>(ws, L.plan);
+  return P;
 }
 
-// Routing (logits mode) and bucketing into the workspace.
+// Routing and bucketing into the workspace.  Small calls route inside the
+// plan kernel; larger ones route with one wave per token first.
 void enqueue_plan(const moe_mxfp4_desc& d, const float* logits, const int32_t* ids, const float* wts, void* ws,
                   hipStream_t s) {
-  const Layout L = make_layout(d);
-  if (logits != nullptr) {
-    int32_t* ids_ws = at<int32_t>(ws, L.ids);
+  moe::PlanArgs P = plan_args(d, ws);
+  if (logits != nullptr && d.T <= moe::kFusedRouteTokens) {
+    P.logits = logits;
+  } else if (logits != nullptr) {
     hipLaunchKernelGGL(moe::route_topk_kernel, dim3((d.T + 3) / 4), dim3(256), 0, s, logits, d.T, d.E_global,
-                       d.top_k, d.scoring, ids_ws, at<float>(ws, L.weights));
-    enqueue_bucket(d, ids_ws, nullptr, ws, s, nullptr, nullptr, nullptr);
+                       d.top_k, d.scoring, P.ids_ws, P.weights_ws);
+    P.ids_in = P.ids_ws;
   } else {
-    enqueue_bucket(d, ids, wts, ws, s, nullptr, nullptr, nullptr);
+    P.ids_in = ids;
+    P.w_in = wts;
+  }
+  hipLaunchKernelGGL(moe::plan_kernel, dim3(1), dim3(1024), 0, s, P);
+}
+
+void enqueue_bucket_hook(const moe_mxfp4_desc& d, const int32_t* ids, void* ws, hipStream_t s, int32_t* counts,
+                         int32_t* offsets, int32_t* routes_out) {
+  moe::PlanArgs P = plan_args(d, ws);
+  P.ids_in = ids;
+  P.counts = counts;
+  P.offsets = offsets;
+  P.routes_out = routes_out;
+  hipLaunchKernelGGL(moe::plan_kernel, dim3(1), dim3(1024), 0, s, P);
+}
+
+// Both regimes of one projection.  Grids are host-side upper bounds: at most
+// min(E_local, T*top_k) experts are touched, and at most T*top_k / (G+1) of
+// them have more than G = kGemvMaxTokens routes; workgroups past the lists exit.
+// With T <= G every expert is in the GEMV list (the GEMV kernel loops over
+// token pairs if repeated ids give an expert more routes); otherwise experts
+// with more than G routes are in the MFMA list, whose token groups per pass
+// follow T.
+void enqueue_expert_pair(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs A, const Layout& L, void* ws,
+                         hipStream_t s) {
+  const int64_t touched = tokens_bound(d);
+  const int rows = A.rows, red = A.red;
+  const int lanes = red > 4096 ? 32 : 16;
+  const int rows_per_wg = 256 / lanes;
+  {
+    moe::ExpertArgs G = A;
+    G.list = at<moe::WorkEntry>(ws, L.gemv_list);
+    const int64_t grid = std::max<int64_t>(1, touched * (rows / rows_per_wg));
+    const size_t lds = static_cast<size_t>(moe::kGemvMaxTokens) * red * 2 +
+                       static_cast<size_t>(gate_up ? 2 : 1) * rows_per_wg * (red / 32);
+    const dim3 g(static_cast<unsigned>(grid));
+    if (gate_up) {
+      if (lanes == 16) hipLaunchKernelGGL((moe::gemv_kernel<true, 16>), g, dim3(256), lds, s, G);
+      else hipLaunchKernelGGL((moe::gemv_kernel<true, 32>), g, dim3(256), lds, s, G);
+    } else {
+      if (lanes == 16) hipLaunchKernelGGL((moe::gemv_kernel<false, 16>), g, dim3(256), lds, s, G);
+      else hipLaunchKernelGGL((moe::gemv_kernel<false, 32>), g, dim3(256), lds, s, G);
+    }
+  }
+  const int64_t R = static_cast<int64_t>(d.T) * d.top_k;
+  const int64_t mfma_experts = std::min<int64_t>(d.E_local, R / (moe::kGemvMaxTokens + 1));
+  if (mfma_experts > 0 && mfma_enabled(d)) {
+    moe::ExpertArgs M = A;
+    M.list = at<moe::WorkEntry>(ws, L.mfma_list);
+    const int64_t grid = mfma_experts * ((rows + moe::kMfmaRows - 1) / moe::kMfmaRows);
+    const int groups = d.T <= 16 ? 1 : (d.T <= 32 ? 2 : 4);
+    const size_t lds = 2 * static_cast<size_t>(16 * groups) * moe::kXRowBytes +
+                       static_cast<size_t>(gate_up ? 2 : 1) * moe::kMfmaRows * (red / 32);
+    const dim3 g(static_cast<unsigned>(grid));
+    if (gate_up) {
+      if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<true, 1>), g, dim3(256), lds, s, M);
+      else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<true, 2>), g, dim3(256), lds, s, M);
+      else hipLaunchKernelGGL((moe::mfma_kernel<true, 4>), g, dim3(256), lds, s, M);
+    } else {
+      if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<false, 1>), g, dim3(256), lds, s, M);
+      else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<false, 2>), g, dim3(256), lds, s, M);
+      else hipLaunchKernelGGL((moe::mfma_kernel<false, 4>), g, dim3(256), lds, s, M);
+    }
   }
 }
 
 void enqueue_w13(const moe_mxfp4_desc& d, const uint16_t* x, const uint8_t* w13p, const uint8_t* w13s,
                  const uint16_t* b13, uint16_t* a, void* ws, hipStream_t s) {
   const Layout L = make_layout(d);
-  moe::W13Args A;
-  A.x = x;
-  A.w13p = w13p;
-  A.w13s = w13s;
-  A.b13 = b13;
-  A.offsets = at<int32_t>(ws, L.offsets);
+  moe::ExpertArgs A{};
+  A.in = x;
   A.routes = at<int32_t>(ws, L.routes);
-  A.touched = at<int32_t>(ws, L.touched);
-  A.plan = at<Plan>(ws, L.plan);
-  A.a = a != nullptr ? a : at<uint16_t>(ws, L.a);
-  A.K = d.K;
-  A.I = d.I;
   A.top_k = d.top_k;
-  A.act = d.activation;
+  A.wp = w13p;
+  A.ws = w13s;
+  A.bias = b13;
+  A.plan = at<Plan>(ws, L.plan);
+  A.red = d.K;
+  A.rows = d.I;
+  A.a_out = a != nullptr ? a : at<uint16_t>(ws, L.a);
+  A.act_kind = d.activation;
   A.alpha = d.swiglu_alpha;
   A.limit = d.swiglu_limit;
-  const int64_t work = static_cast<int64_t>(tokens_bound(d)) * (d.I / moe::kRowsPerTile);
-  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(work, kMaxGrid)));
-  const size_t lds = static_cast<size_t>(moe::kGemvTokens) * d.K * 2;
-  hipLaunchKernelGGL(moe::w13_gemv_kernel, dim3(grid), dim3(256), lds, s, A);
+  enqueue_expert_pair(d, true, A, L, ws, s);
 }
 
 void enqueue_w2_combine(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_t* w2p, const uint8_t* w2s,
                         const uint16_t* b2, uint16_t* out, void* ws, hipStream_t s) {
   const Layout L = make_layout(d);
-  moe::W2Args A;
-  A.a = a != nullptr ? a : at<uint16_t>(ws, L.a);
-  A.w2p = w2p;
-  A.w2s = w2s;
-  A.b2 = b2;
-  A.offsets = at<int32_t>(ws, L.offsets);
-  A.touched = at<int32_t>(ws, L.touched);
+  moe::ExpertArgs A{};
+  A.in = a != nullptr ? a : at<uint16_t>(ws, L.a);
+  A.routes = nullptr;
+  A.top_k = d.top_k;
+  A.wp = w2p;
+  A.ws = w2s;
+  A.bias = b2;
   A.plan = at<Plan>(ws, L.plan);
-  A.o = at<float>(ws, L.o);
-  A.K = d.K;
-  A.I = d.I;
-  const int64_t work = static_cast<int64_t>(tokens_bound(d)) * (d.K / moe::kRowsPerTile);
-  const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(work, kMaxGrid)));
-  const size_t lds = static_cast<size_t>(moe::kGemvTokens) * d.I * 2;
-  hipLaunchKernelGGL(moe::w2_gemv_kernel, dim3(grid), dim3(256), lds, s, A);
+  A.red = d.I;
+  A.rows = d.K;
+  A.o_out = at<float>(ws, L.o);
+  enqueue_expert_pair(d, false, A, L, ws, s);
 
   moe::CombineArgs C;
   C.o = at<float>(ws, L.o);
@@ -197,7 +269,9 @@ int moe_mxfp4_decode(const moe_mxfp4_desc* desc, const uint16_t* x, const float*
   if ((st = check_routing(d, router_logits, topk_ids, topk_weights)) != MOE_OK) return st;
   if (d.T == 0) return MOE_OK;
   if (!x || !w13_packed || !w13_scales || !w2_packed || !w2_scales || !out) return MOE_ERR_NULL;
-  if (!aligned16(x) || !aligned16(w13_packed) || !aligned16(w2_packed) || !aligned16(out)) return MOE_ERR_ALIGN;
+  if (!aligned16(x) || !aligned16(w13_packed) || !aligned16(w2_packed) || !aligned16(out) || !aligned16(w13_scales) ||
+      !aligned16(w2_scales))
+    return MOE_ERR_ALIGN;
   if ((st = check_workspace(d, workspace, workspace_bytes)) != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   enqueue_plan(d, router_logits, topk_ids, topk_weights, workspace, s);
@@ -224,7 +298,7 @@ int moe_mxfp4_gate_up(const moe_mxfp4_desc* desc, const uint16_t* x, const uint8
   if (st != MOE_OK) return st;
   if (desc->T == 0) return MOE_OK;
   if (!x || !w13_packed || !w13_scales) return MOE_ERR_NULL;
-  if (!aligned16(x) || !aligned16(w13_packed) || !aligned16(a)) return MOE_ERR_ALIGN;
+  if (!aligned16(x) || !aligned16(w13_packed) || !aligned16(w13_scales) || !aligned16(a)) return MOE_ERR_ALIGN;
   if ((st = check_workspace(*desc, workspace, workspace_bytes)) != MOE_OK) return st;
   enqueue_w13(*desc, x, w13_packed, w13_scales, w13_bias, a, workspace, static_cast<hipStream_t>(stream));
   return launch_status();
@@ -237,7 +311,7 @@ int moe_mxfp4_down(const moe_mxfp4_desc* desc, const uint16_t* a, const uint8_t*
   if (st != MOE_OK) return st;
   if (desc->T == 0) return MOE_OK;
   if (!w2_packed || !w2_scales || !out) return MOE_ERR_NULL;
-  if (!aligned16(a) || !aligned16(w2_packed) || !aligned16(out)) return MOE_ERR_ALIGN;
+  if (!aligned16(a) || !aligned16(w2_packed) || !aligned16(w2_scales) || !aligned16(out)) return MOE_ERR_ALIGN;
   if ((st = check_workspace(*desc, workspace, workspace_bytes)) != MOE_OK) return st;
   enqueue_w2_combine(*desc, a, w2_packed, w2_scales, w2_bias, out, workspace, static_cast<hipStream_t>(stream));
   return launch_status();
@@ -263,7 +337,7 @@ int moe_mxfp4_bucket(const moe_mxfp4_desc* desc, const int32_t* topk_ids, int32_
   if (desc->T == 0) return MOE_OK;
   if (!topk_ids || !counts || !offsets || !routes) return MOE_ERR_NULL;
   if ((st = check_workspace(*desc, workspace, workspace_bytes)) != MOE_OK) return st;
-  enqueue_bucket(*desc, topk_ids, nullptr, workspace, static_cast<hipStream_t>(stream), counts, offsets, routes);
+  enqueue_bucket_hook(*desc, topk_ids, workspace, static_cast<hipStream_t>(stream), counts, offsets, routes);
   return launch_status();
 }
 

@@ -108,6 +108,7 @@ def test_decode_error_paths():
     assert _decode(d, out=None) == E.MOE_ERR_NULL
     assert _decode(d, x=A_MIS) == E.MOE_ERR_ALIGN
     assert _decode(d, w13p=A_MIS) == E.MOE_ERR_ALIGN
+    assert _decode(d, w2s=A_MIS) == E.MOE_ERR_ALIGN
     assert _decode(d, out=A_MIS) == E.MOE_ERR_ALIGN
     assert _decode(d, ws=None) == E.MOE_ERR_WORKSPACE
     assert _decode(d, ws=A_MIS) == E.MOE_ERR_ALIGN

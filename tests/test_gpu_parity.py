@@ -196,7 +196,8 @@ def test_gate_up_step(case, T):
     Rl = len(ref["routes"])
     got = bf16_to_np(a)[:Rl]
     _assert_close(got, ref["a"], f"a case{case} T{T}")
-    assert np.mean(got == ref["a"]) > 0.98   # bf16 values agree except rare rounding-boundary cases
+    if Rl:
+        assert np.mean(got == ref["a"]) > 0.98   # bf16 values agree except rare rounding-boundary cases
 
 
 @pytest.mark.parametrize("case", range(len(STEP_CASES)))
@@ -248,6 +249,9 @@ LAYER_CASES = [
                            scoring="sigmoid", scale_lo=115, scale_hi=127), 9, 1.0),
     ("many-tokens-per-expert", dict(K=512, I=768, E_global=2, E_local=2, top_k=2), 37, 1.0),
     ("odd-blocks", dict(K=96, I=224, E_global=5, E_local=5, top_k=3, activation="swiglu_oai", bias=True), 11, 1.0),
+    ("two-mfma-passes", dict(K=256, I=128, E_global=1, E_local=1, top_k=1), 100, 1.0),
+    ("wide-k-mixed-regimes", dict(K=7168, I=2048, E_global=16, E_local=3, expert_offset=2, top_k=4,
+                                  scoring="sigmoid", scale_lo=115, scale_hi=127), 12, 1.0),
 ]
 
 
