@@ -115,9 +115,10 @@ int moe_mxfp4_workspace_bytes(const moe_mxfp4_desc* desc, size_t* bytes);
  *  workspace    device buffer of at least moe_mxfp4_workspace_bytes() bytes,
  *               16-byte aligned; contents on entry are ignored
  *
- * Pointers to x, the packed weights, the scales, out and workspace must be
- * 16-byte aligned (MOE_ERR_ALIGN); the same holds for every entry point below.  Preconditions not checked: finite x and
- * logits, buffers of the stated sizes.  Results are deterministic: no
+ * Pointers to x, the packed weights, the scales, the biases (when given), out
+ * and workspace must be 16-byte aligned (MOE_ERR_ALIGN); the same holds for
+ * every entry point below.  Preconditions not checked: finite x and logits,
+ * buffers of the stated sizes.  Results are deterministic: no
  * floating-point atomics; a call repeated on the same inputs is bit-identical.
  */
 int moe_mxfp4_decode(const moe_mxfp4_desc* desc,

@@ -69,6 +69,12 @@ __device__ __forceinline__ void dma_strip(const uint8_t* __restrict__ src, unsig
   }
 }
 
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int kLanesPerRow>
 __device__ __forceinline__ float row_sum(float v) {
   v = row16_sum(v);
@@ -259,21 +265,11 @@ __global__ __launch_bounds__(256, 4) void gemv_kernel(ExpertArgs A) {
 // kRing chunks deep, with the loop unrolled by the ring depth so every slot
 // stays in its own registers and the compiler can count outstanding loads
 // exactly.  One LDS-only barrier per chunk; no branches inside the ring.
-namespace {
-
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-}  // namespace
-
 template <bool kGateUp, int kGroups>
-__global__ __launch_bounds__(256, 2) void mfma_kernel(ExpertArgs A) {
+__global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertArgs A) {
   constexpr int kTokens = 16 * kGroups;
   constexpr int kBuf = kTokens * kXRowBytes;
-  constexpr int kRing = 4;
+  constexpr int kRing = kGroups == 1 ? 5 : 4;  // chunks in flight per wave
   extern __shared__ __align__(16) unsigned char lds[];  // [2][kTokens][kXRowBytes], then the scale strips
 
   const int tiles = (A.rows + kMfmaRows - 1) / kMfmaRows;
@@ -370,31 +366,31 @@ __global__ __launch_bounds__(256, 2) void mfma_kernel(ExpertArgs A) {
         const int c = c0 + s;
         const bool valid = c * kChunkBlocks + q < RB;  // false past the row and past the last chunk
         // a zero scale turns a ragged-tail block into zeros
-        bf16x8 a0[4], a1[4];
         const int bs = min(c * kChunkBlocks + q, RB - 1);
         const float sc0 = valid ? e8m0_to_f32(sstrip[srow_l * RB + bs]) : 0.0f;
-        a0[0] = decode_dword_bf16x8(rw0[s].x, sc0);
-        a0[1] = decode_dword_bf16x8(rw0[s].y, sc0);
-        a0[2] = decode_dword_bf16x8(rw0[s].z, sc0);
-        a0[3] = decode_dword_bf16x8(rw0[s].w, sc0);
+        const float sc1 = (kGateUp && valid) ? e8m0_to_f32(sstrip[strip + srow_l * RB + bs]) : 0.0f;
+        const uint32_t d0[4] = {rw0[s].x, rw0[s].y, rw0[s].z, rw0[s].w};
+        uint32_t d1[4] = {0, 0, 0, 0};
         if (kGateUp) {
-          const float sc1 = valid ? e8m0_to_f32(sstrip[strip + srow_l * RB + bs]) : 0.0f;
-          a1[0] = decode_dword_bf16x8(rw1[s].x, sc1);
-          a1[1] = decode_dword_bf16x8(rw1[s].y, sc1);
-          a1[2] = decode_dword_bf16x8(rw1[s].z, sc1);
-          a1[3] = decode_dword_bf16x8(rw1[s].w, sc1);
+          d1[0] = rw1[s].x;
+          d1[1] = rw1[s].y;
+          d1[2] = rw1[s].z;
+          d1[3] = rw1[s].w;
         }
         wload(c + kRing, s);
         const unsigned char* xb = lds + (c & 1) * kBuf + q * 64;
+        // decode each 8-value operand right before its MFMAs (keeps few registers live)
 #pragma unroll
-        for (int tg = 0; tg < kGroups; ++tg) {
-          if (tg < NG) {
-            const unsigned char* xrow = xb + (tg * 16 + r) * kXRowBytes;
+        for (int g = 0; g < 4; ++g) {
+          const bf16x8 a0 = decode_dword_bf16x8(d0[g], sc0);
+          bf16x8 a1;
+          if (kGateUp) a1 = decode_dword_bf16x8(d1[g], sc1);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const bf16x8 bx = *reinterpret_cast<const bf16x8*>(xrow + g * 16);
-              acc0[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[g], bx, acc0[tg], 0, 0, 0);
-              if (kGateUp) acc1[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[g], bx, acc1[tg], 0, 0, 0);
+          for (int tg = 0; tg < kGroups; ++tg) {
+            if (tg < NG) {
+              const bf16x8 bx = *reinterpret_cast<const bf16x8*>(xb + (tg * 16 + r) * kXRowBytes + g * 16);
+              acc0[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bx, acc0[tg], 0, 0, 0);
+              if (kGateUp) acc1[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bx, acc1[tg], 0, 0, 0);
             }
           }
         }

@@ -36,13 +36,31 @@ struct WorkEntry {
 };
 static_assert(sizeof(WorkEntry) == 32, "WorkEntry is 32 bytes");
 
+// Decode regime (T <= kStreamMaxTokens): one persistent kernel per
+// projection walks work items (expert pass x row tile).  A pass is up to
+// kStreamPassTokens routes of one expert; the plan kernel lists the passes of
+// every touched expert in expert order.
+constexpr int kStreamMaxTokens = 64;
+constexpr int kStreamPassTokens = 16;
+
+struct PassEntry {
+  int32_t e;        // local expert
+  int32_t nt;       // routes in this pass (1..tokens per pass)
+  int32_t p;        // plan position of the pass's first route
+  int32_t pad0;
+  uint16_t tok[kStreamPassTokens];  // token (x row) of each route of the pass; slots >= nt unset
+  int32_t pad1[4];
+};
+static_assert(sizeof(PassEntry) == 64, "PassEntry is 64 bytes");
+
 // Header of the device plan, at the start of the workspace.
 struct Plan {
   int32_t n_touched;   // local experts with at least one route
   int32_t R_local;     // local routes
   int32_t n_gemv;      // experts in the GEMV list
   int32_t n_mfma;      // experts in the MFMA list
-  int32_t pad[60];
+  int32_t n_passes;    // entries of the pass list (decode regime)
+  int32_t pad[59];
 };
 
 struct PlanArgs {
@@ -59,6 +77,8 @@ struct PlanArgs {
   int32_t* pos;            // [R] plan position by route index, -1 if not local
   WorkEntry* gemv_list;    // [E_l]
   WorkEntry* mfma_list;    // [E_l]
+  PassEntry* passes;       // pass list, or nullptr
+  int pass_tokens;         // routes per pass (1..kStreamPassTokens) when passes != nullptr
   Plan* plan;
   int32_t* routes_out;     // bucket hook: copy of routes padded with -1, or nullptr
 };
@@ -76,6 +96,25 @@ struct ExpertArgs {
   int rows;                // output rows per expert: I row pairs (gate/up) or K (down)
   uint16_t* a_out;         // gate/up output [R, I] bf16
   float* o_out;            // down output [R, K] fp32
+  int act_kind;
+  float alpha, limit;
+};
+
+// Persistent decode-regime kernel: workgroup b of P takes items b, b+P, ...
+// of the n_passes x tiles items; item = (pass, tile of 64/kSplit rows).
+struct StreamArgs {
+  const uint16_t* in;        // gate/up: x [T, K]; down: a [R, I]  (bf16)
+  uint32_t in_bytes;         // size of `in` (out-of-range loads read zeros)
+  const uint8_t* wp;         // packed weights [E_l][rows_e][red/2]
+  const uint8_t* ws;         // scales [E_l][rows_e][red/32]
+  const uint16_t* bias;      // [E_l][rows_e] bf16, or nullptr
+  const PassEntry* passes;
+  const Plan* plan;
+  int red;                   // reduction length: K (gate/up) or I (down)
+  int rows;                  // output rows per expert: I row pairs (gate/up) or K (down)
+  int tok_from_pass;         // 1: activation row = entry token (gate/up); 0: row = plan position (down)
+  uint16_t* a_out;           // gate/up output [R, I] bf16
+  float* o_out;              // down output [R, K] fp32
   int act_kind;
   float alpha, limit;
 };
@@ -98,6 +137,12 @@ __global__ void gemv_kernel(ExpertArgs A);
 // MFMA regime: 64 rows of one expert per workgroup, kGroups groups of 16 tokens per pass.
 template <bool kGateUp, int kGroups>
 __global__ void mfma_kernel(ExpertArgs A);
+// Decode regime: kSplit waves share one 16-row sub-tile and split the
+// reduction (kSplit = 4, 2 or 1 for up to 4, 8 or 16 routes per pass).
+template <bool kGateUp, int kSplit>
+__global__ void stream_kernel(StreamArgs A);
+constexpr int kStreamRing = 4;   // steps (4 MX blocks per lane) in flight per wave
+constexpr int kStreamMaxItems = 32;  // items per workgroup (their entries live in LDS)
 __global__ void combine_kernel(CombineArgs A);
 __global__ void dequant_kernel(const uint8_t* packed, const uint8_t* scales, int64_t n_blocks, int out_bf16,
                                void* out);

@@ -20,7 +20,7 @@ using moe::Plan;
 
 
 struct Layout {
-  size_t plan, ids, weights, counts, offsets, gemv_list, mfma_list, routes, pos, a, o, total;
+  size_t plan, ids, weights, counts, offsets, gemv_list, mfma_list, passes, routes, pos, a, o, total;
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -41,6 +41,8 @@ Layout make_layout(const moe_mxfp4_desc& d) {
   L.offsets = take((static_cast<size_t>(d.E_local) + 1) * 4);
   L.gemv_list = take(static_cast<size_t>(d.E_local) * sizeof(moe::WorkEntry));
   L.mfma_list = take(static_cast<size_t>(d.E_local) * sizeof(moe::WorkEntry));
+  // decode regime: at most one pass per route
+  L.passes = take(d.T <= moe::kStreamMaxTokens ? R * sizeof(moe::PassEntry) : 0);
   L.routes = take(R * 4);
   L.pos = take(R * 4);
   L.a = take(R * d.I * 2);
@@ -90,6 +92,53 @@ int tokens_bound(const moe_mxfp4_desc& d) {
 // kernel and the launches below apply the same rule.
 bool mfma_enabled(const moe_mxfp4_desc& d) { return d.T > moe::kGemvMaxTokens; }
 
+// Decode regime (T <= kStreamMaxTokens): the persistent stream kernel, whose
+// waves split the reduction kSplit ways with 16/kSplit routes per pass.  The
+// split follows T (4 up to 4 tokens, 2 up to 8, else 1) and is lowered until
+// every slice of both projections has at least kStreamRing steps; a
+// projection whose reduction is still too short for that uses the
+// GEMV/MFMA list kernels.
+int steps_per_slice(int red, int split) { return ((red / 32 + 3) / 4 + split - 1) / split; }
+bool stream_fits(int red, int split) { return split > 0 && steps_per_slice(red, split) >= moe::kStreamRing; }
+
+int stream_split(const moe_mxfp4_desc& d) {
+  if (d.T < 1 || d.T > moe::kStreamMaxTokens) return 0;
+  int split = d.T <= 4 ? 4 : (d.T <= 8 ? 2 : 1);
+  while (split > 1 && !(stream_fits(d.K, split) && stream_fits(d.I, split))) split /= 2;
+  return split;
+}
+
+size_t stream_lds_bytes(int red, bool gate_up, int split) {
+  const size_t nw = gate_up ? 2 : 1;
+  const size_t sw = (nw * 16 * (red / 32) + nw * 32 + 15) / 16 * 16;
+  return 2 * 16 * static_cast<size_t>(moe::kXRowBytes) + 2 * 4 * sw + (split > 1 ? 4 * 64 * 8 * 4 : 0) +
+         moe::kStreamMaxItems * sizeof(moe::PassEntry);
+}
+
+// Resident workgroups of a kernel on the current device (cached per device and kernel).
+template <typename K>
+int resident_workgroups(K kernel, size_t lds) {
+  struct Entry {
+    const void* fn;
+    size_t lds;
+    int dev;
+    int n;
+  };
+  static Entry cache[64];
+  static int used = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const void* fn = reinterpret_cast<const void*>(kernel);
+  for (int i = 0; i < used; ++i)
+    if (cache[i].fn == fn && cache[i].lds == lds && cache[i].dev == dev) return cache[i].n;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds) != hipSuccess) return 0;
+  const int n = std::max(1, cus * per_cu);
+  if (used < 64) cache[used++] = Entry{fn, lds, dev, n};
+  return n;
+}
+
 moe::PlanArgs plan_args(const moe_mxfp4_desc& d, void* ws) {
   const Layout L = make_layout(d);
   moe::PlanArgs P{};
@@ -117,6 +166,11 @@ moe::PlanArgs plan_args(const moe_mxfp4_desc& d, void* ws) {
 void enqueue_plan(const moe_mxfp4_desc& d, const float* logits, const int32_t* ids, const float* wts, void* ws,
                   hipStream_t s) {
   moe::PlanArgs P = plan_args(d, ws);
+  const int split = stream_split(d);
+  if (split > 0) {
+    P.passes = at<moe::PassEntry>(ws, make_layout(d).passes);
+    P.pass_tokens = moe::kStreamPassTokens / split;
+  }
   if (logits != nullptr && d.T <= moe::kFusedRouteTokens) {
     P.logits = logits;
   } else if (logits != nullptr) {
@@ -174,7 +228,7 @@ void enqueue_expert_pair(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs 
     moe::ExpertArgs M = A;
     M.list = at<moe::WorkEntry>(ws, L.mfma_list);
     const int64_t grid = mfma_experts * ((rows + moe::kMfmaRows - 1) / moe::kMfmaRows);
-    const int groups = d.T <= 16 ? 1 : (d.T <= 32 ? 2 : 4);
+    const int groups = d.T <= 32 ? 1 : (d.T <= 64 ? 2 : 4);
     const size_t lds = 2 * static_cast<size_t>(16 * groups) * moe::kXRowBytes +
                        static_cast<size_t>(gate_up ? 2 : 1) * moe::kMfmaRows * (red / 32);
     const dim3 g(static_cast<unsigned>(grid));
@@ -188,6 +242,43 @@ void enqueue_expert_pair(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs 
       else hipLaunchKernelGGL((moe::mfma_kernel<false, 4>), g, dim3(256), lds, s, M);
     }
   }
+}
+
+// One projection in the decode regime.  Items: n_passes x tiles of 64/split
+// rows, where an expert with Te routes has ceil(Te / tp) passes, so n_passes
+// <= (R + min(E_local, R) * (tp - 1)) / tp.  The persistent grid is the
+// resident workgroup count, raised if needed so that no workgroup has more
+// than kStreamMaxItems items, and never above the item bound.
+template <bool kGateUp, int kSplit>
+void launch_stream(const moe_mxfp4_desc& d, const moe::StreamArgs& S, hipStream_t s) {
+  const size_t lds = stream_lds_bytes(S.red, kGateUp, kSplit);
+  const int64_t R = static_cast<int64_t>(d.T) * d.top_k;
+  const int64_t tp = moe::kStreamPassTokens / kSplit;
+  const int64_t passes = std::min<int64_t>(R, (R + tokens_bound(d) * (tp - 1)) / tp);
+  const int item_rows = 64 / kSplit;
+  const int64_t bound = passes * ((S.rows + item_rows - 1) / item_rows);
+  const int resident = resident_workgroups(moe::stream_kernel<kGateUp, kSplit>, lds);
+  int64_t grid = std::max<int64_t>(resident > 0 ? resident : 1024,
+                                   (bound + moe::kStreamMaxItems - 1) / moe::kStreamMaxItems);
+  grid = std::max<int64_t>(1, std::min<int64_t>(grid, bound));
+  hipLaunchKernelGGL((moe::stream_kernel<kGateUp, kSplit>), dim3(static_cast<unsigned>(grid)), dim3(256), lds, s, S);
+}
+
+template <bool kGateUp>
+void enqueue_stream(const moe_mxfp4_desc& d, int split, const moe::StreamArgs& S, hipStream_t s) {
+  if (split == 4) launch_stream<kGateUp, 4>(d, S, s);
+  else if (split == 2) launch_stream<kGateUp, 2>(d, S, s);
+  else launch_stream<kGateUp, 1>(d, S, s);
+}
+
+moe::StreamArgs stream_args(const moe_mxfp4_desc& d, const Layout& L, void* ws) {
+  moe::StreamArgs S{};
+  S.passes = at<moe::PassEntry>(ws, L.passes);
+  S.plan = at<Plan>(ws, L.plan);
+  S.act_kind = d.activation;
+  S.alpha = d.swiglu_alpha;
+  S.limit = d.swiglu_limit;
+  return S;
 }
 
 void enqueue_w13(const moe_mxfp4_desc& d, const uint16_t* x, const uint8_t* w13p, const uint8_t* w13s,
@@ -207,6 +298,21 @@ void enqueue_w13(const moe_mxfp4_desc& d, const uint16_t* x, const uint8_t* w13p
   A.act_kind = d.activation;
   A.alpha = d.swiglu_alpha;
   A.limit = d.swiglu_limit;
+  const int split = stream_split(d);
+  if (stream_fits(d.K, split)) {
+    moe::StreamArgs S = stream_args(d, L, ws);
+    S.in = x;
+    S.in_bytes = static_cast<uint32_t>(static_cast<size_t>(d.T) * d.K * 2);
+    S.wp = w13p;
+    S.ws = w13s;
+    S.bias = b13;
+    S.red = d.K;
+    S.rows = d.I;
+    S.tok_from_pass = 1;
+    S.a_out = A.a_out;
+    enqueue_stream<true>(d, split, S, s);
+    return;
+  }
   enqueue_expert_pair(d, true, A, L, ws, s);
 }
 
@@ -224,7 +330,22 @@ void enqueue_w2_combine(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_
   A.red = d.I;
   A.rows = d.K;
   A.o_out = at<float>(ws, L.o);
-  enqueue_expert_pair(d, false, A, L, ws, s);
+  const int split = stream_split(d);
+  if (stream_fits(d.I, split)) {
+    moe::StreamArgs S = stream_args(d, L, ws);
+    S.in = A.in;
+    S.in_bytes = static_cast<uint32_t>(static_cast<size_t>(d.T) * d.top_k * d.I * 2);
+    S.wp = w2p;
+    S.ws = w2s;
+    S.bias = b2;
+    S.red = d.I;
+    S.rows = d.K;
+    S.tok_from_pass = 0;
+    S.o_out = A.o_out;
+    enqueue_stream<false>(d, split, S, s);
+  } else {
+    enqueue_expert_pair(d, false, A, L, ws, s);
+  }
 
   moe::CombineArgs C;
   C.o = at<float>(ws, L.o);
@@ -270,7 +391,7 @@ int moe_mxfp4_decode(const moe_mxfp4_desc* desc, const uint16_t* x, const float*
   if (d.T == 0) return MOE_OK;
   if (!x || !w13_packed || !w13_scales || !w2_packed || !w2_scales || !out) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(w13_packed) || !aligned16(w2_packed) || !aligned16(out) || !aligned16(w13_scales) ||
-      !aligned16(w2_scales))
+      !aligned16(w2_scales) || !aligned16(w13_bias) || !aligned16(w2_bias))
     return MOE_ERR_ALIGN;
   if ((st = check_workspace(d, workspace, workspace_bytes)) != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -298,7 +419,8 @@ int moe_mxfp4_gate_up(const moe_mxfp4_desc* desc, const uint16_t* x, const uint8
   if (st != MOE_OK) return st;
   if (desc->T == 0) return MOE_OK;
   if (!x || !w13_packed || !w13_scales) return MOE_ERR_NULL;
-  if (!aligned16(x) || !aligned16(w13_packed) || !aligned16(w13_scales) || !aligned16(a)) return MOE_ERR_ALIGN;
+  if (!aligned16(x) || !aligned16(w13_packed) || !aligned16(w13_scales) || !aligned16(w13_bias) || !aligned16(a))
+    return MOE_ERR_ALIGN;
   if ((st = check_workspace(*desc, workspace, workspace_bytes)) != MOE_OK) return st;
   enqueue_w13(*desc, x, w13_packed, w13_scales, w13_bias, a, workspace, static_cast<hipStream_t>(stream));
   return launch_status();
@@ -311,7 +433,8 @@ int moe_mxfp4_down(const moe_mxfp4_desc* desc, const uint16_t* a, const uint8_t*
   if (st != MOE_OK) return st;
   if (desc->T == 0) return MOE_OK;
   if (!w2_packed || !w2_scales || !out) return MOE_ERR_NULL;
-  if (!aligned16(a) || !aligned16(w2_packed) || !aligned16(w2_scales) || !aligned16(out)) return MOE_ERR_ALIGN;
+  if (!aligned16(a) || !aligned16(w2_packed) || !aligned16(w2_scales) || !aligned16(w2_bias) || !aligned16(out))
+    return MOE_ERR_ALIGN;
   if ((st = check_workspace(*desc, workspace, workspace_bytes)) != MOE_OK) return st;
   enqueue_w2_combine(*desc, a, w2_packed, w2_scales, w2_bias, out, workspace, static_cast<hipStream_t>(stream));
   return launch_status();

@@ -151,11 +151,15 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 //     stable, and the chunk's leader advances the slot;
 //  4. the touched experts, in expert order, become two work lists: experts
 //     with at most kGemvMaxTokens routes (GEMV regime, with their tokens) and
-//     the others (MFMA regime).
+//     the others (MFMA regime);
+//  5. (decode regime) each expert's routes, in plan order, are cut into
+//     passes of pass_tokens routes; every route writes its token into its
+//     pass entry as it is placed, and the pass's first route the header.
 __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
   __shared__ int hist[kPlanWaves][kMaxLocalExperts];
   __shared__ int base_e[kMaxLocalExperts + 1];
   __shared__ int ids_s[kFusedRouteTokens * kMaxTopK];
+  __shared__ int pass_base[kMaxLocalExperts];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int R = P.T * P.top_k, E_l = P.E_local, offset = P.offset;
   const bool fused = P.logits != nullptr;
@@ -228,6 +232,21 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
       P.offsets[E_l] = total;
       base_e[E_l] = total;
     }
+    if (P.passes != nullptr) {
+      const int tp = P.pass_tokens;
+      int np = 0;
+#pragma unroll
+      for (int i = 0; i < per; ++i) np += (c[i] + tp - 1) / tp;
+      int np_total;
+      int prun = wave_exclusive_scan(np, lane, np_total);
+#pragma unroll
+      for (int i = 0; i < per; ++i) {
+        const int e = lane * per + i;
+        if (e < E_l) pass_base[e] = prun;
+        prun += (c[i] + tp - 1) / tp;
+      }
+      if (lane == 0) P.plan->n_passes = np_total;
+    }
   }
   __syncthreads();
 
@@ -248,6 +267,18 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
         const int p = hist[wave][key] + rank;
         P.routes[p] = r;
         P.pos[r] = p;
+        if (P.passes != nullptr) {
+          const int tp = P.pass_tokens;
+          const int j = p - base_e[key];
+          const int pass = j / tp, slot = j - pass * tp;
+          PassEntry* pe = P.passes + pass_base[key] + pass;
+          pe->tok[slot] = static_cast<uint16_t>(r / P.top_k);
+          if (slot == 0) {
+            pe->e = key;
+            pe->nt = min(tp, base_e[key + 1] - base_e[key] - pass * tp);
+            pe->p = p;
+          }
+        }
       }
       __builtin_amdgcn_wave_barrier();
       if (lane == leader) hist[wave][key] += __popcll(m);

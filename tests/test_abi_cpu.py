@@ -110,6 +110,8 @@ def test_decode_error_paths():
     assert _decode(d, w13p=A_MIS) == E.MOE_ERR_ALIGN
     assert _decode(d, w2s=A_MIS) == E.MOE_ERR_ALIGN
     assert _decode(d, out=A_MIS) == E.MOE_ERR_ALIGN
+    assert _decode(d, b13=A_MIS) == E.MOE_ERR_ALIGN                      # biases are copied 16 B at a time
+    assert _decode(d, b2=A_MIS) == E.MOE_ERR_ALIGN
     assert _decode(d, ws=None) == E.MOE_ERR_WORKSPACE
     assert _decode(d, ws=A_MIS) == E.MOE_ERR_ALIGN
     _, need = _ws_bytes(d)

@@ -176,6 +176,7 @@ STEP_CASES = [
          bias=True, scale_lo=115, scale_hi=127),                               # ragged 90-block rows
     dict(K=6144, I=2048, E_global=16, E_local=2, top_k=8, scoring="sigmoid", scale_lo=115, scale_hi=127),
     dict(K=96, I=160, E_global=3, E_local=3, top_k=2, bias=True, activation="swiglu_oai"),
+    dict(K=1056, I=1120, E_global=6, E_local=6, top_k=3, bias=True, activation="swiglu_oai"),  # stream path
 ]
 
 
@@ -252,6 +253,18 @@ LAYER_CASES = [
     ("two-mfma-passes", dict(K=256, I=128, E_global=1, E_local=1, top_k=1), 100, 1.0),
     ("wide-k-mixed-regimes", dict(K=7168, I=2048, E_global=16, E_local=3, expert_offset=2, top_k=4,
                                   scoring="sigmoid", scale_lo=115, scale_hi=127), 12, 1.0),
+    # decode-regime stream kernel: reduction split 4 ways (T <= 4), 2 ways (T <= 8), none (T <= 64)
+    ("stream-split4-ring-exact", dict(K=2048, I=2048, E_global=8, E_local=8, top_k=2, activation="swiglu_oai",
+                                      bias=True, scale_lo=115, scale_hi=127), 3, 1.0),
+    ("stream-split4-ragged", dict(K=2080, I=2080, E_global=6, E_local=6, top_k=3, bias=True), 4, 1.0),
+    ("stream-split2", dict(K=1056, I=1120, E_global=4, E_local=4, top_k=2, bias=True,
+                           activation="swiglu_oai"), 7, 1.0),
+    ("stream-partial-tile", dict(K=544, I=608, E_global=4, E_local=4, top_k=2), 20, 1.0),
+    ("stream-multi-pass", dict(K=640, I=512, E_global=2, E_local=2, top_k=2, bias=True), 64, 1.0),
+    ("stream-split-lowered", dict(K=512, I=1024, E_global=4, E_local=4, top_k=2), 2, 1.0),
+    ("stream-gate-up-only", dict(K=2048, I=256, E_global=4, E_local=4, top_k=2, bias=True), 3, 1.0),
+    ("stream-slice-sigmoid", dict(K=6144, I=2048, E_global=64, E_local=8, expert_offset=16, top_k=8,
+                                  scoring="sigmoid", scale_lo=115, scale_hi=127), 32, 1.0),
 ]
 
 
@@ -276,6 +289,18 @@ def test_layer_ids_mode_with_padding_and_foreign_ids():
     _assert_close(y, ref["y"], "ids mode")
     no_route = ~np.any((inp.topk_ids >= 3) & (inp.topk_ids < 8), axis=1)
     assert not y[no_route].any()
+
+
+def test_layer_duplicate_ids_more_routes_than_tokens():
+    # ids mode lets one token route to an expert several times: expert 1 gets
+    # 3 * 7 routes from 3 tokens (several passes), each weighted on its own
+    cfg = _cfg(K=1024, I=1024, E_global=8, E_local=4, top_k=8, bias=True)
+    w = make_weights(cfg)
+    inp = make_topk_inputs(cfg, 3, seed=11)
+    inp.topk_ids[:] = np.array([1, 1, 1, 1, 1, 1, 1, 3], np.int32)
+    ref = oracle.moe_forward_cfg(cfg, w, inp)
+    y = bf16_to_np(run_decode(cfg, DeviceLayer(w), inp))
+    _assert_close(y, ref["y"], "duplicate ids")
 
 
 def test_layer_no_local_route_writes_zeros():
