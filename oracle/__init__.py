@@ -18,5 +18,7 @@ from .moe_oracle import (  # noqa: F401
     rel_l2,
     round_to_bf16,
     route_topk,
+    tile16,
     unpack_codes,
+    untile16,
 )

@@ -44,6 +44,11 @@ Readings where the pages are silent (each is listed in the design doc):
   the local subset; in ids mode the given weights are used as they are.
 * the bf16 rounding is round-to-nearest-even.
 
+The tiled weight layout (``tile16``) is this library's own storage order, not
+the pages': the pages' kernels read the served row layout and name a repack
+as the next step they chose not to take, to keep one copy of the experts.
+Here the repack is an in-place permutation, so there is still one copy.
+
 Precision: ``dtype=np.float32`` (default) is the pages' parity reference.
 ``dtype=np.float64`` runs the same steps in fp64 to bound the oracle's own
 rounding.
@@ -113,6 +118,37 @@ def dequantize(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # bf16
 # --------------------------------------------------------------------------
+
+# --------------------------------------------------------------------------
+# tiled weight layout
+# --------------------------------------------------------------------------
+
+TILE_ROWS = 16    # rows per tile group
+PIECE_BYTES = 16  # one MX block of packed codes
+
+
+def tile16(packed: np.ndarray) -> np.ndarray:
+    """Row layout -> tiled layout of packed MXFP4 rows ``[..., rows, cols/2]``.
+
+    In every group of 16 consecutive rows, the 16-byte blocks are stored
+    block-major: block b of row r of the group lands at byte 256*b + 16*r of
+    the group.  Rows must be a multiple of 16.  A pure byte permutation.
+    """
+    packed = np.asarray(packed, dtype=np.uint8)
+    *lead, rows, rb = packed.shape
+    assert rows % TILE_ROWS == 0 and rb % PIECE_BYTES == 0
+    g = packed.reshape(*lead, rows // TILE_ROWS, TILE_ROWS, rb // PIECE_BYTES, PIECE_BYTES)
+    return np.ascontiguousarray(np.swapaxes(g, -3, -2)).reshape(packed.shape)
+
+
+def untile16(tiled: np.ndarray) -> np.ndarray:
+    """Inverse of ``tile16``."""
+    tiled = np.asarray(tiled, dtype=np.uint8)
+    *lead, rows, rb = tiled.shape
+    assert rows % TILE_ROWS == 0 and rb % PIECE_BYTES == 0
+    g = tiled.reshape(*lead, rows // TILE_ROWS, rb // PIECE_BYTES, TILE_ROWS, PIECE_BYTES)
+    return np.ascontiguousarray(np.swapaxes(g, -3, -2)).reshape(tiled.shape)
+
 
 def bf16_bits_to_float(bits: np.ndarray) -> np.ndarray:
     """Raw bf16 patterns (uint16) -> float32 (exact widening)."""

@@ -213,3 +213,49 @@ def test_activation_closed_forms():
     assert np.array_equal(oracle.activation(g, np.ones(3, f32), "silu_mul"), g)
     # a very negative gate gives -0 / 0, never NaN
     assert np.isfinite(oracle.activation(np.array([-200.0], f32), np.array([3.0], f32), "silu_mul")).all()
+
+
+# --------------------------------------------------------------------------
+# tiled weight layout: a byte permutation, pinned by labelling every piece
+# --------------------------------------------------------------------------
+
+def _labelled_rows(groups, blocks):
+    """Rows whose 16-byte pieces carry (row, block) in their first bytes."""
+    rows = 16 * groups
+    a = np.zeros((rows, 16 * blocks), np.uint8)
+    for r in range(rows):
+        for b in range(blocks):
+            a[r, 16 * b] = r % 256
+            a[r, 16 * b + 1] = r // 256
+            a[r, 16 * b + 2] = b
+            a[r, 16 * b + 3:16 * b + 16] = np.arange(13, dtype=np.uint8) + (r * 7 + b) % 200
+    return a
+
+
+@pytest.mark.parametrize("groups,blocks", [(1, 1), (1, 4), (3, 90), (2, 17)])
+def test_tile16_places_block_b_of_row_r_at_256b_plus_16r(groups, blocks):
+    a = _labelled_rows(groups, blocks)
+    t = oracle.tile16(a).reshape(-1)
+    for g in range(groups):
+        base = g * 16 * 16 * blocks
+        for r in range(16):
+            for b in range(blocks):
+                off = base + 256 * b + 16 * r
+                assert list(t[off:off + 16]) == list(a[16 * g + r, 16 * b:16 * b + 16])
+
+
+def test_tile16_round_trip_and_leading_axes():
+    rng = np.random.default_rng(5)
+    a = rng.integers(0, 256, size=(3, 64, 48), dtype=np.uint8)   # 3 experts, 64 rows, 96 values per row
+    t = oracle.tile16(a)
+    assert t.shape == a.shape and not np.array_equal(t, a)
+    assert np.array_equal(oracle.untile16(t), a)
+    for e in range(3):                                             # experts are tiled on their own
+        assert np.array_equal(t[e], oracle.tile16(a[e]))
+    assert np.array_equal(np.sort(t.reshape(-1)), np.sort(a.reshape(-1)))
+
+
+def test_tile16_single_block_rows_are_unchanged():
+    # with one block per row, block-major and row-major orders coincide
+    a = np.arange(32 * 16, dtype=np.uint32).astype(np.uint8).reshape(32, 16)
+    assert np.array_equal(oracle.tile16(a), a)
