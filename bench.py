@@ -13,6 +13,10 @@ bracketed by HIP events on the launch stream and device synchronisation.
 The same chains of the three steps alone (plan, gate_up, down) give the
 per-kernel times; the gate/up kernel is the dominant one and feeds `roofline`.
 
+Weights are stored in the library's tiled layout (MOE_LAYOUT_TILE16), made in
+place once at load before any timing; `--layout rows` measures the served row
+layout instead.
+
 Algorithmic bytes of one call: for every touched local expert its packed
 weights and scales (3*I*K*17/32 bytes) plus biases, plus x (2TK), the router
 logits (4*T*E_global) and the output (2TK).  Touched experts and local routes
@@ -52,6 +56,8 @@ def parse():
     p.add_argument("--tokens", default=None, help="comma-separated T values (default: the layer's decode sweep)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--rotate-mb", type=float, default=512.0, help="bytes one replica rotation must exceed")
+    p.add_argument("--layout", default="tile16", choices=("rows", "tile16"),
+                   help="packed weight storage order (tile16: tiled in place once, before any timing)")
     return p.parse_args()
 
 
@@ -114,6 +120,10 @@ def main():
     t0 = time.time()
     w0 = make_weights(cfg, replica=0)
     reps = [Replica(torch, cfg, 0, w0)] + [Replica(torch, cfg, i) for i in range(1, L)]
+    if args.layout == "tile16":   # one-time, at weight load
+        for r in reps:
+            moe.moe_mxfp4_tile_weights(r.w13p)
+            moe.moe_mxfp4_tile_weights(r.w2p)
     torch.cuda.synchronize()
     log(f"weights ready ({L} x {cfg.E_local} experts) in {time.time() - t0:.1f}s")
 
@@ -122,7 +132,7 @@ def main():
     for T in tokens:
         d = moe.make_desc(T=T, K=K, I=I, E_global=cfg.E_global, E_local=cfg.E_local, top_k=cfg.top_k,
                           expert_offset=cfg.expert_offset, scoring=cfg.scoring, activation=cfg.activation,
-                          swiglu_alpha=cfg.swiglu_alpha, swiglu_limit=cfg.swiglu_limit)
+                          swiglu_alpha=cfg.swiglu_alpha, swiglu_limit=cfg.swiglu_limit, weight_layout=args.layout)
         ws_bytes = moe.moe_mxfp4_workspace_bytes(d)
         inputs = [make_inputs(cfg, T, call=i) for i in range(L)]
         xs = [torch.from_numpy(inp.x.view(np.int16)).cuda().view(torch.bfloat16) for inp in inputs]
@@ -220,10 +230,10 @@ def main():
         "data": "synthetic (seeded random E2M1 codes, E8M0 scales, Gaussian x and logits)",
         "config": {"workload": f"{cfg.description}; one call at each T in {tokens} per step",
                    "K": K, "I": I, "E_global": cfg.E_global, "E_local": cfg.E_local, "top_k": cfg.top_k,
-                   "tokens": tokens, "replicas": L, "parallelism": "single GPU"},
+                   "tokens": tokens, "replicas": L, "weight_layout": args.layout, "parallelism": "single GPU"},
         "pct_peak": round(100 * value / HBM_PEAK_GBS, 1),
         "per_T": {str(k): v for k, v in results.items()},
-        "roofline": {"kernel": "gate/up projection: moe::gemv_kernel<true,*> + moe::mfma_kernel<true,*>",
+        "roofline": {"kernel": "gate/up projection: moe::stream_kernel<true,*> (one launch per call)",
                      "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "avg_launch_us": round(w13_avg_us, 2),
@@ -231,11 +241,11 @@ def main():
         "device": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, w0, reps[0], torch, moe)
+        line["cpu_baseline"] = cpu_baseline(cfg, w0, reps[0], torch, moe, args.layout)
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(cfg, w0, rep0, torch, moe):
+def cpu_baseline(cfg, w0, rep0, torch, moe, layout):
     """The CPU oracle, as it stands, on a bounded sample: one call at T=1 and one at T=4."""
     import oracle
     from workloads import make_inputs
@@ -257,7 +267,7 @@ def cpu_baseline(cfg, w0, rep0, torch, moe):
         # the same call on the device, compared with the oracle
         d = moe.make_desc(T=T, K=cfg.K, I=cfg.I, E_global=cfg.E_global, E_local=cfg.E_local, top_k=cfg.top_k,
                           expert_offset=cfg.expert_offset, scoring=cfg.scoring, activation=cfg.activation,
-                          swiglu_alpha=cfg.swiglu_alpha, swiglu_limit=cfg.swiglu_limit)
+                          swiglu_alpha=cfg.swiglu_alpha, swiglu_limit=cfg.swiglu_limit, weight_layout=layout)
         out = torch.empty((T, cfg.K), dtype=torch.bfloat16, device="cuda")
         moe.moe_mxfp4_decode(d, torch.from_numpy(inp.x.view(np.int16)).cuda().view(torch.bfloat16), rep0.w13p,
                              rep0.w13s, rep0.w2p, rep0.w2s, out, router_logits=torch.from_numpy(inp.logits).cuda(),

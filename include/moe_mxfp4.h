@@ -61,6 +61,16 @@ extern "C" {
 #define MOE_DTYPE_F32  0
 #define MOE_DTYPE_BF16 1
 
+/* Storage order of the packed weights w13_packed and w2_packed (scales always
+ * keep the row layout).  MOE_LAYOUT_TILE16 is this library's own order, made
+ * in place from the row layout by moe_mxfp4_tile_weights(): in every group of
+ * 16 consecutive rows, the 16-byte blocks (32 values each) are stored
+ * block-major, block b of row r at byte 256*b + 16*r of the group.  Each step
+ * of the expert kernels then reads one contiguous 1 KB run per wave; the row
+ * layout is read in 64-byte pieces of 16 rows.  Same bytes, one copy.       */
+#define MOE_LAYOUT_ROWS    0    /* the served layout of "Read the served layout"      */
+#define MOE_LAYOUT_TILE16  1
+
 /* ---- layer descriptor --------------------------------------------------- */
 typedef struct moe_mxfp4_desc {
     int32_t T;              /* tokens in the call, >= 0 (T = 0 is a no-op)               */
@@ -75,6 +85,7 @@ typedef struct moe_mxfp4_desc {
     int32_t activation;     /* MOE_ACT_*                                                  */
     float   swiglu_alpha;   /* 1.702 for gpt-oss  (MOE_ACT_SWIGLU_OAI only)              */
     float   swiglu_limit;   /* 7.0 for gpt-oss    (MOE_ACT_SWIGLU_OAI only)              */
+    int32_t weight_layout;  /* MOE_LAYOUT_* of w13_packed and w2_packed                   */
 } moe_mxfp4_desc;
 
 /*
@@ -202,6 +213,17 @@ int moe_mxfp4_bucket(const moe_mxfp4_desc* desc, const int32_t* topk_ids,
  */
 int moe_mxfp4_dequant(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t cols,
                       int32_t out_dtype, void* out, void* stream);
+
+/*
+ * In-place change of packed weight storage order between MOE_LAYOUT_ROWS and
+ * MOE_LAYOUT_TILE16 (inverse = 0: rows -> tiled; 1: tiled -> rows).
+ * packed: u8 [rows, cols/2], e.g. w13_packed as [E_local * 2I, K/2] or
+ * w2_packed as [E_local * K, I/2]; rows % 16 == 0, cols % 32 == 0 and
+ * 32 <= cols <= 8192 (MOE_ERR_SHAPE), packed 16-byte aligned (MOE_ERR_ALIGN).
+ * A one-time step at weight load: a call that overlaps a layer call reading
+ * the same weights races with it.
+ */
+int moe_mxfp4_tile_weights(uint8_t* packed, int64_t rows, int64_t cols, int32_t inverse, void* stream);
 
 /* Static string naming a status code. */
 const char* moe_mxfp4_status_string(int status);

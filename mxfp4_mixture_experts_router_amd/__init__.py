@@ -25,6 +25,8 @@ from ._lib import (  # noqa: F401
     MOE_ERR_NULL,
     MOE_ERR_SHAPE,
     MOE_ERR_WORKSPACE,
+    MOE_LAYOUT_ROWS,
+    MOE_LAYOUT_TILE16,
     MOE_OK,
     MOE_SCORING_SIGMOID,
     MOE_SCORING_SOFTMAX,
@@ -34,11 +36,12 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "MoeDesc", "MoeError", "make_desc", "moe_mxfp4_workspace_bytes", "moe_mxfp4_decode",
     "moe_mxfp4_plan", "moe_mxfp4_gate_up", "moe_mxfp4_down", "moe_mxfp4_route", "moe_mxfp4_bucket",
-    "moe_mxfp4_dequant", "moe_mxfp4_status_string", "moe_mxfp4_version",
+    "moe_mxfp4_dequant", "moe_mxfp4_tile_weights", "moe_mxfp4_status_string", "moe_mxfp4_version",
 ]
 
 _SCORING = {"softmax": MOE_SCORING_SOFTMAX, "sigmoid": MOE_SCORING_SIGMOID}
 _ACT = {"silu_mul": MOE_ACT_SILU_MUL, "swiglu_oai": MOE_ACT_SWIGLU_OAI}
+_LAYOUT = {"rows": MOE_LAYOUT_ROWS, "tile16": MOE_LAYOUT_TILE16}
 
 
 class MoeError(RuntimeError):
@@ -49,10 +52,11 @@ class MoeError(RuntimeError):
 
 def make_desc(T: int, K: int, I: int, E_global: int, E_local: int, top_k: int, expert_offset: int = 0,
               scoring="softmax", activation="silu_mul", swiglu_alpha: float = 1.702,
-              swiglu_limit: float = 7.0) -> MoeDesc:
+              swiglu_limit: float = 7.0, weight_layout="rows") -> MoeDesc:
     sc = _SCORING[scoring] if isinstance(scoring, str) else int(scoring)
     ac = _ACT[activation] if isinstance(activation, str) else int(activation)
-    return MoeDesc(T, K, I, E_global, E_local, expert_offset, top_k, sc, ac, swiglu_alpha, swiglu_limit)
+    wl = _LAYOUT[weight_layout] if isinstance(weight_layout, str) else int(weight_layout)
+    return MoeDesc(T, K, I, E_global, E_local, expert_offset, top_k, sc, ac, swiglu_alpha, swiglu_limit, wl)
 
 
 def moe_mxfp4_status_string(status: int) -> str:
@@ -219,6 +223,22 @@ def moe_mxfp4_bucket(desc: MoeDesc, topk_ids, counts, offsets, routes, workspace
         _ptr(routes, torch.int32, (d.T * d.top_k,), "routes"),
         wsp, wsn, _stream(stream)), "moe_mxfp4_bucket")
     return ws
+
+
+def moe_mxfp4_tile_weights(packed, inverse=False, stream=None):
+    """In place: packed u8 [..., rows, cols/2] between the row and the tiled layout.
+
+    Leading axes (experts) are folded into the rows; rows per expert must be a
+    multiple of 16.
+    """
+    torch = _torch()
+    if packed.dim() < 2:
+        raise ValueError("packed must have at least 2 dimensions")
+    half = packed.shape[-1]
+    rows = packed.numel() // half if half else 0
+    _check(_lib.lib().moe_mxfp4_tile_weights(
+        _ptr(packed, torch.uint8, tuple(packed.shape), "packed"), rows, 2 * half, 1 if inverse else 0,
+        _stream(stream)), "moe_mxfp4_tile_weights")
 
 
 def moe_mxfp4_dequant(packed, scales, out, stream=None):

@@ -27,6 +27,8 @@ MOE_ACT_SILU_MUL = 0
 MOE_ACT_SWIGLU_OAI = 1
 MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
+MOE_LAYOUT_ROWS = 0
+MOE_LAYOUT_TILE16 = 1
 
 EXPORTED = (
     "moe_mxfp4_workspace_bytes",
@@ -37,6 +39,7 @@ EXPORTED = (
     "moe_mxfp4_gate_up",
     "moe_mxfp4_down",
     "moe_mxfp4_dequant",
+    "moe_mxfp4_tile_weights",
     "moe_mxfp4_status_string",
     "moe_mxfp4_version",
 )
@@ -55,6 +58,7 @@ class MoeDesc(ctypes.Structure):
         ("activation", ctypes.c_int32),
         ("swiglu_alpha", ctypes.c_float),
         ("swiglu_limit", ctypes.c_float),
+        ("weight_layout", ctypes.c_int32),
     ]
 
 
@@ -73,6 +77,7 @@ _SIGNATURES = {
     "moe_mxfp4_route": (_I32, [_DESC, _P, _P, _P, _P]),
     "moe_mxfp4_bucket": (_I32, [_DESC, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_mxfp4_dequant": (_I32, [_P, _P, _I64, _I64, _I32, _P, _P]),
+    "moe_mxfp4_tile_weights": (_I32, [_P, _I64, _I64, _I32, _P]),
     "moe_mxfp4_status_string": (ctypes.c_char_p, [_I32]),
     "moe_mxfp4_version": (ctypes.c_char_p, []),
 }

@@ -110,10 +110,11 @@ __global__ __launch_bounds__(256, 4) void gemv_kernel(ExpertArgs A) {
   const int rows_e = kGateUp ? 2 * A.rows : A.rows;
   const uint8_t* __restrict__ wbase = A.wp + static_cast<size_t>(we.e) * rows_e * (red >> 1);
   const uint8_t* __restrict__ sbase = A.ws + static_cast<size_t>(we.e) * rows_e * RB;
-  const uint32_t wo0 = static_cast<uint32_t>(n) * (red >> 1), wo1 = static_cast<uint32_t>(n + A.rows) * (red >> 1);
+  const uint32_t wo0 = row_offset(n, red >> 1, A.tiled), wo1 = row_offset(n + A.rows, red >> 1, A.tiled);
+  const uint32_t bstride = block_stride(A.tiled);
   const size_t row0 = static_cast<size_t>(we.e) * rows_e + n;  // bias index of the gate (or single) row
   const size_t row1 = row0 + A.rows;                             // bias index of the up row
-  auto ldw = [&](uint32_t off, int b) { return *reinterpret_cast<const uint4*>(wbase + off + 16u * b); };
+  auto ldw = [&](uint32_t off, int b) { return *reinterpret_cast<const uint4*>(wbase + off + bstride * b); };
   // scale strips of the tile's rows, staged in LDS: [kRowsPerWG][RB] (gate/single), then up
   unsigned char* sstrip = reinterpret_cast<unsigned char*>(xs) + kGemvMaxTokens * red * 2;
   const int strip = kRowsPerWG * RB;
@@ -288,8 +289,9 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
   const int rows_e = kGateUp ? 2 * A.rows : A.rows;
   const uint8_t* __restrict__ wbase = A.wp + static_cast<size_t>(we.e) * rows_e * (red >> 1);
   const uint8_t* __restrict__ sbase = A.ws + static_cast<size_t>(we.e) * rows_e * RB;
-  const uint32_t wo0 = static_cast<uint32_t>(wrow) * (red >> 1);
-  const uint32_t wo1 = static_cast<uint32_t>(wrow + A.rows) * (red >> 1);
+  const uint32_t wo0 = row_offset(wrow, red >> 1, A.tiled);
+  const uint32_t wo1 = row_offset(wrow + A.rows, red >> 1, A.tiled);
+  const uint32_t bstride = block_stride(A.tiled);
   // scale strips of the tile's rows (clamped to the expert), staged in LDS once:
   // [kMfmaRows][RB] (gate/single), then up
   const int srows = min(kMfmaRows, A.rows - tile * kMfmaRows);
@@ -345,8 +347,8 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
     uint4 rw0[kRing], rw1[kRing], rx[kRing][kGroups];
     auto wload = [&](int c, int slot) {
       const int b = min(c * kChunkBlocks + q, RB - 1);
-      rw0[slot] = *reinterpret_cast<const uint4*>(wbase + wo0 + 16u * b);
-      if (kGateUp) rw1[slot] = *reinterpret_cast<const uint4*>(wbase + wo1 + 16u * b);
+      rw0[slot] = *reinterpret_cast<const uint4*>(wbase + wo0 + bstride * b);
+      if (kGateUp) rw1[slot] = *reinterpret_cast<const uint4*>(wbase + wo1 + bstride * b);
     };
 
     // prologue: chunks 0..kRing-1 in flight, chunk 0 staged in LDS
@@ -477,6 +479,33 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs A) {
 }
 
 // One thread per 32-value MX block: 16 packed bytes + 1 scale byte.
+// In place: the group's 16 * blocks pieces of 16 bytes are all read into
+// registers before any is written (blocks <= kMaxDim / 32, so at most 16 per
+// thread).  Forward: piece (r, b) at r * blocks + b moves to b * 16 + r.
+__global__ __launch_bounds__(256) void tile_kernel(uint8_t* packed, int64_t groups, int blocks, int inverse) {
+  constexpr int kPer = 16 * (kMaxDim / 32) / 256;
+  const int64_t g = blockIdx.x;
+  if (g >= groups) return;
+  uint4* base = reinterpret_cast<uint4*>(packed + g * 16 * static_cast<int64_t>(blocks) * 16);
+  const int n = 16 * blocks;
+  uint4 v[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int s = threadIdx.x + 256 * i;
+    if (s < n) v[i] = base[s];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int s = threadIdx.x + 256 * i;
+    if (s < n) {
+      // forward: source is row-major (r, b); inverse: source is block-major (b, r)
+      const int d = inverse ? (s & 15) * blocks + (s >> 4) : (s % blocks) * 16 + s / blocks;
+      base[d] = v[i];
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ packed,
                                                       const uint8_t* __restrict__ scales, int64_t n_blocks,
                                                       int out_bf16, void* __restrict__ out) {

@@ -83,6 +83,15 @@ struct PlanArgs {
   int32_t* routes_out;     // bucket hook: copy of routes padded with -1, or nullptr
 };
 
+// Packed weight rows are in the row layout, or tiled: in each group of 16
+// rows, block b of row r at byte 256*b + 16*r of the group.  Either way a
+// lane's 16-byte block b of row n is at row_offset(n) + b * block_stride.
+__device__ __forceinline__ uint32_t row_offset(int n, uint32_t row_bytes, int tiled) {
+  return tiled ? static_cast<uint32_t>(n & ~15) * row_bytes + 16u * static_cast<uint32_t>(n & 15)
+               : static_cast<uint32_t>(n) * row_bytes;
+}
+__device__ __forceinline__ uint32_t block_stride(int tiled) { return tiled ? 256u : 16u; }
+
 struct ExpertArgs {
   const uint16_t* in;      // gate/up: x [T, K]; down: a [R, I]  (bf16)
   const int32_t* routes;   // gate/up: activation row of position p is routes[p] / top_k; down: nullptr (row p)
@@ -94,6 +103,7 @@ struct ExpertArgs {
   const Plan* plan;
   int red;                 // reduction length: K (gate/up) or I (down)
   int rows;                // output rows per expert: I row pairs (gate/up) or K (down)
+  int tiled;               // packed weights in the tiled layout
   uint16_t* a_out;         // gate/up output [R, I] bf16
   float* o_out;            // down output [R, K] fp32
   int act_kind;
@@ -113,6 +123,7 @@ struct StreamArgs {
   int red;                   // reduction length: K (gate/up) or I (down)
   int rows;                  // output rows per expert: I row pairs (gate/up) or K (down)
   int tok_from_pass;         // 1: activation row = entry token (gate/up); 0: row = plan position (down)
+  int tiled;                 // packed weights in the tiled layout
   uint16_t* a_out;           // gate/up output [R, I] bf16
   float* o_out;              // down output [R, K] fp32
   int act_kind;
@@ -144,6 +155,8 @@ __global__ void stream_kernel(StreamArgs A);
 constexpr int kStreamRing = 4;   // steps (4 MX blocks per lane) in flight per wave
 constexpr int kStreamMaxItems = 32;  // items per workgroup (their entries live in LDS)
 __global__ void combine_kernel(CombineArgs A);
+// In-place row layout <-> tiled layout, one workgroup per 16-row group.
+__global__ void tile_kernel(uint8_t* packed, int64_t groups, int blocks, int inverse);
 __global__ void dequant_kernel(const uint8_t* packed, const uint8_t* scales, int64_t n_blocks, int out_bf16,
                                void* out);
 

@@ -65,6 +65,7 @@ int check_desc(const moe_mxfp4_desc* d) {
   if (static_cast<int64_t>(d->T) * d->top_k > (int64_t{1} << 24)) return MOE_ERR_SHAPE;
   if (d->scoring != MOE_SCORING_SOFTMAX && d->scoring != MOE_SCORING_SIGMOID) return MOE_ERR_MODE;
   if (d->activation != MOE_ACT_SILU_MUL && d->activation != MOE_ACT_SWIGLU_OAI) return MOE_ERR_MODE;
+  if (d->weight_layout != MOE_LAYOUT_ROWS && d->weight_layout != MOE_LAYOUT_TILE16) return MOE_ERR_MODE;
   return MOE_OK;
 }
 
@@ -278,6 +279,7 @@ moe::StreamArgs stream_args(const moe_mxfp4_desc& d, const Layout& L, void* ws) 
   S.act_kind = d.activation;
   S.alpha = d.swiglu_alpha;
   S.limit = d.swiglu_limit;
+  S.tiled = d.weight_layout == MOE_LAYOUT_TILE16;
   return S;
 }
 
@@ -294,6 +296,7 @@ void enqueue_w13(const moe_mxfp4_desc& d, const uint16_t* x, const uint8_t* w13p
   A.plan = at<Plan>(ws, L.plan);
   A.red = d.K;
   A.rows = d.I;
+  A.tiled = d.weight_layout == MOE_LAYOUT_TILE16;
   A.a_out = a != nullptr ? a : at<uint16_t>(ws, L.a);
   A.act_kind = d.activation;
   A.alpha = d.swiglu_alpha;
@@ -329,6 +332,7 @@ void enqueue_w2_combine(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_
   A.plan = at<Plan>(ws, L.plan);
   A.red = d.I;
   A.rows = d.K;
+  A.tiled = d.weight_layout == MOE_LAYOUT_TILE16;
   A.o_out = at<float>(ws, L.o);
   const int split = stream_split(d);
   if (stream_fits(d.I, split)) {
@@ -477,6 +481,19 @@ int moe_mxfp4_dequant(const uint8_t* packed, const uint8_t* scales, int64_t rows
   hipLaunchKernelGGL(moe::dequant_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), packed, scales, n_blocks, out_dtype == MOE_DTYPE_BF16 ? 1 : 0,
                      out);
+  return launch_status();
+}
+
+int moe_mxfp4_tile_weights(uint8_t* packed, int64_t rows, int64_t cols, int32_t inverse, void* stream) {
+  if (rows < 0 || rows % 16 != 0 || cols < 32 || cols > moe::kMaxDim || cols % 32 != 0) return MOE_ERR_SHAPE;
+  if (inverse != 0 && inverse != 1) return MOE_ERR_MODE;
+  const int64_t groups = rows / 16;
+  if (groups == 0) return MOE_OK;
+  if (packed == nullptr) return MOE_ERR_NULL;
+  if (!aligned16(packed)) return MOE_ERR_ALIGN;
+  if (groups > 0x7FFFFFFF) return MOE_ERR_SHAPE;
+  hipLaunchKernelGGL(moe::tile_kernel, dim3(static_cast<unsigned>(groups)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), packed, groups, static_cast<int>(cols / 32), inverse);
   return launch_status();
 }
 

@@ -95,6 +95,7 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
   const int rows_e = kNW * rows;
   const uint32_t row_bytes = static_cast<uint32_t>(red >> 1);
   const uint32_t expert_bytes = static_cast<uint32_t>(rows_e) * row_bytes;
+  const uint32_t bstride = block_stride(A.tiled);
 
   const int N = A.plan->n_passes * tiles;
   const int P = gridDim.x;
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
     // this wave's sub-tile: rows are a multiple of 16, so a sub-tile is all in
     // or all out; an out sub-tile re-reads the expert's last 16 rows (results dropped)
     const int row0w = min(l_row0 + st * 16, rows - 16);
-    l_wo = static_cast<uint32_t>(row0w + r) * row_bytes;
+    l_wo = row_offset(row0w + r, row_bytes, A.tiled);
     wrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(A.wp) + static_cast<size_t>(l_e) * expert_bytes, 0,
                                             expert_bytes, 0x00020000);
     // scale strip(s) and bias of rows row0w..row0w+15 into this wave's slot
@@ -184,10 +185,10 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
     // past this workgroup's items read zeros
     const int b = (kp * NCp + ls) * 4 + q;
     const bool ok = li < n_my && b < RB;
-    const uint32_t o0 = ok ? l_wo + 16u * b : kOob;
+    const uint32_t o0 = ok ? l_wo + bstride * b : kOob;
     rw0[slot] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(wrs, o0, 0, 0));
     if (kGateUp) {
-      const uint32_t o1 = ok ? l_wo + static_cast<uint32_t>(rows) * row_bytes + 16u * b : kOob;
+      const uint32_t o1 = ok ? l_wo + static_cast<uint32_t>(rows) * row_bytes + bstride * b : kOob;
       rw1[slot] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(wrs, o1, 0, 0));
     }
     // activation piece of the staging thread

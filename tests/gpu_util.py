@@ -43,9 +43,14 @@ def bf16_bits_np(t):
 
 
 class DeviceLayer:
-    """Weights of one layer slice resident on the device."""
+    """Weights of one layer slice resident on the device.
 
-    def __init__(self, w):
+    layout "tile16" tiles the packed weights in place on the device with the
+    library's own entry point after the upload (the row-layout bytes are what
+    the generators and the oracle use).
+    """
+
+    def __init__(self, w, layout="rows"):
         self.w13p = dev_u8(w.w13_packed)
         self.w13s = dev_u8(w.w13_scales)
         self.w2p = dev_u8(w.w2_packed)
@@ -53,20 +58,25 @@ class DeviceLayer:
         self.b13 = dev_bf16(w.b13) if w.b13 is not None else None
         self.b2 = dev_bf16(w.b2) if w.b2 is not None else None
         self.E_local = w.w13_packed.shape[0]
+        self.layout = layout
+        if layout == "tile16":
+            moe.moe_mxfp4_tile_weights(self.w13p)
+            moe.moe_mxfp4_tile_weights(self.w2p)
 
 
-def desc_for(cfg, T, E_local=None, expert_offset=None):
+def desc_for(cfg, T, E_local=None, expert_offset=None, weight_layout="rows"):
     return moe.make_desc(T=T, K=cfg.K, I=cfg.I, E_global=cfg.E_global,
                          E_local=cfg.E_local if E_local is None else E_local, top_k=cfg.top_k,
                          expert_offset=cfg.expert_offset if expert_offset is None else expert_offset,
                          scoring=cfg.scoring, activation=cfg.activation,
-                         swiglu_alpha=cfg.swiglu_alpha, swiglu_limit=cfg.swiglu_limit)
+                         swiglu_alpha=cfg.swiglu_alpha, swiglu_limit=cfg.swiglu_limit,
+                         weight_layout=weight_layout)
 
 
 def run_decode(cfg, layer, inp, expert_offset=None, workspace=None, stream=None):
     t = torch()
     T = inp.x.shape[0]
-    d = desc_for(cfg, T, E_local=layer.E_local, expert_offset=expert_offset)
+    d = desc_for(cfg, T, E_local=layer.E_local, expert_offset=expert_offset, weight_layout=layer.layout)
     x = dev_bf16(inp.x)
     out = t.full((T, cfg.K), float("nan"), dtype=t.bfloat16, device="cuda")
     kw = {}

@@ -43,7 +43,7 @@ def test_version_and_status_strings():
 
 def _desc(**kw):
     d = dict(T=4, K=256, I=256, E_global=8, E_local=8, expert_offset=0, top_k=2, scoring=0,
-             activation=0, swiglu_alpha=1.702, swiglu_limit=7.0)
+             activation=0, swiglu_alpha=1.702, swiglu_limit=7.0, weight_layout=0)
     d.update(kw)
     return _lib.MoeDesc(**d)
 
@@ -119,6 +119,18 @@ def test_decode_error_paths():
     assert _decode(_desc(E_global=2048, E_local=8)) == E.MOE_ERR_SHAPE   # too many experts to route
     assert _decode(_desc(T=0)) == E.MOE_OK                               # T = 0: nothing to do
     assert _decode(_desc(T=0), x=None, out=None) == E.MOE_OK
+
+
+def test_tile_weights_error_paths():
+    L, E = _lib.lib(), _lib
+    assert L.moe_mxfp4_tile_weights(A, 24, 64, 0, None) == E.MOE_ERR_SHAPE      # rows not a multiple of 16
+    assert L.moe_mxfp4_tile_weights(A, 32, 48, 0, None) == E.MOE_ERR_SHAPE      # cols not a multiple of 32
+    assert L.moe_mxfp4_tile_weights(A, 32, 16384, 0, None) == E.MOE_ERR_SHAPE   # cols above 8192
+    assert L.moe_mxfp4_tile_weights(A, 32, 64, 2, None) == E.MOE_ERR_MODE
+    assert L.moe_mxfp4_tile_weights(None, 32, 64, 0, None) == E.MOE_ERR_NULL
+    assert L.moe_mxfp4_tile_weights(A_MIS, 32, 64, 0, None) == E.MOE_ERR_ALIGN
+    assert L.moe_mxfp4_tile_weights(None, 0, 64, 0, None) == E.MOE_OK           # nothing to do
+    assert _decode(_desc(weight_layout=2)) == E.MOE_ERR_MODE
 
 
 def test_hook_error_paths():

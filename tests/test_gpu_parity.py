@@ -89,6 +89,23 @@ def test_dequant_random_large():
 
 
 # --------------------------------------------------------------------------
+# tiled weight layout: bit-exact permutation, in place
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(3, 64, 48), (32, 1440), (16, 4096), (48, 16), (2, 5760, 1440)])
+def test_tile_weights_matches_oracle_and_inverts(shape):
+    rng = np.random.default_rng(sum(shape))
+    a = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    d = dev_u8(a)
+    moe.moe_mxfp4_tile_weights(d)
+    torch().cuda.synchronize()
+    assert np.array_equal(d.cpu().numpy(), oracle.tile16(a))
+    moe.moe_mxfp4_tile_weights(d, inverse=True)
+    torch().cuda.synchronize()
+    assert np.array_equal(d.cpu().numpy(), a)
+
+
+# --------------------------------------------------------------------------
 # routing and bucketing: bit-exact ids and permutation
 # --------------------------------------------------------------------------
 
@@ -277,6 +294,31 @@ def test_layer_elementwise(case):
     ref = oracle.moe_forward_cfg(cfg, w, inp)
     out = run_decode(cfg, DeviceLayer(w), inp)
     _assert_close(bf16_to_np(out), ref["y"], f"layer {name} T{T}")
+
+
+TILED_CASES = [
+    ("split4", dict(K=2880, I=2880, E_global=32, E_local=6, expert_offset=20, top_k=4, activation="swiglu_oai",
+                    bias=True, scale_lo=115, scale_hi=127), 1),
+    ("split2", dict(K=1056, I=1120, E_global=4, E_local=4, top_k=2, bias=True), 7),
+    ("split1", dict(K=544, I=608, E_global=4, E_local=4, top_k=2), 20),
+    ("fallback-lists", dict(), 4),                                         # K = I = 256: GEMV / MFMA list kernels
+    ("large-T-lists", dict(K=512, I=768, E_global=2, E_local=2, top_k=2), 80),
+    ("gate-up-only", dict(K=2048, I=256, E_global=4, E_local=4, top_k=2, bias=True), 3),
+]
+
+
+@pytest.mark.parametrize("case", range(len(TILED_CASES)))
+def test_layer_tiled_weights_bit_identical_to_rows(case):
+    name, kw, T = TILED_CASES[case]
+    cfg = _cfg(**kw)
+    w = make_weights(cfg)
+    inp = make_inputs(cfg, T, t_index=case)
+    rows = bf16_bits_np(run_decode(cfg, DeviceLayer(w), inp))
+    tiled = bf16_bits_np(run_decode(cfg, DeviceLayer(w, layout="tile16"), inp))
+    assert np.array_equal(rows, tiled), name
+    if case == 0:
+        ref = oracle.moe_forward_cfg(cfg, w, inp)
+        _assert_close(bf16_to_np(run_decode(cfg, DeviceLayer(w, layout="tile16"), inp)), ref["y"], "tiled")
 
 
 def test_layer_ids_mode_with_padding_and_foreign_ids():
