@@ -453,29 +453,12 @@ template __global__ void mfma_kernel<false, 1>(ExpertArgs);
 template __global__ void mfma_kernel<false, 2>(ExpertArgs);
 template __global__ void mfma_kernel<false, 4>(ExpertArgs);
 
-// y[t, :] = sum over j (ascending) of w[t, j] * o[pos(t, j), :] for the
-// token's local routes; zeros for a token without one.  Fixed order, no
-// atomics, so the result is reproducible bit for bit.
+// y[t, :] from the per-route down projections (combine4).
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs A) {
   const int t = blockIdx.y;
   const int k4 = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (k4 >= A.K) return;
-  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int j = 0; j < A.top_k; ++j) {
-    const int r = t * A.top_k + j;
-    const int p = A.pos[r];
-    if (p < 0) continue;
-    const float wt = A.weights[r];
-    const float4 o = *reinterpret_cast<const float4*>(A.o + static_cast<size_t>(p) * A.K + k4);
-    acc.x = __fadd_rn(acc.x, __fmul_rn(wt, o.x));
-    acc.y = __fadd_rn(acc.y, __fmul_rn(wt, o.y));
-    acc.z = __fadd_rn(acc.z, __fmul_rn(wt, o.z));
-    acc.w = __fadd_rn(acc.w, __fmul_rn(wt, o.w));
-  }
-  uint2 packed;
-  packed.x = static_cast<uint32_t>(f32_to_bf16_rne(acc.x)) | (static_cast<uint32_t>(f32_to_bf16_rne(acc.y)) << 16);
-  packed.y = static_cast<uint32_t>(f32_to_bf16_rne(acc.z)) | (static_cast<uint32_t>(f32_to_bf16_rne(acc.w)) << 16);
-  *reinterpret_cast<uint2*>(A.out + static_cast<size_t>(t) * A.K + k4) = packed;
+  combine4(A, t, k4);
 }
 
 // One thread per 32-value MX block: 16 packed bytes + 1 scale byte.

@@ -48,7 +48,7 @@ struct PassEntry {
   int32_t nt;       // routes in this pass (1..tokens per pass)
   int32_t p;        // plan position of the pass's first route
   int32_t pad0;
-  uint16_t tok[kStreamPassTokens];  // token (x row) of each route of the pass; slots >= nt unset
+  uint16_t rte[kStreamPassTokens];  // route index t*top_k + j of each route of the pass; slots >= nt unset
   int32_t pad1[4];
 };
 static_assert(sizeof(PassEntry) == 64, "PassEntry is 64 bytes");
@@ -69,6 +69,7 @@ struct PlanArgs {
   const float* w_in;       // caller's weights to copy into the workspace (ids mode), or nullptr
   int T, top_k, E_global, E_local, offset, scoring;
   int mfma_enabled;        // the MFMA kernels run for this call (T > kGemvMaxTokens); else all experts go to GEMV
+  int lists;               // build the GEMV / MFMA work lists (some projection uses the list kernels)
   int32_t* ids_ws;         // [R] routed ids (logits mode)
   float* weights_ws;       // [R] routing weights
   int32_t* counts;         // [E_l]
@@ -78,7 +79,7 @@ struct PlanArgs {
   WorkEntry* gemv_list;    // [E_l]
   WorkEntry* mfma_list;    // [E_l]
   PassEntry* passes;       // pass list, or nullptr
-  int pass_tokens;         // routes per pass (1..kStreamPassTokens) when passes != nullptr
+  int pass_shift;          // routes per pass = 1 << pass_shift (<= kStreamPassTokens) when passes != nullptr
   Plan* plan;
   int32_t* routes_out;     // bucket hook: copy of routes padded with -1, or nullptr
 };
@@ -110,6 +111,47 @@ struct ExpertArgs {
   float alpha, limit;
 };
 
+struct CombineArgs {
+  const float* o;          // per-route down projections [R, K] fp32, row = plan position or route
+  const int32_t* pos;
+  const float* weights;
+  uint16_t* out;
+  int T, K, top_k;
+  int by_route;            // o rows indexed by route: their loads need not wait for pos
+};
+
+// out[t, k4..k4+3] = sum over j (ascending) of w[t, j] * o[route (t, j), k4..k4+3]
+// over the token's local routes (zeros without one), rounded to bf16.  Fixed
+// order and explicit roundings: the same bits wherever it runs.
+__device__ __forceinline__ void combine4(const CombineArgs& A, int t, int k4) {
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int j0 = 0; j0 < A.top_k; j0 += 4) {
+    int p[4];
+    float wt[4];
+    float4 o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = t * A.top_k + min(j0 + i, A.top_k - 1);
+      p[i] = j0 + i < A.top_k ? A.pos[r] : -1;
+      wt[i] = A.weights[r];
+      if (A.by_route) o[i] = *reinterpret_cast<const float4*>(A.o + static_cast<size_t>(r) * A.K + k4);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (p[i] < 0) continue;
+      if (!A.by_route) o[i] = *reinterpret_cast<const float4*>(A.o + static_cast<size_t>(p[i]) * A.K + k4);
+      acc.x = __fadd_rn(acc.x, __fmul_rn(wt[i], o[i].x));
+      acc.y = __fadd_rn(acc.y, __fmul_rn(wt[i], o[i].y));
+      acc.z = __fadd_rn(acc.z, __fmul_rn(wt[i], o[i].z));
+      acc.w = __fadd_rn(acc.w, __fmul_rn(wt[i], o[i].w));
+    }
+  }
+  uint2 packed;
+  packed.x = static_cast<uint32_t>(f32_to_bf16_rne(acc.x)) | (static_cast<uint32_t>(f32_to_bf16_rne(acc.y)) << 16);
+  packed.y = static_cast<uint32_t>(f32_to_bf16_rne(acc.z)) | (static_cast<uint32_t>(f32_to_bf16_rne(acc.w)) << 16);
+  *reinterpret_cast<uint2*>(A.out + static_cast<size_t>(t) * A.K + k4) = packed;
+}
+
 // Persistent decode-regime kernel: workgroup b of P takes items b, b+P, ...
 // of the n_passes x tiles items; item = (pass, tile of 64/kSplit rows).
 struct StreamArgs {
@@ -122,7 +164,9 @@ struct StreamArgs {
   const Plan* plan;
   int red;                   // reduction length: K (gate/up) or I (down)
   int rows;                  // output rows per expert: I row pairs (gate/up) or K (down)
-  int tok_from_pass;         // 1: activation row = entry token (gate/up); 0: row = plan position (down)
+  int tok_from_pass;         // 1: activation row = token of the entry's route (gate/up); 0: row = plan position (down)
+  int top_k;
+  int o_by_route;            // down: o rows indexed by route (t*top_k + j) instead of plan position
   int tiled;                 // packed weights in the tiled layout
   uint16_t* a_out;           // gate/up output [R, I] bf16
   float* o_out;              // down output [R, K] fp32
@@ -130,13 +174,6 @@ struct StreamArgs {
   float alpha, limit;
 };
 
-struct CombineArgs {
-  const float* o;
-  const int32_t* pos;
-  const float* weights;
-  uint16_t* out;
-  int T, K, top_k;
-};
 
 __global__ void route_topk_kernel(const float* logits, int T, int E, int k, int scoring, int32_t* ids,
                                   float* weights);

@@ -150,6 +150,7 @@ moe::PlanArgs plan_args(const moe_mxfp4_desc& d, void* ws) {
   P.offset = d.expert_offset;
   P.scoring = d.scoring;
   P.mfma_enabled = mfma_enabled(d) ? 1 : 0;
+  P.lists = 1;
   P.ids_ws = at<int32_t>(ws, L.ids);
   P.weights_ws = at<float>(ws, L.weights);
   P.counts = at<int32_t>(ws, L.counts);
@@ -170,8 +171,10 @@ void enqueue_plan(const moe_mxfp4_desc& d, const float* logits, const int32_t* i
   const int split = stream_split(d);
   if (split > 0) {
     P.passes = at<moe::PassEntry>(ws, make_layout(d).passes);
-    P.pass_tokens = moe::kStreamPassTokens / split;
+    P.pass_shift = split == 4 ? 2 : (split == 2 ? 3 : 4);  // kStreamPassTokens / split routes per pass
   }
+  // the GEMV / MFMA lists are needed when a projection is not served by the stream kernel
+  P.lists = !(stream_fits(d.K, split) && stream_fits(d.I, split));
   if (logits != nullptr && d.T <= moe::kFusedRouteTokens) {
     P.logits = logits;
   } else if (logits != nullptr) {
@@ -280,6 +283,7 @@ moe::StreamArgs stream_args(const moe_mxfp4_desc& d, const Layout& L, void* ws) 
   S.alpha = d.swiglu_alpha;
   S.limit = d.swiglu_limit;
   S.tiled = d.weight_layout == MOE_LAYOUT_TILE16;
+  S.top_k = d.top_k;
   return S;
 }
 
@@ -334,8 +338,18 @@ void enqueue_w2_combine(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_
   A.rows = d.K;
   A.tiled = d.weight_layout == MOE_LAYOUT_TILE16;
   A.o_out = at<float>(ws, L.o);
+  moe::CombineArgs C;
+  C.o = at<float>(ws, L.o);
+  C.pos = at<int32_t>(ws, L.pos);
+  C.weights = at<float>(ws, L.weights);
+  C.out = out;
+  C.T = d.T;
+  C.K = d.K;
+  C.top_k = d.top_k;
+  C.by_route = 0;
   const int split = stream_split(d);
   if (stream_fits(d.I, split)) {
+    C.by_route = 1;
     moe::StreamArgs S = stream_args(d, L, ws);
     S.in = A.in;
     S.in_bytes = static_cast<uint32_t>(static_cast<size_t>(d.T) * d.top_k * d.I * 2);
@@ -345,20 +359,12 @@ void enqueue_w2_combine(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_
     S.red = d.I;
     S.rows = d.K;
     S.tok_from_pass = 0;
+    S.o_by_route = 1;
     S.o_out = A.o_out;
     enqueue_stream<false>(d, split, S, s);
   } else {
     enqueue_expert_pair(d, false, A, L, ws, s);
   }
-
-  moe::CombineArgs C;
-  C.o = at<float>(ws, L.o);
-  C.pos = at<int32_t>(ws, L.pos);
-  C.weights = at<float>(ws, L.weights);
-  C.out = out;
-  C.T = d.T;
-  C.K = d.K;
-  C.top_k = d.top_k;
   hipLaunchKernelGGL(moe::combine_kernel, dim3((d.K / 4 + 255) / 256, d.T), dim3(256), 0, s, C);
 }
 

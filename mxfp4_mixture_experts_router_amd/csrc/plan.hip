@@ -19,68 +19,107 @@ namespace moe {
 
 namespace {
 
-// One step of a wave-wide arg-max on (value desc, id asc) pairs, exchanging
-// with a DPP-permuted partner inside each row of 16 lanes.
-#define MOE_ARGMAX_DPP(v, id, ctrl)                                                                     \
-  do {                                                                                                  \
-    const float ov_ = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),   \
-                                                                         ctrl, 0xF, 0xF, false));       \
-    const int oi_ = __builtin_amdgcn_mov_dpp(id, ctrl, 0xF, 0xF, false);                                \
-    if (ov_ > v || (ov_ == v && oi_ < id)) {                                                            \
-      v = ov_;                                                                                          \
-      id = oi_;                                                                                         \
-    }                                                                                                   \
-  } while (0)
-
-__device__ __forceinline__ void argmax_xor(float& v, int& id, int mask) {
-  const float ov = __shfl_xor(v, mask);
-  const int oi = __shfl_xor(id, mask);
-  if (ov > v || (ov == v && oi < id)) {
-    v = ov;
-    id = oi;
+// Lanes of the wave whose `loc` routes go to the same local expert as this
+// lane: the expert's bits compared lane against lane with one ballot per bit
+// (E_l <= 512: at most 9), no loop over the distinct experts.
+__device__ __forceinline__ uint64_t same_expert_lanes(bool loc, int e, int bits) {
+  uint64_t m = __ballot(loc);
+  for (int b = 0; b < bits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t one = __ballot(loc && bit);
+    m &= bit ? one : ~one;
   }
+  return m;
 }
 
 // Top-k of one token's logits by one wave: k rounds of a wave-wide arg-max
 // over the not-yet-taken experts (value descending, id ascending).  Lane j < k
-// returns the j-th winner.  Each lane holds kPer logits (E <= 64 * kPer).
+// returns the j-th winner.  Each lane holds kPer logits v[i] of experts
+// lane + 64 i (E <= 64 * kPer; entries past E are never taken).
 template <int kPer>
-__device__ __forceinline__ void wave_topk_n(const float* __restrict__ row, int E, int k, int lane, int& my_id,
-                                            float& my_val) {
-  float v[kPer];
-  uint32_t taken = 0;
+__device__ __forceinline__ void load_logits(const float* __restrict__ row, int E, int lane, float (&v)[kPer]) {
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int idx = lane + 64 * i;
     v[i] = idx < E ? row[idx] : 0.0f;
-    if (idx >= E) taken |= 1u << i;
   }
+}
+
+// Wave-wide max and sum without LDS: DPP inside rows of 16 lanes, then the
+// four row results read as scalars and combined in a fixed order.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float rows_of_four(float v, int which) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), which));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x124>(v));  // row_ror:4
+  v = fmaxf(v, dpp_f<0x128>(v));  // row_ror:8
+  return fmaxf(fmaxf(rows_of_four(v, 0), rows_of_four(v, 16)), fmaxf(rows_of_four(v, 32), rows_of_four(v, 48)));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x124>(v);
+  v += dpp_f<0x128>(v);
+  return (rows_of_four(v, 0) + rows_of_four(v, 16)) + (rows_of_four(v, 32) + rows_of_four(v, 48));
+}
+
+// Exclusive prefix sum over the 64 lanes (DPP row shifts, then the row
+// broadcasts of lanes 15 and 31); total = sum over all lanes.
+__device__ __forceinline__ int wave_exclusive_scan_dpp(int v, int& total) {
+  int x = v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  total = __builtin_amdgcn_readlane(x, 63);
+  return x - v;
+}
+
+// Top-k of one token by one wave, k rounds: the largest free logit (wave max),
+// then the lowest expert id holding it (ballot per slot; slot i holds ids
+// 64 i .. 64 i + 63, so the first slot with a match has the lowest id).
+template <int kPer>
+__device__ __forceinline__ void topk_of(const float (&v)[kPer], int E, int k, int lane, int& my_id, float& my_val) {
+  uint32_t taken = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (lane + 64 * i >= E) taken |= 1u << i;
   my_id = 0;
   my_val = 0.0f;
   for (int j = 0; j < k; ++j) {
-    float best = -__builtin_inff();
-    int bid = 0x7FFFFFFF;
+    float lm = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (!((taken >> i) & 1u)) lm = fmaxf(lm, v[i]);
+    const float m = wave_max(lm);
+    int win = -1;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int idx = lane + 64 * i;
-      const bool free = !((taken >> i) & 1u);
-      if (free && (v[i] > best || (v[i] == best && idx < bid))) {
-        best = v[i];
-        bid = idx;
-      }
+      const uint64_t b = __ballot(!((taken >> i) & 1u) && v[i] == m);
+      if (win < 0 && b != 0) win = 64 * i + __ffsll(static_cast<unsigned long long>(b)) - 1;
     }
-    MOE_ARGMAX_DPP(best, bid, 0xB1);   // quad_perm [1,0,3,2]
-    MOE_ARGMAX_DPP(best, bid, 0x4E);   // quad_perm [2,3,0,1]
-    MOE_ARGMAX_DPP(best, bid, 0x124);  // row_ror:4
-    MOE_ARGMAX_DPP(best, bid, 0x128);  // row_ror:8
-    argmax_xor(best, bid, 16);
-    argmax_xor(best, bid, 32);
-    if ((bid & 63) == lane) taken |= 1u << (bid >> 6);
+    if ((win & 63) == lane) taken |= 1u << (win >> 6);
     if (lane == j) {
-      my_id = bid;
-      my_val = best;
+      my_id = win;
+      my_val = m;
     }
   }
+}
+
+template <int kPer>
+__device__ __forceinline__ void wave_topk_n(const float* __restrict__ row, int E, int k, int lane, int& my_id,
+                                            float& my_val) {
+  float v[kPer];
+  load_logits<kPer>(row, E, lane, v);
+  topk_of<kPer>(v, E, k, lane, my_id, my_val);
 }
 
 __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int lane, int& my_id,
@@ -98,27 +137,37 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, 
   }
 }
 
-// Routing weight of lane j's winner: softmax over the k selected logits, or
-// sigmoid renormalised over the k selected.
 __device__ __forceinline__ float wave_route_weight(float my_val, int k, int scoring, int lane) {
-  const float top0 = __shfl(my_val, 0);
+  const float top0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_val), 0));
   float p = 0.0f;
   if (lane < k) p = (scoring == 0) ? expf(my_val - top0) : 1.0f / (1.0f + expf(-my_val));
-  float s = p;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-  return p / s;
+  return p / wave_sum(p);
 }
 
-__device__ __forceinline__ int wave_exclusive_scan(int v, int lane, int& total) {
-  int incl = v;
+template <int kPer>
+__device__ __forceinline__ void route_tokens(const PlanArgs& P, int* ids_s, int wave, int lane) {
+  constexpr int kMaxPerWave = kFusedRouteTokens / kPlanWaves;
+  float v[kMaxPerWave][kPer];
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
+  for (int j = 0; j < kMaxPerWave; ++j) {
+    const int t = wave + kPlanWaves * j;
+    if (t < P.T) load_logits<kPer>(P.logits + static_cast<size_t>(t) * P.E_global, P.E_global, lane, v[j]);
   }
-  total = __shfl(incl, 63);
-  return incl - v;
+#pragma unroll
+  for (int j = 0; j < kMaxPerWave; ++j) {
+    const int t = wave + kPlanWaves * j;
+    if (t < P.T) {
+      int my_id;
+      float my_val;
+      topk_of<kPer>(v[j], P.E_global, P.top_k, lane, my_id, my_val);
+      const float w = wave_route_weight(my_val, P.top_k, P.scoring, lane);
+      if (lane < P.top_k) {
+        ids_s[t * P.top_k + lane] = my_id;
+        P.weights_ws[t * P.top_k + lane] = w;
+        P.ids_ws[t * P.top_k + lane] = my_id;
+      }
+    }
+  }
 }
 
 }  // namespace
@@ -143,20 +192,23 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 // Single workgroup of 16 waves.
 //  0. (router-logits mode, T <= kFusedRouteTokens) route every token, ids to LDS;
 //  1. the R = T*k routes are split into 16 contiguous segments, one per wave;
-//     per-segment histograms of local experts (LDS);
-//  2. per expert, exclusive prefix over segments, then over experts, so that
-//     hist[w][e] becomes the first output slot of segment w's routes to e;
-//  3. each wave walks its segment in 64-route chunks; lanes with the same
-//     expert rank themselves by lane index (ballot), which keeps the sort
-//     stable, and the chunk's leader advances the slot;
+//     per-segment histograms of local experts (LDS), counted per 64-route
+//     chunk by the lowest lane of each group of same-expert lanes (groups
+//     come from one ballot per expert-id bit);
+//  2. per expert, exclusive prefix over segments (a 16-lane DPP row scan),
+//     then over experts, so that entry (e, w) becomes the first output slot of
+//     segment w's routes to e;
+//  3. each wave walks its segment again; a route's rank among the lanes of
+//     its group before it keeps the sort stable, and the group's lowest lane
+//     advances the slot for the next chunk;
 //  4. the touched experts, in expert order, become two work lists: experts
 //     with at most kGemvMaxTokens routes (GEMV regime, with their tokens) and
 //     the others (MFMA regime);
 //  5. (decode regime) each expert's routes, in plan order, are cut into
-//     passes of pass_tokens routes; every route writes its token into its
+//     passes of 2^pass_shift routes; every route writes its index into its
 //     pass entry as it is placed, and the pass's first route the header.
 __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
-  __shared__ int hist[kPlanWaves][kMaxLocalExperts];
+  __shared__ int hist[kMaxLocalExperts * kPlanWaves];  // [expert][segment]
   __shared__ int base_e[kMaxLocalExperts + 1];
   __shared__ int ids_s[kFusedRouteTokens * kMaxTopK];
   __shared__ int pass_base[kMaxLocalExperts];
@@ -165,43 +217,50 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
   const bool fused = P.logits != nullptr;
 
   if (fused) {
-    for (int t = wave; t < P.T; t += kPlanWaves) {
-      int my_id;
-      float my_val;
-      wave_topk(P.logits + static_cast<size_t>(t) * P.E_global, P.E_global, P.top_k, lane, my_id, my_val);
-      const float w = wave_route_weight(my_val, P.top_k, P.scoring, lane);
-      if (lane < P.top_k) {
-        ids_s[t * P.top_k + lane] = my_id;
-        P.weights_ws[t * P.top_k + lane] = w;
-        P.ids_ws[t * P.top_k + lane] = my_id;
-      }
-    }
+    // a wave routes tokens wave, wave + 16, ... (at most kFusedRouteTokens / 16);
+    // all of their logits are requested before the first top-k
+    if (P.E_global <= 64) route_tokens<1>(P, ids_s, wave, lane);
+    else if (P.E_global <= 128) route_tokens<2>(P, ids_s, wave, lane);
+    else if (P.E_global <= 256) route_tokens<4>(P, ids_s, wave, lane);
+    else if (P.E_global <= 512) route_tokens<8>(P, ids_s, wave, lane);
+    else route_tokens<16>(P, ids_s, wave, lane);
   } else if (P.w_in != nullptr) {
     for (int r = tid; r < R; r += blockDim.x) P.weights_ws[r] = P.w_in[r];
   }
-  for (int i = tid; i < kPlanWaves * E_l; i += blockDim.x) hist[i / E_l][i % E_l] = 0;
+  for (int i = tid; i < kPlanWaves * E_l; i += blockDim.x) hist[i] = 0;
   __syncthreads();
 
+  // the R routes in 16 contiguous segments, one per wave, 64 at a time
   const int seg = (R + kPlanWaves - 1) / kPlanWaves;
   const int s0 = min(R, wave * seg), s1 = min(R, s0 + seg);
-  for (int r = s0 + lane; r < s1; r += 64) {
-    const int e = (fused ? ids_s[r] : P.ids_in[r]) - offset;
-    if (static_cast<unsigned>(e) < static_cast<unsigned>(E_l)) {
-      atomicAdd(&hist[wave][e], 1);
-    } else {
-      P.pos[r] = -1;
-    }
+  const int bits = 32 - __clz(max(E_l - 1, 1));
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int b = s0; b < s1; b += 64) {
+    const int r = b + lane;
+    const int e = (r < s1) ? (fused ? ids_s[r] : P.ids_in[r]) - offset : -1;
+    const bool loc = (r < s1) && static_cast<unsigned>(e) < static_cast<unsigned>(E_l);
+    if (r < s1 && !loc) P.pos[r] = -1;
+    const uint64_t m = same_expert_lanes(loc, e, bits);
+    if (loc && (m & lt) == 0) hist[e * kPlanWaves + wave] += __popcll(m);  // the group's lowest lane
+    __builtin_amdgcn_wave_barrier();
   }
   __syncthreads();
 
-  for (int e = tid; e < E_l; e += blockDim.x) {
-    int run = 0;
-    for (int w = 0; w < kPlanWaves; ++w) {
-      const int c = hist[w][e];
-      hist[w][e] = run;
-      run += c;
+  // per expert, exclusive prefix over the 16 segments: one row of 16 lanes
+  // per expert (lane = segment), DPP row shifts; the row's last lane has the total
+  for (int i0 = 0; i0 < kPlanWaves * E_l; i0 += blockDim.x) {  // whole rows of 16 stay together
+    const int i = i0 + tid;
+    const int e = i >> 4, w = i & 15;
+    const int v = e < E_l ? hist[i] : 0;
+    int x = v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    if (e < E_l) {
+      hist[i] = x - v;
+      if (w == 15) base_e[e] = x;  // count of expert e for now
     }
-    base_e[e] = run;  // count of expert e for now
   }
   __syncthreads();
 
@@ -217,7 +276,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
       local += c[i];
     }
     int total;
-    int run = wave_exclusive_scan(local, lane, total);
+    int run = wave_exclusive_scan_dpp(local, total);
 #pragma unroll
     for (int i = 0; i < per; ++i) {
       const int e = lane * per + i;
@@ -228,69 +287,72 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
       }
       run += c[i];
     }
+    int nz = 0;
+#pragma unroll
+    for (int i = 0; i < per; ++i) nz += c[i] > 0;
+    int n_touched;
+    (void)wave_exclusive_scan_dpp(nz, n_touched);
     if (lane == 0) {
       P.offsets[E_l] = total;
       base_e[E_l] = total;
+      P.plan->n_touched = n_touched;
+      P.plan->R_local = total;
     }
     if (P.passes != nullptr) {
-      const int tp = P.pass_tokens;
+      const int sh = P.pass_shift, tp1 = (1 << sh) - 1;
       int np = 0;
 #pragma unroll
-      for (int i = 0; i < per; ++i) np += (c[i] + tp - 1) / tp;
+      for (int i = 0; i < per; ++i) np += (c[i] + tp1) >> sh;
       int np_total;
-      int prun = wave_exclusive_scan(np, lane, np_total);
+      int prun = wave_exclusive_scan_dpp(np, np_total);
 #pragma unroll
       for (int i = 0; i < per; ++i) {
         const int e = lane * per + i;
         if (e < E_l) pass_base[e] = prun;
-        prun += (c[i] + tp - 1) / tp;
+        prun += (c[i] + tp1) >> sh;
       }
       if (lane == 0) P.plan->n_passes = np_total;
     }
   }
   __syncthreads();
 
-  for (int i = tid; i < kPlanWaves * E_l; i += blockDim.x) hist[i / E_l][i % E_l] += base_e[i % E_l];
+  for (int i = tid; i < kPlanWaves * E_l; i += blockDim.x) hist[i] += base_e[i >> 4];
   __syncthreads();
 
+  // placement: a route's slot is its expert's segment base plus its rank
+  // among the same-expert routes before it in the segment (stable)
   for (int b = s0; b < s1; b += 64) {
     const int r = b + lane;
     const int e = (r < s1) ? (fused ? ids_s[r] : P.ids_in[r]) - offset : -1;
     const bool loc = (r < s1) && static_cast<unsigned>(e) < static_cast<unsigned>(E_l);
-    uint64_t rem = __ballot(loc);
-    while (rem) {
-      const int leader = __ffsll(static_cast<unsigned long long>(rem)) - 1;
-      const int key = __shfl(e, leader);
-      const uint64_t m = __ballot(loc && e == key);
-      if (loc && e == key) {
-        const int rank = __popcll(m & ((1ull << lane) - 1ull));
-        const int p = hist[wave][key] + rank;
-        P.routes[p] = r;
-        P.pos[r] = p;
-        if (P.passes != nullptr) {
-          const int tp = P.pass_tokens;
-          const int j = p - base_e[key];
-          const int pass = j / tp, slot = j - pass * tp;
-          PassEntry* pe = P.passes + pass_base[key] + pass;
-          pe->tok[slot] = static_cast<uint16_t>(r / P.top_k);
-          if (slot == 0) {
-            pe->e = key;
-            pe->nt = min(tp, base_e[key + 1] - base_e[key] - pass * tp);
-            pe->p = p;
-          }
+    const uint64_t m = same_expert_lanes(loc, e, bits);
+    if (loc) {
+      const int p = hist[e * kPlanWaves + wave] + __popcll(m & lt);
+      P.routes[p] = r;
+      P.pos[r] = p;
+      if (P.passes != nullptr) {
+        const int sh = P.pass_shift, tp = 1 << sh;
+        const int j = p - base_e[e];
+        const int pass = j >> sh, slot = j & (tp - 1);
+        PassEntry* pe = P.passes + pass_base[e] + pass;
+        pe->rte[slot] = static_cast<uint16_t>(r);
+        if (slot == 0) {
+          pe->e = e;
+          pe->nt = min(tp, base_e[e + 1] - base_e[e] - pass * tp);
+          pe->p = p;
         }
       }
-      __builtin_amdgcn_wave_barrier();
-      if (lane == leader) hist[wave][key] += __popcll(m);
-      __builtin_amdgcn_wave_barrier();
-      rem &= ~m;
     }
+    __builtin_amdgcn_wave_barrier();
+    if (loc && (m & lt) == 0) hist[e * kPlanWaves + wave] += __popcll(m);  // next chunk of the segment
+    __builtin_amdgcn_wave_barrier();
   }
 
   __syncthreads();  // routes[] complete
 
-  // work lists: touched experts in ascending order, split by regime (wave 0)
-  if (wave == 0) {
+  // work lists: touched experts in ascending order, split by regime (wave 0);
+  // calls served by the stream kernel alone need only the counts
+  if (wave == 0 && P.lists) {
     int ng = 0, nm = 0;
     for (int e0 = 0; e0 < E_l; e0 += 64) {
       const int e = e0 + lane;
@@ -319,8 +381,6 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
       nm += __popcll(mm);
     }
     if (lane == 0) {
-      P.plan->n_touched = ng + nm;
-      P.plan->R_local = base_e[E_l];
       P.plan->n_gemv = ng;
       P.plan->n_mfma = nm;
     }

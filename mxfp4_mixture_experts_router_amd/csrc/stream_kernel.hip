@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
     l_p = __builtin_amdgcn_readfirstlane(pe->p);
     l_row0 = __builtin_amdgcn_readfirstlane(pe->pad0) * kItemRows;
     const int tt = stt < l_nt ? stt : 0;
-    const int xrow = A.tok_from_pass ? static_cast<int>(pe->tok[tt]) : l_p + tt;
+    const int xrow = A.tok_from_pass ? static_cast<int>(pe->rte[tt]) / A.top_k : l_p + tt;
     l_xoff = static_cast<uint32_t>(xrow) * static_cast<uint32_t>(red) * 2u;
     // this wave's sub-tile: rows are a multiple of 16, so a sub-tile is all in
     // or all out; an out sub-tile re-reads the expert's last 16 rows (results dropped)
@@ -304,7 +304,8 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
           pk.y = static_cast<uint32_t>(h[2]) | (static_cast<uint32_t>(h[3]) << 16);
           *reinterpret_cast<uint2*>(A.a_out + p * rows + row0w + rl) = pk;
         } else {
-          *reinterpret_cast<float4*>(A.o_out + p * rows + row0w + rl) =
+          const size_t orow = A.o_by_route ? static_cast<size_t>(etab[ci].rte[r]) : p;
+          *reinterpret_cast<float4*>(A.o_out + orow * rows + row0w + rl) =
               make_float4(acc0[0] + b0[0], acc0[1] + b0[1], acc0[2] + b0[2], acc0[3] + b0[3]);
         }
       }

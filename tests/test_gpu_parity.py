@@ -354,6 +354,38 @@ def test_layer_no_local_route_writes_zeros():
     assert np.array_equal(y, np.zeros_like(y)) and not np.signbit(y).any()
 
 
+def test_layer_no_local_route_writes_zeros_stream_path():
+    cfg = _cfg(K=1024, I=1024, E_global=16, E_local=4, expert_offset=12, top_k=2)
+    w = make_weights(cfg)
+    inp = make_topk_inputs(cfg, 6, seed=9)
+    inp.topk_ids[:] = np.array([0, 1], np.int32)
+    y = bf16_to_np(run_decode(cfg, DeviceLayer(w), inp))
+    assert np.array_equal(y, np.zeros_like(y)) and not np.signbit(y).any()
+
+
+@pytest.mark.parametrize("T", [3, 7, 24])
+def test_down_step_twice_on_one_plan(T):
+    # the combine fused into the down projection counts finished row tiles in
+    # the workspace; a second down call on the same plan must combine again
+    t = torch()
+    cfg = _cfg(K=1056, I=1120, E_global=8, E_local=6, expert_offset=1, top_k=3, bias=True)
+    w = make_weights(cfg)
+    inp = make_inputs(cfg, T, t_index=T)
+    ref = oracle.moe_forward_cfg(cfg, w, inp)
+    layer = DeviceLayer(w)
+    d = desc_for(cfg, T)
+    ws = moe.moe_mxfp4_plan(d, router_logits=dev_f32(inp.logits))
+    moe.moe_mxfp4_gate_up(d, dev_bf16(inp.x), layer.w13p, layer.w13s, ws, w13_bias=layer.b13)
+    outs = []
+    for _ in range(2):
+        out = t.full((T, cfg.K), float("nan"), dtype=t.bfloat16, device="cuda")
+        moe.moe_mxfp4_down(d, layer.w2p, layer.w2s, out, ws, w2_bias=layer.b2)
+        t.cuda.synchronize()
+        outs.append(bf16_bits_np(out))
+    assert np.array_equal(outs[0], outs[1])
+    _assert_close(bf16_to_np(out), ref["y"], f"down twice T{T}")
+
+
 def test_layer_exact_chain_bit_exact():
     from test_oracle_layer import build_exact_chain
     t = torch()
