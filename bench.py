@@ -56,6 +56,8 @@ def parse():
     p.add_argument("--tokens", default=None, help="comma-separated T values (default: the layer's decode sweep)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--rotate-mb", type=float, default=512.0, help="bytes one replica rotation must exceed")
+    p.add_argument("--copy-probe", type=float, default=0.0,
+                   help="only copy this many MiB device to device a few times and exit (counter calibration)")
     p.add_argument("--layout", default="tile16", choices=("rows", "tile16"),
                    help="packed weight storage order (tile16: tiled in place once, before any timing)")
     return p.parse_args()
@@ -98,6 +100,18 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_probe > 0:
+        # a plain copy of known size: the FETCH_SIZE / WRITE_SIZE counters of
+        # its kernel calibrate the same counters of the layer kernels
+        n = int(args.copy_probe * (1 << 20))
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 4}), flush=True)
+        return
 
     import mxfp4_mixture_experts_router_amd as moe
     from workloads import get_config, make_inputs, make_weights
@@ -236,13 +250,33 @@ def main():
         "roofline": {"kernel": "gate/up projection: moe::stream_kernel<true,*> (one launch per call)",
                      "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_launch_us": round(w13_avg_us, 2),
+                     "traffic": measured_traffic(cfg, tokens, args.layout), "avg_launch_us": round(w13_avg_us, 2),
                      "algorithmic_bytes_per_launch": int(w13_avg_bytes)},
         "device": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, w0, reps[0], torch, moe, args.layout)
     print(json.dumps(line), flush=True)
+
+
+def measured_traffic(cfg, tokens, layout):
+    """HBM bytes per gate/up launch (mean over T) from the committed counter runs
+    (profiles/roofline_traffic.json), or None when they do not cover this
+    workload or the kernel's sources have changed since they were taken."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "roofline_traffic.json")) as f:
+            prof = json.load(f)
+        with open(os.path.join(ROOT, "mxfp4_mixture_experts_router_amd", "libmoe_mxfp4.manifest.json")) as f:
+            man = json.load(f)
+    except (OSError, ValueError):
+        return None
+    built = {**man.get("sources", {}), **man.get("headers", {})}
+    if any(built.get(k) != v for k, v in prof.get("sources_sha256", {}).items()):
+        return None
+    per_t = prof.get("traffic_bytes_per_launch", {})
+    if cfg.name != "gptoss20b" or layout != "tile16" or any(str(t) not in per_t for t in tokens):
+        return None
+    return int(np.mean([per_t[str(t)] for t in tokens]))
 
 
 def cpu_baseline(cfg, w0, rep0, torch, moe, layout):
