@@ -44,6 +44,15 @@ Readings where the pages are silent (each is listed in the design doc):
   the local subset; in ids mode the given weights are used as they are.
 * the bf16 rounding is round-to-nearest-even.
 
+MXFP4 encoder (``encode_mxfp4``): "GLM-5.2 and GLM-5.3 (744B) in MXFP4 on
+Gaudi 2", What was built, MXFP4 encoder: the OCP shared exponent is
+floor(log2(amax)) - 2 (values above 6 * 2^X clamp); Quark bumps the exponent
+when amax / 2^X >= 7.  Readings where the page is silent: elements round to
+the nearest E2M1 value with ties to the even code (round-to-nearest-even,
+saturating at 6); the sign bit is the input's sign bit (a negative value that
+rounds to zero gives code 8, -0); amax = 0 gives exponent -127 (scale byte 0);
+the exponent is clipped to [-127, 127], so scale byte 255 (NaN) never occurs.
+
 The tiled weight layout (``tile16``) is this library's own storage order, not
 the pages': the pages' kernels read the served row layout and name a repack
 as the next step they chose not to take, to keep one copy of the experts.
@@ -118,6 +127,56 @@ def dequantize(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # bf16
 # --------------------------------------------------------------------------
+
+# --------------------------------------------------------------------------
+# MXFP4 encoder
+# --------------------------------------------------------------------------
+
+OCP = "ocp"
+QUARK = "quark"
+
+
+def round_to_e2m1(a: np.ndarray) -> np.ndarray:
+    """Non-negative float64 -> E2M1 magnitude code 0..7: the nearest grid value,
+    ties to the even code (the even codes are the grid values with mantissa 0)."""
+    a = np.asarray(a, dtype=np.float64)
+    dist = np.abs(a[..., None] - E2M1_MAGNITUDE.astype(np.float64))
+    best = dist.min(axis=-1, keepdims=True)
+    tied = dist == best
+    # among the nearest codes prefer an even one; there are at most two
+    even = tied & (np.arange(8) % 2 == 0)
+    pick = np.where(even.any(axis=-1, keepdims=True), even, tied)
+    return np.argmax(pick, axis=-1).astype(np.uint8)
+
+
+def encode_mxfp4(values: np.ndarray, rule: str = QUARK):
+    """float32/bfloat16-valued array [..., cols] (cols % 32 == 0) -> (packed
+    uint8 [..., cols/2], scales uint8 [..., cols/32]).
+
+    Per block of 32: X = floor(log2(amax)) - 2 from the binary exponent of
+    amax (exact), plus one under the Quark rule when amax / 2^X >= 7; scale
+    byte X + 127; code = sign bit | E2M1 round-to-nearest-even of v / 2^X.
+    """
+    v = np.asarray(values, dtype=np.float64)
+    *lead, cols = v.shape
+    assert cols % MX_BLOCK == 0
+    b = v.reshape(*lead, cols // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(b).max(axis=-1)
+    _, e = np.frexp(amax)                       # amax = m * 2^e, 0.5 <= m < 1
+    x = e.astype(np.int64) - 1 - 2
+    if rule == QUARK:
+        x = np.where(np.ldexp(amax, -x) >= 7.0, x + 1, x)
+    elif rule != OCP:
+        raise ValueError(rule)
+    x = np.where(amax == 0, -127, x)
+    x = np.clip(x, -127, 127)
+    y = np.ldexp(b, -x[..., None])              # exact: a power-of-two scaling
+    codes = round_to_e2m1(np.abs(y)) | np.where(np.signbit(y), 8, 0).astype(np.uint8)
+    codes = codes.reshape(*lead, cols)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    scales = (x + 127).astype(np.uint8)
+    return packed, scales
+
 
 # --------------------------------------------------------------------------
 # tiled weight layout
