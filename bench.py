@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--rotate-mb", type=float, default=512.0, help="bytes one replica rotation must exceed")
     p.add_argument("--copy-probe", type=float, default=0.0,
                    help="only copy this many MiB device to device a few times and exit (counter calibration)")
+    p.add_argument("--encode", action="store_true",
+                   help="measure the MXFP4 encoder instead (bf16 weights of the layer's w13 -> packed + scales)")
     p.add_argument("--layout", default="tile16", choices=("rows", "tile16"),
                    help="packed weight storage order (tile16: tiled in place once, before any timing)")
     return p.parse_args()
@@ -115,6 +117,10 @@ def main():
 
     import mxfp4_mixture_experts_router_amd as moe
     from workloads import get_config, make_inputs, make_weights
+
+    if args.encode:
+        print(json.dumps(encode_bench(torch, moe, get_config(args.config), args)), flush=True)
+        return
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -257,6 +263,37 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, w0, reps[0], torch, moe, args.layout)
     print(json.dumps(line), flush=True)
+
+
+def encode_bench(torch, moe, cfg, args):
+    """MXFP4 encoder throughput: the layer's w13 as bf16 [E, 2I, K] -> packed +
+    scales, Quark rule; bytes = bf16 in + packed + scales out."""
+    E, K, I = cfg.E_local, cfg.K, cfg.I
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1000 * cfg.index + 7)
+    x = (torch.randn((E, 2 * I, K), device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    packed = torch.empty((E, 2 * I, K // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((E, 2 * I, K // 32), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, args.warmup)):
+            moe.moe_mxfp4_encode(x, packed, scales, stream=stream)
+        stream.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            moe.moe_mxfp4_encode(x, packed, scales, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / args.steps
+    nbytes = x.numel() * 2 + packed.numel() + scales.numel()
+    gbs = nbytes / us / 1e3
+    return {"metric": "MXFP4 encode GB/s (bf16 in + packed/scales out)", "value": round(gbs, 1), "unit": "GB/s",
+            "us_per_call": round(us, 2), "bytes_per_call": int(nbytes), "steps": args.steps,
+            "config": {"workload": f"w13 of the {cfg.name} layer as bf16 [{E}, {2 * I}, {K}], Quark rule"},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
 def measured_traffic(cfg, tokens, layout):

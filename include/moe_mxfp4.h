@@ -68,8 +68,21 @@ extern "C" {
  * block-major, block b of row r at byte 256*b + 16*r of the group.  Each step
  * of the expert kernels then reads one contiguous 1 KB run per wave; the row
  * layout is read in 64-byte pieces of 16 rows.  Same bytes, one copy.       */
+#define MOE_ENCODE_OCP     0    /* shared exponent floor(log2(amax)) - 2             */
+#define MOE_ENCODE_QUARK   1    /* the same, plus one when amax / 2^X >= 7           */
+
 #define MOE_LAYOUT_ROWS    0    /* the served layout of "Read the served layout"      */
 #define MOE_LAYOUT_TILE16  1
+
+/* Row pairing of the down projection at decode token counts (a performance
+ * control; the results are bit-identical either way).  Paired, each wave of
+ * the stream kernel computes two 16-row sets 16 rows apart, so every step
+ * loads two weight blocks per lane, as the gate/up projection does; it needs
+ * K % 32 == 0.  AUTO pairs when the paired work items still fill every
+ * resident workgroup slot of the GPU.                                        */
+#define MOE_PAIRING_AUTO   0
+#define MOE_PAIRING_ON     1    /* whenever K % 32 == 0                               */
+#define MOE_PAIRING_OFF    2
 
 /* ---- layer descriptor --------------------------------------------------- */
 typedef struct moe_mxfp4_desc {
@@ -86,6 +99,7 @@ typedef struct moe_mxfp4_desc {
     float   swiglu_alpha;   /* 1.702 for gpt-oss  (MOE_ACT_SWIGLU_OAI only)              */
     float   swiglu_limit;   /* 7.0 for gpt-oss    (MOE_ACT_SWIGLU_OAI only)              */
     int32_t weight_layout;  /* MOE_LAYOUT_* of w13_packed and w2_packed                   */
+    int32_t down_pairing;   /* MOE_PAIRING_* (0 = automatic)                              */
 } moe_mxfp4_desc;
 
 /*
@@ -213,6 +227,22 @@ int moe_mxfp4_bucket(const moe_mxfp4_desc* desc, const int32_t* topk_ids,
  */
 int moe_mxfp4_dequant(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t cols,
                       int32_t out_dtype, void* out, void* stream);
+
+/*
+ * MXFP4 encoder ("GLM-5.2 and GLM-5.3 (744B) in MXFP4 on Gaudi 2", What was
+ * built, MXFP4 encoder): in [rows, cols] fp32 (in_dtype MOE_DTYPE_F32) or
+ * bf16 bits (MOE_DTYPE_BF16) -> packed u8 [rows, cols/2] (element 2c in the
+ * low nibble of byte c) and scales u8 [rows, cols/32] (E8M0).  Per block of
+ * 32: X = floor(log2(amax)) - 2 (MOE_ENCODE_OCP), plus one when
+ * amax / 2^X >= 7 (MOE_ENCODE_QUARK); each element v / 2^X rounds to the
+ * nearest E2M1 value with ties to the even code, saturating at 6, and keeps
+ * the sign bit of v; amax = 0 gives scale byte 0; X is clipped to
+ * [-127, 127].  Inputs must be finite.  cols % 32 == 0 (MOE_ERR_SHAPE);
+ * in and packed 16-byte aligned (MOE_ERR_ALIGN).  A weight-preparation step
+ * (the input of the layer), not part of a layer call.
+ */
+int moe_mxfp4_encode(const void* in, int32_t in_dtype, int64_t rows, int64_t cols, int32_t rule,
+                     uint8_t* packed, uint8_t* scales, void* stream);
 
 /*
  * In-place change of packed weight storage order between MOE_LAYOUT_ROWS and

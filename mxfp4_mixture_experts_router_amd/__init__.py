@@ -19,6 +19,8 @@ from ._lib import (  # noqa: F401
     MOE_ACT_SWIGLU_OAI,
     MOE_DTYPE_BF16,
     MOE_DTYPE_F32,
+    MOE_ENCODE_OCP,
+    MOE_ENCODE_QUARK,
     MOE_ERR_ALIGN,
     MOE_ERR_HIP,
     MOE_ERR_MODE,
@@ -27,6 +29,9 @@ from ._lib import (  # noqa: F401
     MOE_ERR_WORKSPACE,
     MOE_LAYOUT_ROWS,
     MOE_LAYOUT_TILE16,
+    MOE_PAIRING_AUTO,
+    MOE_PAIRING_OFF,
+    MOE_PAIRING_ON,
     MOE_OK,
     MOE_SCORING_SIGMOID,
     MOE_SCORING_SOFTMAX,
@@ -36,12 +41,13 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "MoeDesc", "MoeError", "make_desc", "moe_mxfp4_workspace_bytes", "moe_mxfp4_decode",
     "moe_mxfp4_plan", "moe_mxfp4_gate_up", "moe_mxfp4_down", "moe_mxfp4_route", "moe_mxfp4_bucket",
-    "moe_mxfp4_dequant", "moe_mxfp4_tile_weights", "moe_mxfp4_status_string", "moe_mxfp4_version",
+    "moe_mxfp4_dequant", "moe_mxfp4_tile_weights", "moe_mxfp4_encode", "moe_mxfp4_status_string", "moe_mxfp4_version",
 ]
 
 _SCORING = {"softmax": MOE_SCORING_SOFTMAX, "sigmoid": MOE_SCORING_SIGMOID}
 _ACT = {"silu_mul": MOE_ACT_SILU_MUL, "swiglu_oai": MOE_ACT_SWIGLU_OAI}
 _LAYOUT = {"rows": MOE_LAYOUT_ROWS, "tile16": MOE_LAYOUT_TILE16}
+_PAIRING = {"auto": MOE_PAIRING_AUTO, "on": MOE_PAIRING_ON, "off": MOE_PAIRING_OFF}
 
 
 class MoeError(RuntimeError):
@@ -52,11 +58,12 @@ class MoeError(RuntimeError):
 
 def make_desc(T: int, K: int, I: int, E_global: int, E_local: int, top_k: int, expert_offset: int = 0,
               scoring="softmax", activation="silu_mul", swiglu_alpha: float = 1.702,
-              swiglu_limit: float = 7.0, weight_layout="rows") -> MoeDesc:
+              swiglu_limit: float = 7.0, weight_layout="rows", down_pairing="auto") -> MoeDesc:
     sc = _SCORING[scoring] if isinstance(scoring, str) else int(scoring)
     ac = _ACT[activation] if isinstance(activation, str) else int(activation)
     wl = _LAYOUT[weight_layout] if isinstance(weight_layout, str) else int(weight_layout)
-    return MoeDesc(T, K, I, E_global, E_local, expert_offset, top_k, sc, ac, swiglu_alpha, swiglu_limit, wl)
+    dp = _PAIRING[down_pairing] if isinstance(down_pairing, str) else int(down_pairing)
+    return MoeDesc(T, K, I, E_global, E_local, expert_offset, top_k, sc, ac, swiglu_alpha, swiglu_limit, wl, dp)
 
 
 def moe_mxfp4_status_string(status: int) -> str:
@@ -223,6 +230,27 @@ def moe_mxfp4_bucket(desc: MoeDesc, topk_ids, counts, offsets, routes, workspace
         _ptr(routes, torch.int32, (d.T * d.top_k,), "routes"),
         wsp, wsn, _stream(stream)), "moe_mxfp4_bucket")
     return ws
+
+
+def moe_mxfp4_encode(values, packed, scales, rule="quark", stream=None):
+    """values fp32 or bf16 [..., cols] -> packed u8 [..., cols/2] and scales u8 [..., cols/32] (MXFP4)."""
+    torch = _torch()
+    if values.dtype == torch.float32:
+        code = MOE_DTYPE_F32
+    elif values.dtype == torch.bfloat16:
+        code = MOE_DTYPE_BF16
+    else:
+        raise TypeError(f"values must be float32 or bfloat16, got {values.dtype}")
+    if values.dim() < 1:
+        raise ValueError("values must have at least 1 dimension")
+    cols = values.shape[-1]
+    rows = values.numel() // cols if cols else 0
+    lead = tuple(values.shape[:-1])
+    r = {"ocp": MOE_ENCODE_OCP, "quark": MOE_ENCODE_QUARK}[rule] if isinstance(rule, str) else int(rule)
+    _check(_lib.lib().moe_mxfp4_encode(
+        _ptr(values, values.dtype, tuple(values.shape), "values"), code, rows, cols, r,
+        _ptr(packed, torch.uint8, lead + (cols // 2,), "packed"),
+        _ptr(scales, torch.uint8, lead + (cols // 32,), "scales"), _stream(stream)), "moe_mxfp4_encode")
 
 
 def moe_mxfp4_tile_weights(packed, inverse=False, stream=None):

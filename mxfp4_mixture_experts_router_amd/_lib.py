@@ -27,8 +27,13 @@ MOE_ACT_SILU_MUL = 0
 MOE_ACT_SWIGLU_OAI = 1
 MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
+MOE_ENCODE_OCP = 0
+MOE_ENCODE_QUARK = 1
 MOE_LAYOUT_ROWS = 0
 MOE_LAYOUT_TILE16 = 1
+MOE_PAIRING_AUTO = 0
+MOE_PAIRING_ON = 1
+MOE_PAIRING_OFF = 2
 
 EXPORTED = (
     "moe_mxfp4_workspace_bytes",
@@ -40,6 +45,7 @@ EXPORTED = (
     "moe_mxfp4_down",
     "moe_mxfp4_dequant",
     "moe_mxfp4_tile_weights",
+    "moe_mxfp4_encode",
     "moe_mxfp4_status_string",
     "moe_mxfp4_version",
 )
@@ -59,6 +65,7 @@ class MoeDesc(ctypes.Structure):
         ("swiglu_alpha", ctypes.c_float),
         ("swiglu_limit", ctypes.c_float),
         ("weight_layout", ctypes.c_int32),
+        ("down_pairing", ctypes.c_int32),
     ]
 
 
@@ -78,6 +85,7 @@ _SIGNATURES = {
     "moe_mxfp4_bucket": (_I32, [_DESC, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_mxfp4_dequant": (_I32, [_P, _P, _I64, _I64, _I32, _P, _P]),
     "moe_mxfp4_tile_weights": (_I32, [_P, _I64, _I64, _I32, _P]),
+    "moe_mxfp4_encode": (_I32, [_P, _I32, _I64, _I64, _I32, _P, _P, _P]),
     "moe_mxfp4_status_string": (ctypes.c_char_p, [_I32]),
     "moe_mxfp4_version": (ctypes.c_char_p, []),
 }

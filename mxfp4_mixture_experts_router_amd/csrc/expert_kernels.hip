@@ -489,6 +489,86 @@ __global__ __launch_bounds__(256) void tile_kernel(uint8_t* packed, int64_t grou
   }
 }
 
+// MXFP4 encoder ("GLM-5.2 and GLM-5.3 (744B) in MXFP4 on Gaudi 2", What was
+// built, MXFP4 encoder): per 32-value block X = floor(log2(amax)) - 2, plus
+// one under the Quark rule when amax / 2^X >= 7; elements v / 2^X rounded to
+// the E2M1 grid with ties to the even code, saturating at 6; sign from the
+// sign bit.  Four lanes per block, eight values per lane; every step is exact
+// (power-of-two scaling, a correctly rounded convert), so the bytes are unique.
+namespace {
+
+// floor(log2(a)) for a finite a > 0, from the bits (subnormals included)
+__device__ __forceinline__ int floor_log2(float a) {
+  const uint32_t b = __float_as_uint(a);
+  const int e = static_cast<int>(b >> 23);
+  return e > 0 ? e - 127 : (31 - __clz(static_cast<int>(b & 0x7FFFFFu))) - 149;
+}
+
+}  // namespace
+
+template <bool kBf16>
+__global__ __launch_bounds__(256) void encode_kernel(const void* __restrict__ in, int64_t n_blocks, int quark,
+                                                     uint8_t* __restrict__ packed, uint8_t* __restrict__ scales) {
+  // lane slot g covers eight values of block g >> 2; a thread takes kEncodePer
+  // slots one grid width apart, loading all of them before any compute.  The
+  // grid width is a multiple of 4, so the four lanes of a block stay a quad.
+  const int64_t slots = n_blocks * 4, width = static_cast<int64_t>(gridDim.x) * 256;
+  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  float v[kEncodePer][8];
+#pragma unroll
+  for (int j = 0; j < kEncodePer; ++j) {
+    const int64_t g = min(g0 + j * width, slots - 1);  // surplus slots re-read the last one (not stored)
+    if (kBf16) {
+      const uint4 w = reinterpret_cast<const uint4*>(in)[g];
+      const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[j][2 * i] = __uint_as_float(d[i] << 16);
+        v[j][2 * i + 1] = __uint_as_float(d[i] & 0xFFFF0000u);
+      }
+    } else {
+      const float4 a = reinterpret_cast<const float4*>(in)[2 * g];
+      const float4 b = reinterpret_cast<const float4*>(in)[2 * g + 1];
+      v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
+      v[j][4] = b.x; v[j][5] = b.y; v[j][6] = b.z; v[j][7] = b.w;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kEncodePer; ++j) {
+    const int64_t g = g0 + j * width;
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[j][i]));
+    m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m), 0xB1, 0xF, 0xF, false)));
+    m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, m), 0x4E, 0xF, 0xF, false)));
+    int x = -127;
+    if (m > 0.0f) {
+      x = floor_log2(m) - 2;
+      if (quark && ldexpf(m, -x) >= 7.0f) ++x;
+      x = min(max(x, -127), 127);
+    }
+    // y = v * 2^-x is exact (a power-of-two step); the hardware convert at
+    // unit scale rounds |y| to the nearest E2M1 magnitude, a tie to the even
+    // code, saturating at 6, and keeps the sign bit (also of -0); the first
+    // operand of a pair lands in the low nibble
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = ldexpf(v[j][i], -x);
+    uint32_t word = 0;
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[0], y[1], 1.0f, 0);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[2], y[3], 1.0f, 1);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[4], y[5], 1.0f, 2);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[6], y[7], 1.0f, 3);
+    if (g < slots) {
+      reinterpret_cast<uint32_t*>(packed)[g] = word;
+      if ((g & 3) == 0) scales[g >> 2] = static_cast<uint8_t>(x + 127);
+    }
+  }
+}
+
+template __global__ void encode_kernel<true>(const void*, int64_t, int, uint8_t*, uint8_t*);
+template __global__ void encode_kernel<false>(const void*, int64_t, int, uint8_t*, uint8_t*);
+
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ packed,
                                                       const uint8_t* __restrict__ scales, int64_t n_blocks,
                                                       int out_bf16, void* __restrict__ out) {

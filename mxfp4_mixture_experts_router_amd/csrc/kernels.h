@@ -186,14 +186,20 @@ __global__ void gemv_kernel(ExpertArgs A);
 template <bool kGateUp, int kGroups>
 __global__ void mfma_kernel(ExpertArgs A);
 // Decode regime: kSplit waves share one 16-row sub-tile and split the
-// reduction (kSplit = 4, 2 or 1 for up to 4, 8 or 16 routes per pass).
-template <bool kGateUp, int kSplit>
+// reduction (kSplit = 4, 2 or 1 for up to 4, 8 or 16 routes per pass); with
+// kPair (down projection, rows % 32 == 0) a wave's sub-tile is 32 rows.
+template <bool kGateUp, int kSplit, bool kPair>
 __global__ void stream_kernel(StreamArgs A);
 constexpr int kStreamRing = 4;   // steps (4 MX blocks per lane) in flight per wave
 constexpr int kStreamMaxItems = 32;  // items per workgroup (their entries live in LDS)
 __global__ void combine_kernel(CombineArgs A);
 // In-place row layout <-> tiled layout, one workgroup per 16-row group.
 __global__ void tile_kernel(uint8_t* packed, int64_t groups, int blocks, int inverse);
+// MXFP4 encoder, four lanes per 32-value block (bf16 or fp32 input); each
+// thread takes kEncodePer lane slots one grid width apart.
+constexpr int kEncodePer = 4;
+template <bool kBf16>
+__global__ void encode_kernel(const void* in, int64_t n_blocks, int quark, uint8_t* packed, uint8_t* scales);
 __global__ void dequant_kernel(const uint8_t* packed, const uint8_t* scales, int64_t n_blocks, int out_bf16,
                                void* out);
 

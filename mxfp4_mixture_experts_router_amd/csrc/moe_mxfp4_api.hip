@@ -66,6 +66,8 @@ int check_desc(const moe_mxfp4_desc* d) {
   if (d->scoring != MOE_SCORING_SOFTMAX && d->scoring != MOE_SCORING_SIGMOID) return MOE_ERR_MODE;
   if (d->activation != MOE_ACT_SILU_MUL && d->activation != MOE_ACT_SWIGLU_OAI) return MOE_ERR_MODE;
   if (d->weight_layout != MOE_LAYOUT_ROWS && d->weight_layout != MOE_LAYOUT_TILE16) return MOE_ERR_MODE;
+  if (d->down_pairing != MOE_PAIRING_AUTO && d->down_pairing != MOE_PAIRING_ON && d->down_pairing != MOE_PAIRING_OFF)
+    return MOE_ERR_MODE;
   return MOE_OK;
 }
 
@@ -248,31 +250,62 @@ void enqueue_expert_pair(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs 
   }
 }
 
-// One projection in the decode regime.  Items: n_passes x tiles of 64/split
-// rows, where an expert with Te routes has ceil(Te / tp) passes, so n_passes
+// One projection in the decode regime.  Items: n_passes x tiles of
+// 64/split rows (128/split for a paired down projection), where an expert
+// with Te routes has ceil(Te / tp) passes, so n_passes
 // <= (R + min(E_local, R) * (tp - 1)) / tp.  The persistent grid is the
 // resident workgroup count, raised if needed so that no workgroup has more
 // than kStreamMaxItems items, and never above the item bound.
-template <bool kGateUp, int kSplit>
-void launch_stream(const moe_mxfp4_desc& d, const moe::StreamArgs& S, hipStream_t s) {
-  const size_t lds = stream_lds_bytes(S.red, kGateUp, kSplit);
+struct StreamGrid {
+  size_t lds;
+  int64_t bound;  // items
+  int resident;
+};
+
+template <bool kGateUp, int kSplit, bool kPair>
+StreamGrid stream_grid(const moe_mxfp4_desc& d, const moe::StreamArgs& S) {
+  StreamGrid G;
+  G.lds = stream_lds_bytes(S.red, kGateUp || kPair, kSplit);
   const int64_t R = static_cast<int64_t>(d.T) * d.top_k;
   const int64_t tp = moe::kStreamPassTokens / kSplit;
   const int64_t passes = std::min<int64_t>(R, (R + tokens_bound(d) * (tp - 1)) / tp);
-  const int item_rows = 64 / kSplit;
-  const int64_t bound = passes * ((S.rows + item_rows - 1) / item_rows);
-  const int resident = resident_workgroups(moe::stream_kernel<kGateUp, kSplit>, lds);
-  int64_t grid = std::max<int64_t>(resident > 0 ? resident : 1024,
-                                   (bound + moe::kStreamMaxItems - 1) / moe::kStreamMaxItems);
-  grid = std::max<int64_t>(1, std::min<int64_t>(grid, bound));
-  hipLaunchKernelGGL((moe::stream_kernel<kGateUp, kSplit>), dim3(static_cast<unsigned>(grid)), dim3(256), lds, s, S);
+  const int item_rows = (kPair ? 128 : 64) / kSplit;
+  G.bound = passes * ((S.rows + item_rows - 1) / item_rows);
+  G.resident = resident_workgroups(moe::stream_kernel<kGateUp, kSplit, kPair>, G.lds);
+  return G;
+}
+
+template <bool kGateUp, int kSplit, bool kPair>
+void launch_stream(const StreamGrid& G, const moe::StreamArgs& S, hipStream_t s) {
+  int64_t grid = std::max<int64_t>(G.resident > 0 ? G.resident : 1024,
+                                   (G.bound + moe::kStreamMaxItems - 1) / moe::kStreamMaxItems);
+  grid = std::max<int64_t>(1, std::min<int64_t>(grid, G.bound));
+  hipLaunchKernelGGL((moe::stream_kernel<kGateUp, kSplit, kPair>), dim3(static_cast<unsigned>(grid)), dim3(256), G.lds,
+                     s, S);
+}
+
+// The down projection runs in pairs of 16-row sets per wave (two weight loads
+// per lane and step, like gate/up) when the rows allow it and, under
+// MOE_PAIRING_AUTO, the paired items still fill every resident workgroup
+// slot; otherwise (few touched experts) the unpaired items keep more of the
+// chip streaming.
+template <bool kGateUp, int kSplit>
+void launch_stream_proj(const moe_mxfp4_desc& d, const moe::StreamArgs& S, hipStream_t s) {
+  if (!kGateUp && S.rows % 32 == 0 && d.down_pairing != MOE_PAIRING_OFF) {
+    const StreamGrid G = stream_grid<false, kSplit, true>(d, S);
+    if (d.down_pairing == MOE_PAIRING_ON || G.bound >= G.resident) {
+      launch_stream<false, kSplit, true>(G, S, s);
+      return;
+    }
+  }
+  launch_stream<kGateUp, kSplit, false>(stream_grid<kGateUp, kSplit, false>(d, S), S, s);
 }
 
 template <bool kGateUp>
 void enqueue_stream(const moe_mxfp4_desc& d, int split, const moe::StreamArgs& S, hipStream_t s) {
-  if (split == 4) launch_stream<kGateUp, 4>(d, S, s);
-  else if (split == 2) launch_stream<kGateUp, 2>(d, S, s);
-  else launch_stream<kGateUp, 1>(d, S, s);
+  if (split == 4) launch_stream_proj<kGateUp, 4>(d, S, s);
+  else if (split == 2) launch_stream_proj<kGateUp, 2>(d, S, s);
+  else launch_stream_proj<kGateUp, 1>(d, S, s);
 }
 
 moe::StreamArgs stream_args(const moe_mxfp4_desc& d, const Layout& L, void* ws) {
@@ -487,6 +520,28 @@ int moe_mxfp4_dequant(const uint8_t* packed, const uint8_t* scales, int64_t rows
   hipLaunchKernelGGL(moe::dequant_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), packed, scales, n_blocks, out_dtype == MOE_DTYPE_BF16 ? 1 : 0,
                      out);
+  return launch_status();
+}
+
+int moe_mxfp4_encode(const void* in, int32_t in_dtype, int64_t rows, int64_t cols, int32_t rule, uint8_t* packed,
+                     uint8_t* scales, void* stream) {
+  if (rows < 0 || cols < 0 || cols % 32 != 0) return MOE_ERR_SHAPE;
+  if (in_dtype != MOE_DTYPE_F32 && in_dtype != MOE_DTYPE_BF16) return MOE_ERR_MODE;
+  if (rule != MOE_ENCODE_OCP && rule != MOE_ENCODE_QUARK) return MOE_ERR_MODE;
+  const int64_t n_blocks = rows * (cols / 32);
+  if (n_blocks == 0) return MOE_OK;
+  if (!in || !packed || !scales) return MOE_ERR_NULL;
+  if (!aligned16(in) || !aligned16(packed)) return MOE_ERR_ALIGN;
+  const int64_t grid = (n_blocks * 4 + 256 * moe::kEncodePer - 1) / (256 * moe::kEncodePer);
+  if (grid > 0x7FFFFFFF) return MOE_ERR_SHAPE;
+  const int quark = rule == MOE_ENCODE_QUARK ? 1 : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (in_dtype == MOE_DTYPE_BF16)
+    hipLaunchKernelGGL(moe::encode_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, in, n_blocks, quark,
+                       packed, scales);
+  else
+    hipLaunchKernelGGL(moe::encode_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, in, n_blocks, quark,
+                       packed, scales);
   return launch_status();
 }
 

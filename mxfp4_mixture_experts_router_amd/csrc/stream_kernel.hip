@@ -13,7 +13,9 @@
 //    wave's step sequence runs across item boundaries, so the register ring
 //    of kStreamRing steps keeps loading the next item's weights while the
 //    current item finishes (no per-item ramp);
-//  * a wave owns a 16-row sub-tile and one of kSplit slices of the reduction;
+//  * a wave owns a 16-row sub-tile and one of kSplit slices of the reduction
+//    (down projection, kPair: two 16-row sets 16 rows apart, so that, like the
+//    gate/up rows, every step loads two weight blocks per lane);
 //    one step = 4 MX blocks per lane (lane (r, q) holds block q of row r), so
 //    a step is 4 v_mfma_f32_16x16x32_bf16 per row set, the 4 dwords of a
 //    lane's 16-byte block giving the k-slots of the 4 MFMAs (the activation
@@ -74,13 +76,15 @@ constexpr uint32_t kOob = 0x80000000u;  // buffer offset past every range: the l
 
 }  // namespace
 
-template <bool kGateUp, int kSplit>
+template <bool kGateUp, int kSplit, bool kPair>
 __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
+  static_assert(!(kGateUp && kPair), "pairing is for the down projection");
   constexpr int kR = kStreamRing;
   constexpr int kTp = 16 / kSplit;         // routes per pass
-  constexpr int kSub = 4 / kSplit;         // 16-row sub-tiles per item
-  constexpr int kItemRows = 16 * kSub;
-  constexpr int kNW = kGateUp ? 2 : 1;     // weight rows per output row
+  constexpr int kSub = 4 / kSplit;         // wave sub-tiles per item
+  constexpr int kWaveRows = kPair ? 32 : 16;  // output rows per wave
+  constexpr int kItemRows = kWaveRows * kSub;
+  constexpr int kNW = (kGateUp || kPair) ? 2 : 1;  // weight row sets per wave
   extern __shared__ __align__(16) unsigned char lds[];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -92,7 +96,11 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
   const int NC = (RB + 3) >> 2;            // steps per row
   const int NCp = (NC + kSplit - 1) / kSplit;  // steps per slice (host guarantees >= kR)
   const int tiles = rows / kItemRows + (rows % kItemRows != 0);
-  const int rows_e = kNW * rows;
+  const int rows_e = (kGateUp ? 2 : 1) * rows;
+  // second weight row set of a wave, in rows past the first: the up rows of
+  // gate/up, the next 16 output rows of a paired down wave (in both weight
+  // layouts row n + 16 sits 16 row lengths after row n)
+  const int set1 = kGateUp ? rows : 16;
   const uint32_t row_bytes = static_cast<uint32_t>(red >> 1);
   const uint32_t expert_bytes = static_cast<uint32_t>(rows_e) * row_bytes;
   const uint32_t bstride = block_stride(A.tiled);
@@ -153,9 +161,9 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
     const int tt = stt < l_nt ? stt : 0;
     const int xrow = A.tok_from_pass ? static_cast<int>(pe->rte[tt]) / A.top_k : l_p + tt;
     l_xoff = static_cast<uint32_t>(xrow) * static_cast<uint32_t>(red) * 2u;
-    // this wave's sub-tile: rows are a multiple of 16, so a sub-tile is all in
-    // or all out; an out sub-tile re-reads the expert's last 16 rows (results dropped)
-    const int row0w = min(l_row0 + st * 16, rows - 16);
+    // this wave's sub-tile: rows are a multiple of kWaveRows, so a sub-tile is
+    // all in or all out; an out sub-tile re-reads the expert's last rows (results dropped)
+    const int row0w = min(l_row0 + st * kWaveRows, rows - kWaveRows);
     l_wo = row_offset(row0w + r, row_bytes, A.tiled);
     wrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(A.wp) + static_cast<size_t>(l_e) * expert_bytes, 0,
                                             expert_bytes, 0x00020000);
@@ -165,8 +173,8 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
     for (int m = 0; m * 64 < RB; ++m) {
       if (m * 64 + lane < RB) lds_dma16(dst + m * 1024, s0 + (m * 64 + lane) * 16);
     }
-    if (kGateUp) {
-      const uint8_t* s1 = s0 + static_cast<size_t>(rows) * RB;
+    if (kNW == 2) {
+      const uint8_t* s1 = s0 + static_cast<size_t>(set1) * RB;
       for (int m = 0; m * 64 < RB; ++m) {
         if (m * 64 + lane < RB) lds_dma16(dst + strip_bytes + m * 1024, s1 + (m * 64 + lane) * 16);
       }
@@ -174,7 +182,7 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
     if (A.bias != nullptr && lane < 2) {
       const uint16_t* b0 = A.bias + static_cast<size_t>(l_e) * rows_e + row0w;
       lds_dma16(dst + kNW * strip_bytes, b0 + lane * 8);
-      if (kGateUp) lds_dma16(dst + kNW * strip_bytes + 32, b0 + rows + lane * 8);
+      if (kNW == 2) lds_dma16(dst + kNW * strip_bytes + 32, b0 + set1 + lane * 8);
     }
   };
 
@@ -187,8 +195,8 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
     const bool ok = li < n_my && b < RB;
     const uint32_t o0 = ok ? l_wo + bstride * b : kOob;
     rw0[slot] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(wrs, o0, 0, 0));
-    if (kGateUp) {
-      const uint32_t o1 = ok ? l_wo + static_cast<uint32_t>(rows) * row_bytes + bstride * b : kOob;
+    if (kNW == 2) {
+      const uint32_t o1 = ok ? l_wo + static_cast<uint32_t>(set1) * row_bytes + bstride * b : kOob;
       rw1[slot] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(wrs, o1, 0, 0));
     }
     // activation piece of the staging thread
@@ -237,14 +245,14 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
     const bool valid = b < RB;
     const int bs = valid ? b : 0;
     const float sc0 = valid ? e8m0_to_f32(strip[r * RB + bs]) : 0.0f;
-    const float sc1 = (kGateUp && valid) ? e8m0_to_f32(strip[strip_bytes + r * RB + bs]) : 0.0f;
+    const float sc1 = (kNW == 2 && valid) ? e8m0_to_f32(strip[strip_bytes + r * RB + bs]) : 0.0f;
     const unsigned char* xb = xbuf + (g & 1) * kXBufBytes + bts * kXRowBytes + q * 64;
     const uint32_t d0[4] = {rw0[s].x, rw0[s].y, rw0[s].z, rw0[s].w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const bf16x8 bx = *reinterpret_cast<const bf16x8*>(xb + k * 16);
       acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8(d0[k], sc0), bx, acc0, 0, 0, 0);
-      if (kGateUp) {
+      if (kNW == 2) {
         const uint32_t d1 = k == 0 ? rw1[s].x : k == 1 ? rw1[s].y : k == 2 ? rw1[s].z : rw1[s].w;
         acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode8(d1, sc1), bx, acc1, 0, 0, 0);
       }
@@ -265,13 +273,13 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           b0[i] = bf16_bits_to_f32(bb[4 * q + i]);
-          if (kGateUp) b1[i] = bf16_bits_to_f32(bb[16 + 4 * q + i]);
+          if (kNW == 2) b1[i] = bf16_bits_to_f32(bb[16 + 4 * q + i]);
         }
       }
       if (kSplit > 1) {
         float* my = redbuf + (wave * 64 + lane) * 8;
         *reinterpret_cast<f32x4*>(my) = acc0;
-        if (kGateUp) *reinterpret_cast<f32x4*>(my + 4) = acc1;
+        if (kNW == 2) *reinterpret_cast<f32x4*>(my + 4) = acc1;
       }
     }
     // refill this slot with step g + kR, stage step g + 1
@@ -286,11 +294,11 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
         for (int j = 1; j < kSplit; ++j) {
           const float* o = redbuf + ((wave + j) * 64 + lane) * 8;
           acc0 += *reinterpret_cast<const f32x4*>(o);
-          if (kGateUp) acc1 += *reinterpret_cast<const f32x4*>(o + 4);
+          if (kNW == 2) acc1 += *reinterpret_cast<const f32x4*>(o + 4);
         }
       }
       // lane holds rows row0w + 4q + i (i < 4) of route r of the pass
-      const int row0w = c_row0 + st * 16;
+      const int row0w = c_row0 + st * kWaveRows;
       if (kp == 0 && row0w < rows && r < c_nt && r < kTp) {
         const int rl = 4 * q;
         const size_t p = static_cast<size_t>(c_p + r);
@@ -307,6 +315,9 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
           const size_t orow = A.o_by_route ? static_cast<size_t>(etab[ci].rte[r]) : p;
           *reinterpret_cast<float4*>(A.o_out + orow * rows + row0w + rl) =
               make_float4(acc0[0] + b0[0], acc0[1] + b0[1], acc0[2] + b0[2], acc0[3] + b0[3]);
+          if (kPair)
+            *reinterpret_cast<float4*>(A.o_out + orow * rows + row0w + 16 + rl) =
+                make_float4(acc1[0] + b1[0], acc1[1] + b1[1], acc1[2] + b1[2], acc1[3] + b1[3]);
         }
       }
       acc0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -333,11 +344,14 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
     if (g0 + s < total) step(g0 + s, s);
 }
 
-template __global__ void stream_kernel<true, 1>(StreamArgs);
-template __global__ void stream_kernel<true, 2>(StreamArgs);
-template __global__ void stream_kernel<true, 4>(StreamArgs);
-template __global__ void stream_kernel<false, 1>(StreamArgs);
-template __global__ void stream_kernel<false, 2>(StreamArgs);
-template __global__ void stream_kernel<false, 4>(StreamArgs);
+template __global__ void stream_kernel<true, 1, false>(StreamArgs);
+template __global__ void stream_kernel<true, 2, false>(StreamArgs);
+template __global__ void stream_kernel<true, 4, false>(StreamArgs);
+template __global__ void stream_kernel<false, 1, false>(StreamArgs);
+template __global__ void stream_kernel<false, 2, false>(StreamArgs);
+template __global__ void stream_kernel<false, 4, false>(StreamArgs);
+template __global__ void stream_kernel<false, 1, true>(StreamArgs);
+template __global__ void stream_kernel<false, 2, true>(StreamArgs);
+template __global__ void stream_kernel<false, 4, true>(StreamArgs);
 
 }  // namespace moe

@@ -43,7 +43,7 @@ def test_version_and_status_strings():
 
 def _desc(**kw):
     d = dict(T=4, K=256, I=256, E_global=8, E_local=8, expert_offset=0, top_k=2, scoring=0,
-             activation=0, swiglu_alpha=1.702, swiglu_limit=7.0, weight_layout=0)
+             activation=0, swiglu_alpha=1.702, swiglu_limit=7.0, weight_layout=0, down_pairing=0)
     d.update(kw)
     return _lib.MoeDesc(**d)
 
@@ -131,6 +131,20 @@ def test_tile_weights_error_paths():
     assert L.moe_mxfp4_tile_weights(A_MIS, 32, 64, 0, None) == E.MOE_ERR_ALIGN
     assert L.moe_mxfp4_tile_weights(None, 0, 64, 0, None) == E.MOE_OK           # nothing to do
     assert _decode(_desc(weight_layout=2)) == E.MOE_ERR_MODE
+    assert _decode(_desc(down_pairing=3)) == E.MOE_ERR_MODE
+    assert _decode(_desc(down_pairing=-1)) == E.MOE_ERR_MODE
+
+
+def test_encode_error_paths():
+    L, E = _lib.lib(), _lib
+    assert L.moe_mxfp4_encode(A, 0, 4, 48, 0, A, A, None) == E.MOE_ERR_SHAPE      # cols not a multiple of 32
+    assert L.moe_mxfp4_encode(A, 2, 4, 64, 0, A, A, None) == E.MOE_ERR_MODE       # dtype
+    assert L.moe_mxfp4_encode(A, 0, 4, 64, 2, A, A, None) == E.MOE_ERR_MODE       # rule
+    assert L.moe_mxfp4_encode(None, 0, 4, 64, 0, A, A, None) == E.MOE_ERR_NULL
+    assert L.moe_mxfp4_encode(A, 0, 4, 64, 0, A, None, None) == E.MOE_ERR_NULL
+    assert L.moe_mxfp4_encode(A_MIS, 1, 4, 64, 1, A, A, None) == E.MOE_ERR_ALIGN
+    assert L.moe_mxfp4_encode(A, 1, 4, 64, 1, A_MIS, A, None) == E.MOE_ERR_ALIGN
+    assert L.moe_mxfp4_encode(None, 0, 0, 64, 0, None, None, None) == E.MOE_OK    # nothing to do
 
 
 def test_hook_error_paths():

@@ -106,6 +106,72 @@ def test_tile_weights_matches_oracle_and_inverts(shape):
 
 
 # --------------------------------------------------------------------------
+# MXFP4 encoder: bit-exact against the oracle under both rules
+# --------------------------------------------------------------------------
+
+def _encode_on_device(v, rule, bf16):
+    t = torch()
+    rows, cols = v.shape
+    if bf16:
+        bits = (np.ascontiguousarray(v, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        x = dev_bf16(bits)
+        v = (bits.astype(np.uint32) << 16).view(np.float32)   # the values the device sees
+    else:
+        x = dev_f32(v)
+    packed = t.empty((rows, cols // 2), dtype=t.uint8, device="cuda")
+    scales = t.empty((rows, cols // 32), dtype=t.uint8, device="cuda")
+    moe.moe_mxfp4_encode(x, packed, scales, rule=rule)
+    t.cuda.synchronize()
+    return v, packed, scales
+
+
+@pytest.mark.parametrize("rule", ["ocp", "quark"])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_encode_bit_exact(rule, bf16):
+    rng = np.random.default_rng(31 + bf16)
+    rows, cols = 300, 2880
+    mag = np.exp2(rng.integers(-115, 115, size=(rows, 1))).astype(np.float32)       # 1e-35 .. 1e35 per row
+    v = (rng.standard_normal((rows, cols)) * mag).astype(np.float32)
+    v[0, :64] = 0.0                                                                # an all-zero block (and -0)
+    v[0, 40] = -0.0
+    v[1, :32] = np.float32(1e-40) * np.arange(32)                                  # subnormal block
+    v[2, :8] = [7.0, -3.2, 0.26, 0.25, 0.75, -1.25, 2.5, 5.0]                       # the golden block
+    v, packed, scales = _encode_on_device(v, rule, bf16)
+    p_ref, s_ref = oracle.encode_mxfp4(v, rule)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(packed.cpu().numpy(), p_ref)
+    # and the device dequantises them back to the oracle's values
+    out = torch().empty((rows, cols), dtype=torch().float32, device="cuda")
+    moe.moe_mxfp4_dequant(packed, scales, out)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), oracle.dequantize(p_ref, s_ref).view(np.uint32))
+
+
+def test_encode_then_layer_matches_oracle():
+    # weights quantised on the device from Gaussian values, then one layer call
+    t = torch()
+    cfg = _cfg(K=1024, I=512, E_global=4, E_local=4, top_k=2)
+    rng = np.random.default_rng(33)
+    w13 = (rng.standard_normal((4, 2 * 512, 1024)) * 0.05).astype(np.float32)
+    w2 = (rng.standard_normal((4, 1024, 512)) * 0.05).astype(np.float32)
+    d13p = t.empty((4, 1024, 512), dtype=t.uint8, device="cuda")
+    d13s = t.empty((4, 1024, 32), dtype=t.uint8, device="cuda")
+    d2p = t.empty((4, 1024, 256), dtype=t.uint8, device="cuda")
+    d2s = t.empty((4, 1024, 16), dtype=t.uint8, device="cuda")
+    moe.moe_mxfp4_encode(dev_f32(w13), d13p, d13s)
+    moe.moe_mxfp4_encode(dev_f32(w2), d2p, d2s)
+    t.cuda.synchronize()
+    p13, s13 = oracle.encode_mxfp4(w13)
+    p2, s2 = oracle.encode_mxfp4(w2)
+    assert np.array_equal(d13p.cpu().numpy(), p13) and np.array_equal(d13s.cpu().numpy(), s13)
+    assert np.array_equal(d2p.cpu().numpy(), p2) and np.array_equal(d2s.cpu().numpy(), s2)
+    w = make_weights(cfg)
+    w.w13_packed, w.w13_scales, w.w2_packed, w.w2_scales = p13, s13, p2, s2
+    inp = make_inputs(cfg, 6, t_index=1)
+    ref = oracle.moe_forward_cfg(cfg, w, inp)
+    _assert_close(bf16_to_np(run_decode(cfg, DeviceLayer(w), inp)), ref["y"], "encoded weights")
+
+
+# --------------------------------------------------------------------------
 # routing and bucketing: bit-exact ids and permutation
 # --------------------------------------------------------------------------
 
@@ -319,6 +385,33 @@ def test_layer_tiled_weights_bit_identical_to_rows(case):
     if case == 0:
         ref = oracle.moe_forward_cfg(cfg, w, inp)
         _assert_close(bf16_to_np(run_decode(cfg, DeviceLayer(w, layout="tile16"), inp)), ref["y"], "tiled")
+
+
+# paired down rows (two 16-row sets per wave) against unpaired: same MFMA
+# sequence and reduction order per output row, so bit-identical
+PAIRING_CASES = [
+    ("split4", dict(K=2080, I=2048, E_global=8, E_local=6, expert_offset=1, top_k=2, activation="swiglu_oai",
+                    bias=True, scale_lo=115, scale_hi=127), 2, "rows"),
+    ("split4-tiled", dict(K=2080, I=2048, E_global=8, E_local=6, expert_offset=1, top_k=2, activation="swiglu_oai",
+                          bias=True, scale_lo=115, scale_hi=127), 3, "tile16"),
+    ("split2", dict(K=1120, I=1056, E_global=4, E_local=4, top_k=2, bias=True), 7, "tile16"),
+    ("split1", dict(K=544, I=608, E_global=4, E_local=4, top_k=2), 20, "rows"),
+    ("split1-multipass", dict(K=640, I=512, E_global=2, E_local=2, top_k=2, bias=True), 40, "tile16"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PAIRING_CASES)))
+def test_down_pairing_bit_identical_and_matches_oracle(case):
+    name, kw, T, layout = PAIRING_CASES[case]
+    cfg = _cfg(**kw)
+    w = make_weights(cfg)
+    inp = make_inputs(cfg, T, t_index=case)
+    layer = DeviceLayer(w, layout=layout)
+    off = bf16_bits_np(run_decode(cfg, layer, inp, down_pairing="off"))
+    on = bf16_bits_np(run_decode(cfg, layer, inp, down_pairing="on"))
+    assert np.array_equal(off, on), name
+    ref = oracle.moe_forward_cfg(cfg, w, inp)
+    _assert_close(bf16_to_np(run_decode(cfg, layer, inp, down_pairing="on")), ref["y"], name)
 
 
 def test_layer_ids_mode_with_padding_and_foreign_ids():
