@@ -65,8 +65,12 @@ def topk_by_argmax(row, k):
 def moe_bruteforce(*, x_bits, w13_packed, w13_scales, w2_packed, w2_scales, K, I,
                    E_global, E_local, top_k, expert_offset=0, scoring="softmax",
                    activation_kind="silu_mul", swiglu_alpha=1.702, swiglu_limit=7.0,
-                   logits=None, topk_ids=None, topk_weights=None, b13=None, b2=None):
+                   logits=None, topk_ids=None, topk_weights=None, b13=None, b2=None,
+                   w13_order="gate_up", per_route=False):
+    """y [T][K] as nested lists; with per_route, also the per-route rows
+    {t * top_k + j: [K]} (a W2^T + b2 of each local route, no routing weight)."""
     T = len(x_bits)
+    rows = {}
     x = [[bf16_value(x_bits[t][c]) for c in range(K)] for t in range(T)]
     y = [[0.0] * K for _ in range(T)]
     for t in range(T):
@@ -96,7 +100,10 @@ def moe_bruteforce(*, x_bits, w13_packed, w13_scales, w2_packed, w2_scales, K, I
                 h.append(acc)
             a = []
             for n in range(I):
-                g, u = h[n], h[I + n]
+                if w13_order == "gate_up":
+                    g, u = h[n], h[I + n]
+                else:                       # interleaved: gate row n is row 2n, up row n is row 2n + 1
+                    g, u = h[2 * n], h[2 * n + 1]
                 if activation_kind == "silu_mul":
                     a.append(g * _sigmoid(g) * u)
                 else:
@@ -110,4 +117,5 @@ def moe_bruteforce(*, x_bits, w13_packed, w13_scales, w2_packed, w2_scales, K, I
                 if b2 is not None:
                     acc += bf16_value(b2[e][kk])
                 y[t][kk] += w[j] * acc
-    return y
+                rows.setdefault(t * top_k + j, [0.0] * K)[kk] = acc
+    return (y, rows) if per_route else y

@@ -53,6 +53,20 @@ saturating at 6); the sign bit is the input's sign bit (a negative value that
 rounds to zero gives code 8, -0); amax = 0 gives exponent -127 (scale byte 0);
 the exponent is clipped to [-127, 127], so scale byte 255 (NaN) never occurs.
 
+Gate/up row order (``w13_order``): "MXFP4 MoE decode kernels", Beyond
+gpt-oss, lists a w13 kernel for interleaved gate/up rows next to the
+[gate; up] one, and Design, Read the served layout, describes gpt-oss's
+served w13 as interleaved (the GLM page's item 1 says gpt-oss's own loader
+undoes that).  Reading: interleaved means row 2n is gate row n and row 2n + 1
+is up row n, with b13 and the scale rows in the same order; the activation is
+chosen independently of the order.
+
+Per-route output (``route_outputs``): the same page's Beyond gpt-oss lists a
+down kernel that writes one output row per route for models that apply a
+per-route operation before the token sum.  Reading: row r = t*k + j holds
+a W2^T (+ b2) in fp32 for a local route, without the routing weight, and
+zeros for a route outside the local slice.
+
 The tiled weight layout (``tile16``) is this library's own storage order, not
 the pages': the pages' kernels read the served row layout and name a repack
 as the next step they chose not to take, to keep one copy of the experts.
@@ -81,6 +95,8 @@ SOFTMAX = "softmax"
 SIGMOID = "sigmoid"
 SILU_MUL = "silu_mul"
 SWIGLU_OAI = "swiglu_oai"
+GATE_UP = "gate_up"           # w13 rows [gate; up]
+INTERLEAVED = "interleaved"   # w13 row 2n gate n, row 2n + 1 up n
 
 
 # --------------------------------------------------------------------------
@@ -320,7 +336,7 @@ def moe_forward(*, x_bits, w13_packed, w13_scales, w2_packed, w2_scales, K, I,
                 E_global, E_local, top_k, expert_offset=0, scoring=SOFTMAX,
                 activation_kind=SILU_MUL, swiglu_alpha=1.702, swiglu_limit=7.0,
                 logits=None, topk_ids=None, topk_weights=None, b13=None, b2=None,
-                dtype=np.float32, round_intermediate=True, experts_cache=None):
+                dtype=np.float32, round_intermediate=True, experts_cache=None, w13_order=GATE_UP):
     """One MoE layer call on an expert-parallel slice.
 
     Inputs are the raw arrays: x as bf16 bits [T, K]; either router logits
@@ -329,9 +345,11 @@ def moe_forward(*, x_bits, w13_packed, w13_scales, w2_packed, w2_scales, K, I,
 
     Steps: (1) x to fp32; (2) route (or take the given ids and weights);
     (3) bucket the local routes; (4) per local expert with routes: dequantise
-    w13, H = X_e W13^T (+ b13), activation on [gate; up] halves, round to
-    bf16; dequantise w2, O = A_e W2^T (+ b2); (5) y[t] = sum over token t's
-    local routes j (ascending j) of w[t, j] * O[route].
+    w13, H = X_e W13^T (+ b13), activation on the gate and up columns
+    ([gate; up] halves, or even and odd columns for ``w13_order``
+    "interleaved"), round to bf16; dequantise w2, O = A_e W2^T (+ b2);
+    (5) y[t] = sum over token t's local routes j (ascending j) of
+    w[t, j] * O[route].
 
     Returns a dict with y [T, K] and every intermediate: ids, weights, counts,
     offsets, routes, h [R_local, 2I] and a [R_local, I] in route order, o
@@ -343,6 +361,8 @@ def moe_forward(*, x_bits, w13_packed, w13_scales, w2_packed, w2_scales, K, I,
         raise ValueError("bad shapes")
     if expert_offset < 0 or expert_offset + E_local > E_global:
         raise ValueError("local slice outside the global experts")
+    if w13_order not in (GATE_UP, INTERLEAVED):
+        raise ValueError(w13_order)
     x = bf16_bits_to_float(x_bits).astype(dtype)
     if not np.all(np.isfinite(x)):
         raise ValueError("activations must be finite")
@@ -379,7 +399,11 @@ def moe_forward(*, x_bits, w13_packed, w13_scales, w2_packed, w2_scales, K, I,
             h = x[tokens] @ w13.T
             if b13 is not None:
                 h = h + bf16_bits_to_float(b13[e]).astype(dtype)
-            act = activation(h[:, :I], h[:, I:], activation_kind, swiglu_alpha, swiglu_limit)
+            if w13_order == GATE_UP:
+                gate, up = h[:, :I], h[:, I:]
+            else:
+                gate, up = h[:, 0::2], h[:, 1::2]
+            act = activation(gate, up, activation_kind, swiglu_alpha, swiglu_limit)
             a = round_to_bf16(act) if round_intermediate else act
             o = a @ w2.T
             if b2 is not None:
@@ -400,6 +424,16 @@ def moe_forward(*, x_bits, w13_packed, w13_scales, w2_packed, w2_scales, K, I,
 
     return {"y": y, "ids": ids, "weights": weights, "counts": counts, "offsets": offsets,
             "routes": routes, "h": h_all, "a": a_all, "o": o_all}
+
+
+def route_outputs(result: dict, T: int, top_k: int) -> np.ndarray:
+    """Per-route down-projection rows [T * top_k, K] from a ``moe_forward``
+    result: row r = t * top_k + j is O of route r (a W2^T + b2, no routing
+    weight) when the route is local, else zeros."""
+    o = result["o"]
+    out = np.zeros((T * top_k, o.shape[1]), dtype=o.dtype)
+    out[result["routes"]] = o
+    return out
 
 
 def moe_forward_cfg(cfg, weights, inputs, **kw):

@@ -260,6 +260,97 @@ def test_gate_up_negative_controls(cfg_name):
 
 
 # --------------------------------------------------------------------------
+# interleaved gate/up rows and the per-route output
+# --------------------------------------------------------------------------
+
+def interleave_rows(a, I):
+    """[E, 2I, ...] rows [gate; up] -> rows gate 0, up 0, gate 1, up 1, ..."""
+    out = np.empty_like(a)
+    out[:, 0::2] = a[:, :I]
+    out[:, 1::2] = a[:, I:]
+    return out
+
+
+INTERLEAVED_CASES = [
+    dict(),
+    dict(activation="swiglu_oai", bias=True, scale_lo=118, scale_hi=124),
+    dict(K=96, I=32, E_global=8, E_local=3, expert_offset=2, top_k=4, scoring="sigmoid", bias=True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(INTERLEAVED_CASES)))
+def test_interleaved_order_matches_bruteforce_and_gate_up(case):
+    cfg = _cfg(**INTERLEAVED_CASES[case])
+    w = make_weights(cfg)
+    inp = make_inputs(cfg, 3, x_scale=1.0)
+    I = cfg.I
+    p, sc = interleave_rows(w.w13_packed, I), interleave_rows(w.w13_scales, I)
+    b13 = None if w.b13 is None else interleave_rows(w.b13, I)
+    want = np.array(bf.moe_bruteforce(
+        x_bits=inp.x, logits=inp.logits, w13_packed=p, w13_scales=sc, w2_packed=w.w2_packed,
+        w2_scales=w.w2_scales, b13=b13, b2=w.b2, K=cfg.K, I=I, E_global=cfg.E_global,
+        E_local=w.w13_packed.shape[0], top_k=cfg.top_k, expert_offset=cfg.expert_offset,
+        scoring=cfg.scoring, activation_kind=cfg.activation, w13_order="interleaved"), dtype=np.float64)
+    kw = dict(x_bits=inp.x, logits=inp.logits, w2_packed=w.w2_packed, w2_scales=w.w2_scales, b2=w.b2,
+              K=cfg.K, I=I, E_global=cfg.E_global, E_local=w.w13_packed.shape[0], top_k=cfg.top_k,
+              expert_offset=cfg.expert_offset, scoring=cfg.scoring, activation_kind=cfg.activation,
+              dtype=np.float64, round_intermediate=False)
+    got = oracle.moe_forward(w13_packed=p, w13_scales=sc, b13=b13, w13_order="interleaved", **kw)["y"]
+    assert oracle.rel_l2(got, want) <= 1e-12
+    same = oracle.moe_forward(w13_packed=w.w13_packed, w13_scales=w.w13_scales, b13=w.b13, **kw)["y"]
+    assert oracle.rel_l2(got, same) <= 1e-12
+    # each order read as the other is far off
+    wrong = oracle.moe_forward(w13_packed=p, w13_scales=sc, b13=b13, **kw)["y"]
+    wrong2 = oracle.moe_forward(w13_packed=w.w13_packed, w13_scales=w.w13_scales, b13=w.b13,
+                                w13_order="interleaved", **kw)["y"]
+    assert oracle.rel_l2(wrong, want) > 0.05 and oracle.rel_l2(wrong2, want) > 0.05
+
+
+def test_exact_chain_interleaved_storage():
+    # the closed form does not depend on how the rows are stored
+    for c0 in (37, 70):
+        for with_bias in (False, True):
+            arrays, want = build_exact_chain(c0, with_bias)
+            I = arrays["I"]
+            arrays["w13_packed"] = interleave_rows(arrays["w13_packed"], I)
+            arrays["w13_scales"] = interleave_rows(arrays["w13_scales"], I)
+            if arrays["b13"] is not None:
+                arrays["b13"] = interleave_rows(arrays["b13"], I)
+            for dt in (np.float32, np.float64):
+                got = oracle.moe_forward(**arrays, dtype=dt, w13_order="interleaved")["y"]
+                assert np.array_equal(got.astype(np.float64), want), (c0, with_bias, dt)
+
+
+@pytest.mark.parametrize("case", [dict(), dict(K=96, I=32, E_global=8, E_local=3, expert_offset=2, top_k=4,
+                                               scoring="sigmoid", bias=True)])
+def test_route_outputs_match_bruteforce_and_sum_to_y(case):
+    cfg = _cfg(**case)
+    w = make_weights(cfg)
+    T = 3
+    inp = make_inputs(cfg, T, x_scale=1.0)
+    res = oracle.moe_forward_cfg(cfg, w, inp, dtype=np.float64, round_intermediate=False)
+    rows = oracle.route_outputs(res, T, cfg.top_k)
+    assert rows.shape == (T * cfg.top_k, cfg.K)
+    _, want = bf.moe_bruteforce(
+        x_bits=inp.x, logits=inp.logits, w13_packed=w.w13_packed, w13_scales=w.w13_scales,
+        w2_packed=w.w2_packed, w2_scales=w.w2_scales, b13=w.b13, b2=w.b2, K=cfg.K, I=cfg.I,
+        E_global=cfg.E_global, E_local=w.w13_packed.shape[0], top_k=cfg.top_k,
+        expert_offset=cfg.expert_offset, scoring=cfg.scoring, activation_kind=cfg.activation,
+        per_route=True)
+    local = np.zeros(T * cfg.top_k, bool)
+    for r, row in want.items():
+        local[r] = True
+        assert oracle.rel_l2(rows[r], np.array(row)) <= 1e-12, r
+    assert not rows[~local].any()                       # routes outside the slice: zero rows
+    if case:
+        assert (~local).any()                           # the slice case has some
+    # sum over j of w[t, j] * row(t, j) is the layer output
+    y = np.einsum("tj,tjk->tk", res["weights"].astype(np.float64),
+                  rows.reshape(T, cfg.top_k, cfg.K))
+    assert oracle.rel_l2(y, res["y"]) <= 1e-12
+
+
+# --------------------------------------------------------------------------
 # invariants
 # --------------------------------------------------------------------------
 
