@@ -62,6 +62,10 @@ def parse():
                    help="measure the MXFP4 encoder instead (bf16 weights of the layer's w13 -> packed + scales)")
     p.add_argument("--layout", default="tile16", choices=("rows", "tile16"),
                    help="packed weight storage order (tile16: tiled in place once, before any timing)")
+    p.add_argument("--w13-order", default="gate_up", choices=("gate_up", "interleaved"),
+                   help="row order of w13 (interleaved: gate and up rows alternate)")
+    p.add_argument("--per-route", action="store_true",
+                   help="per-route output: fp32 [T*top_k, K] rows instead of the bf16 token sums")
     return p.parse_args()
 
 
@@ -152,18 +156,25 @@ def main():
     for T in tokens:
         d = moe.make_desc(T=T, K=K, I=I, E_global=cfg.E_global, E_local=cfg.E_local, top_k=cfg.top_k,
                           expert_offset=cfg.expert_offset, scoring=cfg.scoring, activation=cfg.activation,
-                          swiglu_alpha=cfg.swiglu_alpha, swiglu_limit=cfg.swiglu_limit, weight_layout=args.layout)
+                          swiglu_alpha=cfg.swiglu_alpha, swiglu_limit=cfg.swiglu_limit, weight_layout=args.layout,
+                          w13_order=args.w13_order)
         ws_bytes = moe.moe_mxfp4_workspace_bytes(d)
         inputs = [make_inputs(cfg, T, call=i) for i in range(L)]
         xs = [torch.from_numpy(inp.x.view(np.int16)).cuda().view(torch.bfloat16) for inp in inputs]
         lg = [torch.from_numpy(inp.logits).cuda() for inp in inputs]
         wss = [torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") for _ in range(L)]
-        outs = [torch.empty((T, K), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+        if args.per_route:
+            outs = [torch.empty((T * cfg.top_k, K), dtype=torch.float32, device="cuda") for _ in range(L)]
+        else:
+            outs = [torch.empty((T, K), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+        out_bytes = outs[0].numel() * outs[0].element_size()
+        decode_fn = moe.moe_mxfp4_decode_routes if args.per_route else moe.moe_mxfp4_decode
+        down_fn = moe.moe_mxfp4_down_routes if args.per_route else moe.moe_mxfp4_down
 
         def call_decode(i, s):
             r = reps[i % L]
-            moe.moe_mxfp4_decode(d, xs[i % L], r.w13p, r.w13s, r.w2p, r.w2s, outs[i % L], router_logits=lg[i % L],
-                                 w13_bias=r.b13, w2_bias=r.b2, workspace=wss[i % L], stream=s)
+            decode_fn(d, xs[i % L], r.w13p, r.w13s, r.w2p, r.w2s, outs[i % L], router_logits=lg[i % L],
+                      w13_bias=r.b13, w2_bias=r.b2, workspace=wss[i % L], stream=s)
 
         def call_plan(i, s):
             moe.moe_mxfp4_plan(d, router_logits=lg[i % L], workspace=wss[i % L], stream=s)
@@ -174,7 +185,7 @@ def main():
 
         def call_down(i, s):
             r = reps[i % L]
-            moe.moe_mxfp4_down(d, r.w2p, r.w2s, outs[i % L], wss[i % L], w2_bias=r.b2, stream=s)
+            down_fn(d, r.w2p, r.w2s, outs[i % L], wss[i % L], w2_bias=r.b2, stream=s)
 
         with torch.cuda.stream(stream):
             for i in range(L):
@@ -209,7 +220,7 @@ def main():
             timing[name] = e0.elapsed_time(e1) * 1000.0 / args.steps   # us per call
         # bytes per call, averaged over the calls of the chain (call i uses replica i % L)
         calls = [i % L for i in range(args.steps)]
-        bytes_call = np.mean([touched[c] * per_expert + 4 * T * K + 4 * T * cfg.E_global for c in calls])
+        bytes_call = np.mean([touched[c] * per_expert + 2 * T * K + out_bytes + 4 * T * cfg.E_global for c in calls])
         w13_bytes = np.mean([touched[c] * w13_per_expert + 2 * T * K + 2 * routes[c] * I for c in calls])
         us = timing["decode"]
         results[T] = dict(
@@ -250,17 +261,20 @@ def main():
         "data": "synthetic (seeded random E2M1 codes, E8M0 scales, Gaussian x and logits)",
         "config": {"workload": f"{cfg.description}; one call at each T in {tokens} per step",
                    "K": K, "I": I, "E_global": cfg.E_global, "E_local": cfg.E_local, "top_k": cfg.top_k,
-                   "tokens": tokens, "replicas": L, "weight_layout": args.layout, "parallelism": "single GPU"},
+                   "tokens": tokens, "replicas": L, "weight_layout": args.layout, "w13_order": args.w13_order,
+                   "output": "per-route fp32 rows" if args.per_route else "token sums bf16",
+                   "parallelism": "single GPU"},
         "pct_peak": round(100 * value / HBM_PEAK_GBS, 1),
         "per_T": {str(k): v for k, v in results.items()},
         "roofline": {"kernel": "gate/up projection: moe::stream_kernel<true,*> (one launch per call)",
                      "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(cfg, tokens, args.layout), "avg_launch_us": round(w13_avg_us, 2),
+                     "traffic": measured_traffic(cfg, tokens, args.layout, args.w13_order),
+                     "avg_launch_us": round(w13_avg_us, 2),
                      "algorithmic_bytes_per_launch": int(w13_avg_bytes)},
         "device": torch.cuda.get_device_name(0),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.per_route and args.w13_order == "gate_up":
         line["cpu_baseline"] = cpu_baseline(cfg, w0, reps[0], torch, moe, args.layout)
     print(json.dumps(line), flush=True)
 
@@ -296,7 +310,7 @@ def encode_bench(torch, moe, cfg, args):
                          "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
-def measured_traffic(cfg, tokens, layout):
+def measured_traffic(cfg, tokens, layout, w13_order="gate_up"):
     """HBM bytes per gate/up launch (mean over T) from the committed counter runs
     (profiles/roofline_traffic.json), or None when they do not cover this
     workload or the kernel's sources have changed since they were taken."""
@@ -311,7 +325,8 @@ def measured_traffic(cfg, tokens, layout):
     if any(built.get(k) != v for k, v in prof.get("sources_sha256", {}).items()):
         return None
     per_t = prof.get("traffic_bytes_per_launch", {})
-    if cfg.name != "gptoss20b" or layout != "tile16" or any(str(t) not in per_t for t in tokens):
+    if (cfg.name != "gptoss20b" or layout != "tile16" or w13_order != "gate_up"
+            or any(str(t) not in per_t for t in tokens)):
         return None
     return int(np.mean([per_t[str(t)] for t in tokens]))
 

@@ -80,6 +80,14 @@ extern "C" {
  * loads two weight blocks per lane, as the gate/up projection does; it needs
  * K % 32 == 0.  AUTO pairs when the paired work items still fill every
  * resident workgroup slot of the GPU.                                        */
+/* Row order of w13_packed, w13_scales and w13_bias ("MXFP4 MoE decode
+ * kernels", Beyond gpt-oss: kernels for [gate; up] rows and for interleaved
+ * gate/up rows).  GATE_UP: row n < I is gate row n, row I + n is up row n.
+ * INTERLEAVED: row 2n is gate row n, row 2n + 1 is up row n.  The activation
+ * (desc.activation) is chosen independently of the order.                   */
+#define MOE_W13_GATE_UP      0
+#define MOE_W13_INTERLEAVED  1
+
 #define MOE_PAIRING_AUTO   0
 #define MOE_PAIRING_ON     1    /* whenever K % 32 == 0                               */
 #define MOE_PAIRING_OFF    2
@@ -100,6 +108,7 @@ typedef struct moe_mxfp4_desc {
     float   swiglu_limit;   /* 7.0 for gpt-oss    (MOE_ACT_SWIGLU_OAI only)              */
     int32_t weight_layout;  /* MOE_LAYOUT_* of w13_packed and w2_packed                   */
     int32_t down_pairing;   /* MOE_PAIRING_* (0 = automatic)                              */
+    int32_t w13_order;      /* MOE_W13_* row order of the w13 tensors                      */
 } moe_mxfp4_desc;
 
 /*
@@ -124,9 +133,10 @@ int moe_mxfp4_workspace_bytes(const moe_mxfp4_desc* desc, size_t* bytes);
  *               must be given, else MOE_ERR_MODE.  Ids outside the local
  *               slice (including -1 padding) are skipped; a repeated id is a
  *               separate route.
- *  w13_packed   u8 [E_local, 2I, K/2]: row n < I is gate row n, row I+n is
- *               up row n; byte c of a row holds element 2c in its low nibble
- *               and element 2c+1 in its high nibble (E2M1 codes)
+ *  w13_packed   u8 [E_local, 2I, K/2]: rows in desc->w13_order (GATE_UP:
+ *               row n < I is gate row n, row I+n is up row n); byte c of a
+ *               row holds element 2c in its low nibble and element 2c+1 in
+ *               its high nibble (E2M1 codes)
  *  w13_scales   u8 [E_local, 2I, K/32]: E8M0 scale of elements 32b..32b+31
  *  w13_bias     bf16 [E_local, 2I], or NULL (added to the fp32 projection
  *               before the activation)
@@ -196,6 +206,33 @@ int moe_mxfp4_gate_up(const moe_mxfp4_desc* desc, const uint16_t* x,
 int moe_mxfp4_down(const moe_mxfp4_desc* desc, const uint16_t* a,
                    const uint8_t* w2_packed, const uint8_t* w2_scales, const uint16_t* w2_bias,
                    uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Per-route output ("MXFP4 MoE decode kernels", Beyond gpt-oss: a down kernel
+ * with one output row per route, for models that apply a per-route operation
+ * before the token sum).  Same arguments as moe_mxfp4_decode and
+ * moe_mxfp4_down, except the output:
+ *  out_routes   fp32 [T * top_k, K], fully overwritten: row r = t*top_k + j
+ *               holds W2 a_r + b2 of route r (no routing weight) when the
+ *               route's expert is in the local slice, else zeros.  The routing
+ *               weights of logits mode are in no output; moe_mxfp4_route
+ *               computes the same ones.
+ * moe_mxfp4_decode_routes runs plan, gate_up and the per-route down step;
+ * moe_mxfp4_down_routes is the last step alone, on a workspace that holds a
+ * plan (and, when a is NULL, the gate/up result).
+ */
+int moe_mxfp4_decode_routes(const moe_mxfp4_desc* desc,
+                            const uint16_t* x,
+                            const float* router_logits,
+                            const int32_t* topk_ids, const float* topk_weights,
+                            const uint8_t* w13_packed, const uint8_t* w13_scales, const uint16_t* w13_bias,
+                            const uint8_t* w2_packed, const uint8_t* w2_scales, const uint16_t* w2_bias,
+                            float* out_routes,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+int moe_mxfp4_down_routes(const moe_mxfp4_desc* desc, const uint16_t* a,
+                          const uint8_t* w2_packed, const uint8_t* w2_scales, const uint16_t* w2_bias,
+                          float* out_routes, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Routing step alone (test hook): router logits fp32 [T, E_global] ->

@@ -32,6 +32,8 @@ from ._lib import (  # noqa: F401
     MOE_PAIRING_AUTO,
     MOE_PAIRING_OFF,
     MOE_PAIRING_ON,
+    MOE_W13_GATE_UP,
+    MOE_W13_INTERLEAVED,
     MOE_OK,
     MOE_SCORING_SIGMOID,
     MOE_SCORING_SOFTMAX,
@@ -48,6 +50,7 @@ _SCORING = {"softmax": MOE_SCORING_SOFTMAX, "sigmoid": MOE_SCORING_SIGMOID}
 _ACT = {"silu_mul": MOE_ACT_SILU_MUL, "swiglu_oai": MOE_ACT_SWIGLU_OAI}
 _LAYOUT = {"rows": MOE_LAYOUT_ROWS, "tile16": MOE_LAYOUT_TILE16}
 _PAIRING = {"auto": MOE_PAIRING_AUTO, "on": MOE_PAIRING_ON, "off": MOE_PAIRING_OFF}
+_W13_ORDER = {"gate_up": MOE_W13_GATE_UP, "interleaved": MOE_W13_INTERLEAVED}
 
 
 class MoeError(RuntimeError):
@@ -58,12 +61,14 @@ class MoeError(RuntimeError):
 
 def make_desc(T: int, K: int, I: int, E_global: int, E_local: int, top_k: int, expert_offset: int = 0,
               scoring="softmax", activation="silu_mul", swiglu_alpha: float = 1.702,
-              swiglu_limit: float = 7.0, weight_layout="rows", down_pairing="auto") -> MoeDesc:
+              swiglu_limit: float = 7.0, weight_layout="rows", down_pairing="auto",
+              w13_order="gate_up") -> MoeDesc:
     sc = _SCORING[scoring] if isinstance(scoring, str) else int(scoring)
     ac = _ACT[activation] if isinstance(activation, str) else int(activation)
     wl = _LAYOUT[weight_layout] if isinstance(weight_layout, str) else int(weight_layout)
     dp = _PAIRING[down_pairing] if isinstance(down_pairing, str) else int(down_pairing)
-    return MoeDesc(T, K, I, E_global, E_local, expert_offset, top_k, sc, ac, swiglu_alpha, swiglu_limit, wl, dp)
+    wo = _W13_ORDER[w13_order] if isinstance(w13_order, str) else int(w13_order)
+    return MoeDesc(T, K, I, E_global, E_local, expert_offset, top_k, sc, ac, swiglu_alpha, swiglu_limit, wl, dp, wo)
 
 
 def moe_mxfp4_status_string(status: int) -> str:
@@ -205,6 +210,49 @@ def moe_mxfp4_down(desc: MoeDesc, w2_packed, w2_scales, out, workspace, a=None, 
         _ptr(w2_bias, torch.bfloat16, s2b, "w2_bias", True),
         _ptr(out, torch.bfloat16, (d.T, d.K), "out"),
         wsp, wsn, _stream(stream)), "moe_mxfp4_down")
+
+
+def moe_mxfp4_decode_routes(desc: MoeDesc, x, w13_packed, w13_scales, w2_packed, w2_scales, out_routes,
+                            router_logits=None, topk_ids=None, topk_weights=None, w13_bias=None, w2_bias=None,
+                            workspace=None, stream=None):
+    """One layer call with per-route output: ``out_routes`` fp32 [T*top_k, K] gets
+    W2 a_r + b2 of every local route r (no routing weight), zeros elsewhere."""
+    torch = _torch()
+    d = desc
+    s13p, s13s, s13b, s2p, s2s, s2b = _weights_shapes(d)
+    ws, wsp, wsn = _workspace(d, workspace, x.device)
+    _check(_lib.lib().moe_mxfp4_decode_routes(
+        ctypes.byref(d),
+        _ptr(x, torch.bfloat16, (d.T, d.K), "x"),
+        _ptr(router_logits, torch.float32, (d.T, d.E_global), "router_logits", True),
+        _ptr(topk_ids, torch.int32, (d.T, d.top_k), "topk_ids", True),
+        _ptr(topk_weights, torch.float32, (d.T, d.top_k), "topk_weights", True),
+        _ptr(w13_packed, torch.uint8, s13p, "w13_packed"),
+        _ptr(w13_scales, torch.uint8, s13s, "w13_scales"),
+        _ptr(w13_bias, torch.bfloat16, s13b, "w13_bias", True),
+        _ptr(w2_packed, torch.uint8, s2p, "w2_packed"),
+        _ptr(w2_scales, torch.uint8, s2s, "w2_scales"),
+        _ptr(w2_bias, torch.bfloat16, s2b, "w2_bias", True),
+        _ptr(out_routes, torch.float32, (d.T * d.top_k, d.K), "out_routes"),
+        wsp, wsn, _stream(stream)), "moe_mxfp4_decode_routes")
+    return ws
+
+
+def moe_mxfp4_down_routes(desc: MoeDesc, w2_packed, w2_scales, out_routes, workspace, a=None, w2_bias=None,
+                          stream=None):
+    """Per-route down step on the plan held in ``workspace``; ``a`` None reads the workspace copy."""
+    torch = _torch()
+    d = desc
+    _, _, _, s2p, s2s, s2b = _weights_shapes(d)
+    ws, wsp, wsn = _workspace(d, workspace, out_routes.device)
+    _check(_lib.lib().moe_mxfp4_down_routes(
+        ctypes.byref(d),
+        _ptr(a, torch.bfloat16, (d.T * d.top_k, d.I), "a", True),
+        _ptr(w2_packed, torch.uint8, s2p, "w2_packed"),
+        _ptr(w2_scales, torch.uint8, s2s, "w2_scales"),
+        _ptr(w2_bias, torch.bfloat16, s2b, "w2_bias", True),
+        _ptr(out_routes, torch.float32, (d.T * d.top_k, d.K), "out_routes"),
+        wsp, wsn, _stream(stream)), "moe_mxfp4_down_routes")
 
 
 def moe_mxfp4_route(desc: MoeDesc, router_logits, topk_ids, topk_weights, stream=None):

@@ -34,6 +34,8 @@ MOE_LAYOUT_TILE16 = 1
 MOE_PAIRING_AUTO = 0
 MOE_PAIRING_ON = 1
 MOE_PAIRING_OFF = 2
+MOE_W13_GATE_UP = 0
+MOE_W13_INTERLEAVED = 1
 
 EXPORTED = (
     "moe_mxfp4_workspace_bytes",
@@ -43,6 +45,8 @@ EXPORTED = (
     "moe_mxfp4_bucket",
     "moe_mxfp4_gate_up",
     "moe_mxfp4_down",
+    "moe_mxfp4_decode_routes",
+    "moe_mxfp4_down_routes",
     "moe_mxfp4_dequant",
     "moe_mxfp4_tile_weights",
     "moe_mxfp4_encode",
@@ -66,6 +70,7 @@ class MoeDesc(ctypes.Structure):
         ("swiglu_limit", ctypes.c_float),
         ("weight_layout", ctypes.c_int32),
         ("down_pairing", ctypes.c_int32),
+        ("w13_order", ctypes.c_int32),
     ]
 
 
@@ -81,6 +86,8 @@ _SIGNATURES = {
     "moe_mxfp4_plan": (_I32, [_DESC, _P, _P, _P, _P, _SZ, _P]),
     "moe_mxfp4_gate_up": (_I32, [_DESC, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_mxfp4_down": (_I32, [_DESC, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_mxfp4_decode_routes": (_I32, [_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_mxfp4_down_routes": (_I32, [_DESC, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_mxfp4_route": (_I32, [_DESC, _P, _P, _P, _P]),
     "moe_mxfp4_bucket": (_I32, [_DESC, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_mxfp4_dequant": (_I32, [_P, _P, _I64, _I64, _I32, _P, _P]),

@@ -110,17 +110,22 @@ __global__ __launch_bounds__(256, 4) void gemv_kernel(ExpertArgs A) {
   const int rows_e = kGateUp ? 2 * A.rows : A.rows;
   const uint8_t* __restrict__ wbase = A.wp + static_cast<size_t>(we.e) * rows_e * (red >> 1);
   const uint8_t* __restrict__ sbase = A.ws + static_cast<size_t>(we.e) * rows_e * RB;
-  const uint32_t wo0 = row_offset(n, red >> 1, A.tiled), wo1 = row_offset(n + A.rows, red >> 1, A.tiled);
+  const int il = kGateUp ? A.il : 0;                             // interleaved w13 rows
+  const int nr0 = kGateUp ? gate_row(n, il) : n, nr1 = up_row(n, A.rows, il);
+  const uint32_t wo0 = row_offset(nr0, red >> 1, A.tiled), wo1 = row_offset(nr1, red >> 1, A.tiled);
   const uint32_t bstride = block_stride(A.tiled);
-  const size_t row0 = static_cast<size_t>(we.e) * rows_e + n;  // bias index of the gate (or single) row
-  const size_t row1 = row0 + A.rows;                             // bias index of the up row
+  const size_t row0 = static_cast<size_t>(we.e) * rows_e + nr0;  // bias index of the gate (or single) row
+  const size_t row1 = static_cast<size_t>(we.e) * rows_e + nr1;  // bias index of the up row
   auto ldw = [&](uint32_t off, int b) { return *reinterpret_cast<const uint4*>(wbase + off + bstride * b); };
-  // scale strips of the tile's rows, staged in LDS: [kRowsPerWG][RB] (gate/single), then up
+  // scale strips of the tile's rows, staged in LDS: [kRowsPerWG][RB] (gate/single), then up;
+  // interleaved w13: the tile's 2 * kRowsPerWG stored rows in one strip
   unsigned char* sstrip = reinterpret_cast<unsigned char*>(xs) + kGemvMaxTokens * red * 2;
   const int strip = kRowsPerWG * RB;
-  const uint8_t* ss0 = sbase + static_cast<size_t>(tile * kRowsPerWG) * RB;
+  const uint8_t* ss0 = sbase + static_cast<size_t>(tile * kRowsPerWG) * (il ? 2 : 1) * RB;
   const uint8_t* ss1 = sbase + static_cast<size_t>(tile * kRowsPerWG + A.rows) * RB;
-  auto lds_scale = [&](int which, int b) -> uint32_t { return sstrip[which * strip + g * RB + b]; };
+  auto lds_scale = [&](int which, int b) -> uint32_t {
+    return il ? sstrip[(2 * g + which) * RB + b] : sstrip[which * strip + g * RB + b];
+  };
   const int nmax = (RB + kLanesPerRow - 1) / kLanesPerRow;  // ring steps (uniform)
   const int Te = we.Te;
 
@@ -166,8 +171,12 @@ __global__ __launch_bounds__(256, 4) void gemv_kernel(ExpertArgs A) {
       }
     }
     if (t0 == 0) {
-      dma_strip(ss0, sstrip, strip);
-      if (kGateUp) dma_strip(ss1, sstrip + strip, strip);
+      if (il) {
+        dma_strip(ss0, sstrip, 2 * strip);
+      } else {
+        dma_strip(ss0, sstrip, strip);
+        if (kGateUp) dma_strip(ss1, sstrip + strip, strip);
+      }
     }
     // 2. weight ring, unconditional (indices clamped to the row)
     uint4 r0[kRing], r1[kRing];
@@ -289,16 +298,23 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
   const int rows_e = kGateUp ? 2 * A.rows : A.rows;
   const uint8_t* __restrict__ wbase = A.wp + static_cast<size_t>(we.e) * rows_e * (red >> 1);
   const uint8_t* __restrict__ sbase = A.ws + static_cast<size_t>(we.e) * rows_e * RB;
-  const uint32_t wo0 = row_offset(wrow, red >> 1, A.tiled);
-  const uint32_t wo1 = row_offset(wrow + A.rows, red >> 1, A.tiled);
+  const int il = kGateUp ? A.il : 0;                // interleaved w13 rows
+  const uint32_t wo0 = row_offset(kGateUp ? gate_row(wrow, il) : wrow, red >> 1, A.tiled);
+  const uint32_t wo1 = row_offset(up_row(wrow, A.rows, il), red >> 1, A.tiled);
   const uint32_t bstride = block_stride(A.tiled);
   // scale strips of the tile's rows (clamped to the expert), staged in LDS once:
-  // [kMfmaRows][RB] (gate/single), then up
+  // [kMfmaRows][RB] (gate/single), then up; interleaved w13: the tile's stored
+  // rows (gate, up alternating) in one strip
   const int srows = min(kMfmaRows, A.rows - tile * kMfmaRows);
   unsigned char* sstrip = lds + 2 * kBuf;
   const int strip = kMfmaRows * RB;
-  dma_strip(sbase + static_cast<size_t>(tile * kMfmaRows) * RB, sstrip, srows * RB);
-  if (kGateUp) dma_strip(sbase + static_cast<size_t>(tile * kMfmaRows + A.rows) * RB, sstrip + strip, srows * RB);
+  if (il) {
+    dma_strip(sbase + static_cast<size_t>(2 * tile * kMfmaRows) * RB, sstrip, 2 * srows * RB);
+  } else {
+    dma_strip(sbase + static_cast<size_t>(tile * kMfmaRows) * RB, sstrip, srows * RB);
+    if (kGateUp) dma_strip(sbase + static_cast<size_t>(tile * kMfmaRows + A.rows) * RB, sstrip + strip, srows * RB);
+  }
+  const int s0i = il ? 2 * RB : RB, s1b = il ? RB : strip;  // scale of set j, strip row l: [j * s1b + l * s0i]
   const int srow_l = min(wave * 16 + r, srows - 1);  // this lane's row in the strips
 
   for (int tp0 = 0; tp0 < we.Te; tp0 += kTokens) {
@@ -369,8 +385,8 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
         const bool valid = c * kChunkBlocks + q < RB;  // false past the row and past the last chunk
         // a zero scale turns a ragged-tail block into zeros
         const int bs = min(c * kChunkBlocks + q, RB - 1);
-        const float sc0 = valid ? e8m0_to_f32(sstrip[srow_l * RB + bs]) : 0.0f;
-        const float sc1 = (kGateUp && valid) ? e8m0_to_f32(sstrip[strip + srow_l * RB + bs]) : 0.0f;
+        const float sc0 = valid ? e8m0_to_f32(sstrip[srow_l * s0i + bs]) : 0.0f;
+        const float sc1 = (kGateUp && valid) ? e8m0_to_f32(sstrip[s1b + srow_l * s0i + bs]) : 0.0f;
         const uint32_t d0[4] = {rw0[s].x, rw0[s].y, rw0[s].z, rw0[s].w};
         uint32_t d1[4] = {0, 0, 0, 0};
         if (kGateUp) {
@@ -409,11 +425,11 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
       const int rowbase = wrow0 + 4 * q;
       float b0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, b1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if (A.bias != nullptr) {
-        const size_t bb = static_cast<size_t>(we.e) * rows_e + rowbase;
+        const size_t bb = static_cast<size_t>(we.e) * rows_e;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          b0[i] = bf16_bits_to_f32(A.bias[bb + i]);
-          if (kGateUp) b1[i] = bf16_bits_to_f32(A.bias[bb + A.rows + i]);
+          b0[i] = bf16_bits_to_f32(A.bias[bb + (kGateUp ? gate_row(rowbase + i, il) : rowbase + i)]);
+          if (kGateUp) b1[i] = bf16_bits_to_f32(A.bias[bb + up_row(rowbase + i, A.rows, il)]);
         }
       }
 #pragma unroll
@@ -568,6 +584,21 @@ __global__ __launch_bounds__(256) void encode_kernel(const void* __restrict__ in
 
 template __global__ void encode_kernel<true>(const void*, int64_t, int, uint8_t*, uint8_t*);
 template __global__ void encode_kernel<false>(const void*, int64_t, int, uint8_t*, uint8_t*);
+
+// Per-route output rows: grid (ceil(K / 1024), R); each thread four columns.
+__global__ __launch_bounds__(256) void route_rows_kernel(const float* __restrict__ o, const int32_t* __restrict__ pos,
+                                                         float* __restrict__ out, int R, int K, int in_place) {
+  const int r = blockIdx.y;
+  const int k4 = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (r >= R || k4 >= K) return;
+  const int p = pos[r];
+  float4* dst = reinterpret_cast<float4*>(out + static_cast<size_t>(r) * K + k4);
+  if (p < 0) {
+    *dst = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  } else if (!in_place) {
+    *dst = *reinterpret_cast<const float4*>(o + static_cast<size_t>(p) * K + k4);
+  }
+}
 
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ packed,
                                                       const uint8_t* __restrict__ scales, int64_t n_blocks,

@@ -93,6 +93,13 @@ __device__ __forceinline__ uint32_t row_offset(int n, uint32_t row_bytes, int ti
 }
 __device__ __forceinline__ uint32_t block_stride(int tiled) { return tiled ? 256u : 16u; }
 
+// Stored w13 row of gate row n and of up row n (rows = I row pairs per
+// expert): [gate; up] puts them at n and rows + n, the interleaved order at
+// 2n and 2n + 1 ("MXFP4 MoE decode kernels", Beyond gpt-oss; scales and b13
+// follow the same row order).
+__device__ __forceinline__ int gate_row(int n, int il) { return il ? 2 * n : n; }
+__device__ __forceinline__ int up_row(int n, int rows, int il) { return il ? 2 * n + 1 : rows + n; }
+
 struct ExpertArgs {
   const uint16_t* in;      // gate/up: x [T, K]; down: a [R, I]  (bf16)
   const int32_t* routes;   // gate/up: activation row of position p is routes[p] / top_k; down: nullptr (row p)
@@ -105,6 +112,7 @@ struct ExpertArgs {
   int red;                 // reduction length: K (gate/up) or I (down)
   int rows;                // output rows per expert: I row pairs (gate/up) or K (down)
   int tiled;               // packed weights in the tiled layout
+  int il;                  // gate/up: w13 rows interleaved (gate_row / up_row)
   uint16_t* a_out;         // gate/up output [R, I] bf16
   float* o_out;            // down output [R, K] fp32
   int act_kind;
@@ -168,6 +176,7 @@ struct StreamArgs {
   int top_k;
   int o_by_route;            // down: o rows indexed by route (t*top_k + j) instead of plan position
   int tiled;                 // packed weights in the tiled layout
+  int il;                    // gate/up: w13 rows interleaved (gate_row / up_row)
   uint16_t* a_out;           // gate/up output [R, I] bf16
   float* o_out;              // down output [R, K] fp32
   int act_kind;
@@ -193,6 +202,10 @@ __global__ void stream_kernel(StreamArgs A);
 constexpr int kStreamRing = 4;   // steps (4 MX blocks per lane) in flight per wave
 constexpr int kStreamMaxItems = 32;  // items per workgroup (their entries live in LDS)
 __global__ void combine_kernel(CombineArgs A);
+// Per-route output rows [R, K] fp32: rows of routes outside the slice become
+// zeros; with in_place == 0 the others are copied from o (plan order) to
+// their route's row.
+__global__ void route_rows_kernel(const float* o, const int32_t* pos, float* out, int R, int K, int in_place);
 // In-place row layout <-> tiled layout, one workgroup per 16-row group.
 __global__ void tile_kernel(uint8_t* packed, int64_t groups, int blocks, int inverse);
 // MXFP4 encoder, four lanes per 32-value block (bf16 or fp32 input); each

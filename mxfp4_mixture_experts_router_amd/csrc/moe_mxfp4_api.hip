@@ -68,6 +68,7 @@ int check_desc(const moe_mxfp4_desc* d) {
   if (d->weight_layout != MOE_LAYOUT_ROWS && d->weight_layout != MOE_LAYOUT_TILE16) return MOE_ERR_MODE;
   if (d->down_pairing != MOE_PAIRING_AUTO && d->down_pairing != MOE_PAIRING_ON && d->down_pairing != MOE_PAIRING_OFF)
     return MOE_ERR_MODE;
+  if (d->w13_order != MOE_W13_GATE_UP && d->w13_order != MOE_W13_INTERLEAVED) return MOE_ERR_MODE;
   return MOE_OK;
 }
 
@@ -334,6 +335,7 @@ void enqueue_w13(const moe_mxfp4_desc& d, const uint16_t* x, const uint8_t* w13p
   A.red = d.K;
   A.rows = d.I;
   A.tiled = d.weight_layout == MOE_LAYOUT_TILE16;
+  A.il = d.w13_order == MOE_W13_INTERLEAVED;
   A.a_out = a != nullptr ? a : at<uint16_t>(ws, L.a);
   A.act_kind = d.activation;
   A.alpha = d.swiglu_alpha;
@@ -349,6 +351,7 @@ void enqueue_w13(const moe_mxfp4_desc& d, const uint16_t* x, const uint8_t* w13p
     S.red = d.K;
     S.rows = d.I;
     S.tok_from_pass = 1;
+    S.il = A.il;
     S.a_out = A.a_out;
     enqueue_stream<true>(d, split, S, s);
     return;
@@ -356,8 +359,10 @@ void enqueue_w13(const moe_mxfp4_desc& d, const uint16_t* x, const uint8_t* w13p
   enqueue_expert_pair(d, true, A, L, ws, s);
 }
 
-void enqueue_w2_combine(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_t* w2p, const uint8_t* w2s,
-                        const uint16_t* b2, uint16_t* out, void* ws, hipStream_t s) {
+// The down projection, then either the per-token combine into out (bf16
+// [T, K]) or, with out_routes, the per-route rows (fp32 [T*top_k, K]).
+void enqueue_w2(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_t* w2p, const uint8_t* w2s,
+                const uint16_t* b2, uint16_t* out, float* out_routes, void* ws, hipStream_t s) {
   const Layout L = make_layout(d);
   moe::ExpertArgs A{};
   A.in = a != nullptr ? a : at<uint16_t>(ws, L.a);
@@ -381,8 +386,10 @@ void enqueue_w2_combine(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_
   C.top_k = d.top_k;
   C.by_route = 0;
   const int split = stream_split(d);
+  const int R = d.T * d.top_k;
   if (stream_fits(d.I, split)) {
     C.by_route = 1;
+    if (out_routes != nullptr) A.o_out = out_routes;  // rows by route, straight into the caller's buffer
     moe::StreamArgs S = stream_args(d, L, ws);
     S.in = A.in;
     S.in_bytes = static_cast<uint32_t>(static_cast<size_t>(d.T) * d.top_k * d.I * 2);
@@ -398,7 +405,12 @@ void enqueue_w2_combine(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_
   } else {
     enqueue_expert_pair(d, false, A, L, ws, s);
   }
-  hipLaunchKernelGGL(moe::combine_kernel, dim3((d.K / 4 + 255) / 256, d.T), dim3(256), 0, s, C);
+  if (out_routes != nullptr) {
+    hipLaunchKernelGGL(moe::route_rows_kernel, dim3((d.K / 4 + 255) / 256, R), dim3(256), 0, s, C.o, C.pos,
+                       out_routes, R, d.K, C.by_route);
+  } else {
+    hipLaunchKernelGGL(moe::combine_kernel, dim3((d.K / 4 + 255) / 256, d.T), dim3(256), 0, s, C);
+  }
 }
 
 int check_routing(const moe_mxfp4_desc& d, const float* logits, const int32_t* ids, const float* wts) {
@@ -440,7 +452,29 @@ int moe_mxfp4_decode(const moe_mxfp4_desc* desc, const uint16_t* x, const float*
   hipStream_t s = static_cast<hipStream_t>(stream);
   enqueue_plan(d, router_logits, topk_ids, topk_weights, workspace, s);
   enqueue_w13(d, x, w13_packed, w13_scales, w13_bias, nullptr, workspace, s);
-  enqueue_w2_combine(d, nullptr, w2_packed, w2_scales, w2_bias, out, workspace, s);
+  enqueue_w2(d, nullptr, w2_packed, w2_scales, w2_bias, out, nullptr, workspace, s);
+  return launch_status();
+}
+
+int moe_mxfp4_decode_routes(const moe_mxfp4_desc* desc, const uint16_t* x, const float* router_logits,
+                            const int32_t* topk_ids, const float* topk_weights, const uint8_t* w13_packed,
+                            const uint8_t* w13_scales, const uint16_t* w13_bias, const uint8_t* w2_packed,
+                            const uint8_t* w2_scales, const uint16_t* w2_bias, float* out_routes, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const moe_mxfp4_desc& d = *desc;
+  if ((st = check_routing(d, router_logits, topk_ids, topk_weights)) != MOE_OK) return st;
+  if (d.T == 0) return MOE_OK;
+  if (!x || !w13_packed || !w13_scales || !w2_packed || !w2_scales || !out_routes) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w13_packed) || !aligned16(w2_packed) || !aligned16(out_routes) ||
+      !aligned16(w13_scales) || !aligned16(w2_scales) || !aligned16(w13_bias) || !aligned16(w2_bias))
+    return MOE_ERR_ALIGN;
+  if ((st = check_workspace(d, workspace, workspace_bytes)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  enqueue_plan(d, router_logits, topk_ids, topk_weights, workspace, s);
+  enqueue_w13(d, x, w13_packed, w13_scales, w13_bias, nullptr, workspace, s);
+  enqueue_w2(d, nullptr, w2_packed, w2_scales, w2_bias, nullptr, out_routes, workspace, s);
   return launch_status();
 }
 
@@ -479,7 +513,22 @@ int moe_mxfp4_down(const moe_mxfp4_desc* desc, const uint16_t* a, const uint8_t*
   if (!aligned16(a) || !aligned16(w2_packed) || !aligned16(w2_scales) || !aligned16(w2_bias) || !aligned16(out))
     return MOE_ERR_ALIGN;
   if ((st = check_workspace(*desc, workspace, workspace_bytes)) != MOE_OK) return st;
-  enqueue_w2_combine(*desc, a, w2_packed, w2_scales, w2_bias, out, workspace, static_cast<hipStream_t>(stream));
+  enqueue_w2(*desc, a, w2_packed, w2_scales, w2_bias, out, nullptr, workspace, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int moe_mxfp4_down_routes(const moe_mxfp4_desc* desc, const uint16_t* a, const uint8_t* w2_packed,
+                          const uint8_t* w2_scales, const uint16_t* w2_bias, float* out_routes, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (desc->T == 0) return MOE_OK;
+  if (!w2_packed || !w2_scales || !out_routes) return MOE_ERR_NULL;
+  if (!aligned16(a) || !aligned16(w2_packed) || !aligned16(w2_scales) || !aligned16(w2_bias) || !aligned16(out_routes))
+    return MOE_ERR_ALIGN;
+  if ((st = check_workspace(*desc, workspace, workspace_bytes)) != MOE_OK) return st;
+  enqueue_w2(*desc, a, w2_packed, w2_scales, w2_bias, nullptr, out_routes, workspace,
+             static_cast<hipStream_t>(stream));
   return launch_status();
 }
 

@@ -74,6 +74,17 @@ __device__ __forceinline__ uint4 as_uint4(const __attribute__((ext_vector_type(4
 
 constexpr uint32_t kOob = 0x80000000u;  // buffer offset past every range: the load returns zeros
 
+// Wave priority from the items a workgroup still has to finish (0..3).  At
+// equal priority a CU issues for its oldest waves first, so the workgroups
+// dispatched last onto a CU stream slower; ranking by remaining work lets
+// the ones that fell behind catch up, which shortens the launch's tail.
+__device__ __forceinline__ void set_priority(int remaining_items) {
+  if (remaining_items >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (remaining_items == 2) __builtin_amdgcn_s_setprio(2);
+  else if (remaining_items == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 }  // namespace
 
 template <bool kGateUp, int kSplit, bool kPair>
@@ -101,6 +112,12 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
   // gate/up, the next 16 output rows of a paired down wave (in both weight
   // layouts row n + 16 sits 16 row lengths after row n)
   const int set1 = kGateUp ? rows : 16;
+  // interleaved w13 (gate/up only): the wave's 16 gate rows and 16 up rows
+  // are 32 consecutive stored rows, staged as one strip; scale of set j of
+  // lane row r at strip[sub * j + srs * r + block]
+  const int il = kGateUp ? A.il : 0;
+  const int srs = il ? 2 * RB : RB;
+  const int sub = il ? RB : 16 * RB;
   const uint32_t row_bytes = static_cast<uint32_t>(red >> 1);
   const uint32_t expert_bytes = static_cast<uint32_t>(rows_e) * row_bytes;
   const uint32_t bstride = block_stride(A.tiled);
@@ -147,7 +164,7 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
   // load cursor (item li, step ls) and what it needs of item li
   int li = 0, ls = 0;
   int l_e = 0, l_nt = 0, l_p = 0, l_row0 = 0;  // uniform
-  uint32_t l_wo = 0;                           // this lane's gate row offset in the expert
+  uint32_t l_wo = 0, l_wo1 = 0;                // this lane's row offsets (set 0, set 1) in the expert
   uint32_t l_xoff = 0;                         // staging thread's activation row (bytes)
   __amdgpu_buffer_rsrc_t wrs;                  // weights of expert l_e
 
@@ -164,22 +181,28 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
     // this wave's sub-tile: rows are a multiple of kWaveRows, so a sub-tile is
     // all in or all out; an out sub-tile re-reads the expert's last rows (results dropped)
     const int row0w = min(l_row0 + st * kWaveRows, rows - kWaveRows);
-    l_wo = row_offset(row0w + r, row_bytes, A.tiled);
+    const int n = row0w + r;
+    l_wo = row_offset(kGateUp ? gate_row(n, il) : n, row_bytes, A.tiled);
+    l_wo1 = row_offset(kGateUp ? up_row(n, rows, il) : n + set1, row_bytes, A.tiled);
     wrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(A.wp) + static_cast<size_t>(l_e) * expert_bytes, 0,
                                             expert_bytes, 0x00020000);
     // scale strip(s) and bias of rows row0w..row0w+15 into this wave's slot
     const uint32_t dst = sbuf_off + static_cast<uint32_t>(((li & 1) * 4 + wave) * sw16);
-    const uint8_t* s0 = A.ws + (static_cast<size_t>(l_e) * rows_e + row0w) * RB;
-    for (int m = 0; m * 64 < RB; ++m) {
-      if (m * 64 + lane < RB) lds_dma16(dst + m * 1024, s0 + (m * 64 + lane) * 16);
+    const uint8_t* s0 = A.ws + (static_cast<size_t>(l_e) * rows_e + (il ? 2 * row0w : row0w)) * RB;
+    const int pieces0 = il ? 2 * RB : RB;  // 16 B pieces: 16 rows, or 32 interleaved rows
+    for (int m = 0; m * 64 < pieces0; ++m) {
+      if (m * 64 + lane < pieces0) lds_dma16(dst + m * 1024, s0 + (m * 64 + lane) * 16);
     }
-    if (kNW == 2) {
+    if (kNW == 2 && !il) {
       const uint8_t* s1 = s0 + static_cast<size_t>(set1) * RB;
       for (int m = 0; m * 64 < RB; ++m) {
         if (m * 64 + lane < RB) lds_dma16(dst + strip_bytes + m * 1024, s1 + (m * 64 + lane) * 16);
       }
     }
-    if (A.bias != nullptr && lane < 2) {
+    if (A.bias != nullptr && il && lane < 4) {
+      // 16 interleaved (gate, up) bias pairs
+      lds_dma16(dst + kNW * strip_bytes, A.bias + static_cast<size_t>(l_e) * rows_e + 2 * row0w + lane * 8);
+    } else if (A.bias != nullptr && lane < 2) {
       const uint16_t* b0 = A.bias + static_cast<size_t>(l_e) * rows_e + row0w;
       lds_dma16(dst + kNW * strip_bytes, b0 + lane * 8);
       if (kNW == 2) lds_dma16(dst + kNW * strip_bytes + 32, b0 + set1 + lane * 8);
@@ -196,7 +219,7 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
     const uint32_t o0 = ok ? l_wo + bstride * b : kOob;
     rw0[slot] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(wrs, o0, 0, 0));
     if (kNW == 2) {
-      const uint32_t o1 = ok ? l_wo + static_cast<uint32_t>(set1) * row_bytes + bstride * b : kOob;
+      const uint32_t o1 = ok ? l_wo1 + bstride * b : kOob;
       rw1[slot] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(wrs, o1, 0, 0));
     }
     // activation piece of the staging thread
@@ -236,6 +259,7 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
   // one step of the compute cursor, ring slot s (a compile-time constant)
   auto step = [&](const int g, const int s) {
     if (cs == 0) {
+      set_priority(n_my - ci);
       // strip of item ci: its DMA was issued before this step's weight
       // loads, so once they have arrived (in-order completion) the strip has
       asm volatile("" ::"v"(rw0[s].x), "v"(rw0[s].y), "v"(rw0[s].z), "v"(rw0[s].w) : "memory");
@@ -244,8 +268,8 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
     const int b = (kp * NCp + cs) * 4 + q;
     const bool valid = b < RB;
     const int bs = valid ? b : 0;
-    const float sc0 = valid ? e8m0_to_f32(strip[r * RB + bs]) : 0.0f;
-    const float sc1 = (kNW == 2 && valid) ? e8m0_to_f32(strip[strip_bytes + r * RB + bs]) : 0.0f;
+    const float sc0 = valid ? e8m0_to_f32(strip[r * srs + bs]) : 0.0f;
+    const float sc1 = (kNW == 2 && valid) ? e8m0_to_f32(strip[sub + r * srs + bs]) : 0.0f;
     const unsigned char* xb = xbuf + (g & 1) * kXBufBytes + bts * kXRowBytes + q * 64;
     const uint32_t d0[4] = {rw0[s].x, rw0[s].y, rw0[s].z, rw0[s].w};
 #pragma unroll
@@ -272,8 +296,8 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
         const uint16_t* bb = reinterpret_cast<const uint16_t*>(strip + kNW * strip_bytes);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          b0[i] = bf16_bits_to_f32(bb[4 * q + i]);
-          if (kNW == 2) b1[i] = bf16_bits_to_f32(bb[16 + 4 * q + i]);
+          b0[i] = bf16_bits_to_f32(bb[il ? 2 * (4 * q + i) : 4 * q + i]);
+          if (kNW == 2) b1[i] = bf16_bits_to_f32(bb[il ? 2 * (4 * q + i) + 1 : 16 + 4 * q + i]);
         }
       }
       if (kSplit > 1) {

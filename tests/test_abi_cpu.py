@@ -43,7 +43,7 @@ def test_version_and_status_strings():
 
 def _desc(**kw):
     d = dict(T=4, K=256, I=256, E_global=8, E_local=8, expert_offset=0, top_k=2, scoring=0,
-             activation=0, swiglu_alpha=1.702, swiglu_limit=7.0, weight_layout=0, down_pairing=0)
+             activation=0, swiglu_alpha=1.702, swiglu_limit=7.0, weight_layout=0, down_pairing=0, w13_order=0)
     d.update(kw)
     return _lib.MoeDesc(**d)
 
@@ -77,6 +77,8 @@ def test_workspace_query():
     (dict(E_global=600, E_local=513), _lib.MOE_ERR_SHAPE),
     (dict(scoring=2), _lib.MOE_ERR_MODE),
     (dict(activation=-1), _lib.MOE_ERR_MODE),
+    (dict(w13_order=2), _lib.MOE_ERR_MODE),
+    (dict(w13_order=-1), _lib.MOE_ERR_MODE),
 ])
 def test_bad_descriptors_are_refused(bad, code):
     st, _ = _ws_bytes(_desc(**bad))
@@ -119,6 +121,35 @@ def test_decode_error_paths():
     assert _decode(_desc(E_global=2048, E_local=8)) == E.MOE_ERR_SHAPE   # too many experts to route
     assert _decode(_desc(T=0)) == E.MOE_OK                               # T = 0: nothing to do
     assert _decode(_desc(T=0), x=None, out=None) == E.MOE_OK
+
+
+def _decode_routes(d, **kw):
+    args = dict(x=A, logits=A, ids=None, wts=None, w13p=A, w13s=A, b13=None, w2p=A, w2s=A, b2=None,
+                out=A, ws=A, ws_bytes=1 << 40)
+    args.update(kw)
+    return _lib.lib().moe_mxfp4_decode_routes(
+        ctypes.byref(d), args["x"], args["logits"], args["ids"], args["wts"], args["w13p"], args["w13s"],
+        args["b13"], args["w2p"], args["w2s"], args["b2"], args["out"], args["ws"], args["ws_bytes"], None)
+
+
+def test_route_output_error_paths():
+    d = _desc()
+    E, L = _lib, _lib.lib()
+    assert _decode_routes(d, logits=None) == E.MOE_ERR_MODE
+    assert _decode_routes(d, out=None) == E.MOE_ERR_NULL
+    assert _decode_routes(d, w13p=None) == E.MOE_ERR_NULL
+    assert _decode_routes(d, out=A_MIS) == E.MOE_ERR_ALIGN
+    assert _decode_routes(d, b2=A_MIS) == E.MOE_ERR_ALIGN
+    _, need = _ws_bytes(d)
+    assert _decode_routes(d, ws_bytes=need - 1) == E.MOE_ERR_WORKSPACE
+    assert _decode_routes(_desc(w13_order=5)) == E.MOE_ERR_MODE
+    assert _decode_routes(_desc(T=0), x=None, out=None) == E.MOE_OK
+    down = L.moe_mxfp4_down_routes
+    assert down(ctypes.byref(d), None, A, A, None, None, A, 1 << 40, None) == E.MOE_ERR_NULL
+    assert down(ctypes.byref(d), None, A, A, None, A_MIS, A, 1 << 40, None) == E.MOE_ERR_ALIGN
+    assert down(ctypes.byref(d), A_MIS, A, A, None, A, A, 1 << 40, None) == E.MOE_ERR_ALIGN
+    assert down(ctypes.byref(d), None, A, A, None, A, A, need - 1, None) == E.MOE_ERR_WORKSPACE
+    assert down(ctypes.byref(_desc(T=0)), None, A, A, None, None, A, 1 << 40, None) == E.MOE_OK
 
 
 def test_tile_weights_error_paths():

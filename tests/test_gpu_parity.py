@@ -15,7 +15,7 @@ import pytest
 
 import mxfp4_mixture_experts_router_amd as moe
 import oracle
-from workloads import LayerConfig, get_config, make_inputs, make_topk_inputs, make_weights
+from workloads import LayerConfig, LayerWeights, get_config, make_inputs, make_topk_inputs, make_weights
 
 from gpu_util import (DeviceLayer, bf16_bits_np, bf16_to_np, desc_for, dev_bf16, dev_f32, dev_i32, dev_u8,
                       run_decode, torch)
@@ -412,6 +412,91 @@ def test_down_pairing_bit_identical_and_matches_oracle(case):
     assert np.array_equal(off, on), name
     ref = oracle.moe_forward_cfg(cfg, w, inp)
     _assert_close(bf16_to_np(run_decode(cfg, layer, inp, down_pairing="on")), ref["y"], name)
+
+
+# interleaved gate/up rows: the same per-row arithmetic as [gate; up], so the
+# output is bit-identical to the [gate; up] storage of the same weights
+def _interleaved_weights(w, I):
+    def il(a):
+        out = np.empty_like(a)
+        out[:, 0::2] = a[:, :I]
+        out[:, 1::2] = a[:, I:]
+        return out
+    return LayerWeights(w13_packed=il(w.w13_packed), w13_scales=il(w.w13_scales), w2_packed=w.w2_packed,
+                        w2_scales=w.w2_scales, b13=None if w.b13 is None else il(w.b13), b2=w.b2)
+
+
+INTERLEAVED_CASES = [
+    ("stream-split4", dict(K=2080, I=2048, E_global=8, E_local=6, expert_offset=1, top_k=2,
+                           activation="swiglu_oai", bias=True, scale_lo=115, scale_hi=127), 2, "rows"),
+    ("stream-split4-tiled", dict(K=2080, I=2048, E_global=8, E_local=6, expert_offset=1, top_k=2,
+                                 activation="swiglu_oai", bias=True, scale_lo=115, scale_hi=127), 3, "tile16"),
+    ("stream-split2-tiled", dict(K=1120, I=1056, E_global=4, E_local=4, top_k=2, bias=True), 7, "tile16"),
+    ("stream-split1", dict(K=544, I=608, E_global=4, E_local=4, top_k=2), 20, "rows"),
+    ("gemv-lists", dict(bias=True, activation="swiglu_oai", scale_lo=115, scale_hi=127), 4, "rows"),
+    ("mfma-lists-tiled", dict(K=512, I=768, E_global=2, E_local=2, top_k=2, bias=True), 80, "tile16"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(INTERLEAVED_CASES)))
+def test_interleaved_rows_bit_identical_and_match_oracle(case):
+    name, kw, T, layout = INTERLEAVED_CASES[case]
+    cfg = _cfg(**kw)
+    w = make_weights(cfg)
+    wi = _interleaved_weights(w, cfg.I)
+    inp = make_inputs(cfg, T, t_index=case)
+    blocked = bf16_bits_np(run_decode(cfg, DeviceLayer(w, layout=layout), inp))
+    y = run_decode(cfg, DeviceLayer(wi, layout=layout), inp, w13_order="interleaved")
+    assert np.array_equal(bf16_bits_np(y), blocked), name
+    ref = oracle.moe_forward_cfg(cfg, wi, inp, w13_order="interleaved")
+    _assert_close(bf16_to_np(y), ref["y"], name)
+
+
+# per-route output: W2 a_r + b2 of each local route, zeros elsewhere
+ROUTE_OUT_CASES = [
+    ("stream-slice", dict(K=1120, I=1056, E_global=8, E_local=4, expert_offset=2, top_k=2, bias=True), 6, "tile16"),
+    ("stream-split1", dict(K=544, I=608, E_global=6, E_local=4, expert_offset=1, top_k=2, activation="swiglu_oai", bias=True,
+                           scale_lo=115, scale_hi=127), 20, "rows"),
+    ("gemv-lists-slice", dict(E_global=8, E_local=5, expert_offset=3), 4, "rows"),
+    ("mfma-lists-slice", dict(K=512, I=768, E_global=4, E_local=2, expert_offset=1, top_k=2, bias=True), 80,
+     "tile16"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(ROUTE_OUT_CASES)))
+def test_route_outputs_match_oracle(case):
+    t = torch()
+    name, kw, T, layout = ROUTE_OUT_CASES[case]
+    cfg = _cfg(**kw)
+    w = make_weights(cfg)
+    inp = make_inputs(cfg, T, t_index=case)
+    layer = DeviceLayer(w, layout=layout)
+    d = desc_for(cfg, T, weight_layout=layout)
+    R = T * cfg.top_k
+    x, lg = dev_bf16(inp.x), dev_f32(inp.logits)
+    rows = t.full((R, cfg.K), float("nan"), dtype=t.float32, device="cuda")
+    moe.moe_mxfp4_decode_routes(d, x, layer.w13p, layer.w13s, layer.w2p, layer.w2s, rows, router_logits=lg,
+                                w13_bias=layer.b13, w2_bias=layer.b2)
+    t.cuda.synchronize()
+    got = rows.cpu().numpy()
+    ref = oracle.moe_forward_cfg(cfg, w, inp)
+    want = oracle.route_outputs(ref, T, cfg.top_k)
+    local = np.zeros(R, bool)
+    local[ref["routes"]] = True
+    assert (~local).any() and local.any(), name
+    assert np.array_equal(got[~local], np.zeros_like(got[~local])), name
+    _assert_close(got[local], want[local], name)
+    # the steps one by one give the same bits
+    ws = moe.moe_mxfp4_plan(d, router_logits=lg)
+    moe.moe_mxfp4_gate_up(d, x, layer.w13p, layer.w13s, ws, w13_bias=layer.b13)
+    rows2 = t.full((R, cfg.K), float("nan"), dtype=t.float32, device="cuda")
+    moe.moe_mxfp4_down_routes(d, layer.w2p, layer.w2s, rows2, ws, w2_bias=layer.b2)
+    t.cuda.synchronize()
+    assert np.array_equal(rows2.cpu().numpy(), got), name
+    # the routing-weighted sum of the rows is the layer output
+    y = bf16_to_np(run_decode(cfg, layer, inp)).astype(np.float64)
+    ysum = np.einsum("tj,tjk->tk", ref["weights"].astype(np.float64), got.reshape(T, cfg.top_k, cfg.K))
+    assert oracle.rel_l2(y, ysum) <= 3e-3, name
 
 
 def test_layer_ids_mode_with_padding_and_foreign_ids():
