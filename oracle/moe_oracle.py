@@ -225,6 +225,23 @@ def untile16(tiled: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(np.swapaxes(g, -3, -2)).reshape(tiled.shape)
 
 
+def unpack_bf16(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """The prefill unpack ("MXFP4 MoE decode kernels", Prefill: unpack once,
+    then the stock op): dequantised values as bf16 bit patterns (uint16).
+
+    An E2M1 value times a power of two has at most two significant bits and
+    bf16 keeps fp32's exponent range, so every finite product is a bf16 value:
+    the pattern is the upper half of the fp32 dequantisation, exactly.  A NaN
+    scale (byte 255) gives a NaN pattern.
+    """
+    f = dequantize(packed, scales)
+    bits = f.view(np.uint32)
+    finite = ~np.isnan(f)
+    if np.any((bits[finite] & 0xFFFF) != 0):
+        raise AssertionError("a dequantised value is not a bf16 value")
+    return (bits >> 16).astype(np.uint16)
+
+
 def bf16_bits_to_float(bits: np.ndarray) -> np.ndarray:
     """Raw bf16 patterns (uint16) -> float32 (exact widening)."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16

@@ -67,6 +67,23 @@ def test_dequant_exhaustive_codes_scales_nibble_positions():
             assert v == want and np.signbit(v) == np.signbit(want), (s, col, v, want)
 
 
+def test_unpack_bf16_exhaustive_is_exact():
+    # every code x every scale x both nibble positions: the bf16 pattern widens
+    # back to the fp32 dequantisation exactly and equals round-to-nearest-even
+    # of it (computed from float64, a separate path); NaN stays NaN
+    byte_row = np.array([(i & 0xF) | ((15 - i) << 4) for i in range(16)], dtype=np.uint8)
+    packed = np.tile(byte_row, (256, 1))
+    scales = np.arange(256, dtype=np.uint8).reshape(256, 1)
+    bits = oracle.unpack_bf16(packed, scales)
+    f = oracle.dequantize(packed, scales)
+    wide = oracle.bf16_bits_to_float(bits)
+    nan = np.isnan(f)
+    assert np.array_equal(np.isnan(wide), nan) and nan[255].all() and not nan[:255].any()
+    assert np.array_equal(wide[~nan].view(np.uint32), f[~nan].view(np.uint32))
+    rn = oracle.round_to_bf16(f[~nan].astype(np.float64))
+    assert np.array_equal(rn, f[~nan].astype(np.float64))
+
+
 def test_nibble_order_golden(golden_dir):
     g = json.load(open(os.path.join(golden_dir, "mxfp4_format.json")))
     for ex in g["nibble_examples"]:
