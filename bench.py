@@ -64,6 +64,9 @@ def parse():
                    help="packed weight storage order (tile16: tiled in place once, before any timing)")
     p.add_argument("--w13-order", default="gate_up", choices=("gate_up", "interleaved"),
                    help="row order of w13 (interleaved: gate and up rows alternate)")
+    p.add_argument("--prefill", action="store_true",
+                   help="time the prefill path (unpack the touched experts to bf16, then bf16 MFMA GEMMs) "
+                        "against the decode path on the same calls (default: the wide-K slice at T=256, 2048)")
     p.add_argument("--per-route", action="store_true",
                    help="per-route output: fp32 [T*top_k, K] rows instead of the bf16 token sums")
     return p.parse_args()
@@ -124,6 +127,9 @@ def main():
 
     if args.encode:
         print(json.dumps(encode_bench(torch, moe, get_config(args.config), args)), flush=True)
+        return
+    if args.prefill:
+        print(json.dumps(prefill_bench(torch, moe, args)), flush=True)
         return
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -308,6 +314,90 @@ def encode_bench(torch, moe, cfg, args):
             "config": {"workload": f"w13 of the {cfg.name} layer as bf16 [{E}, {2 * I}, {K}], Quark rule"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
+def prefill_bench(torch, moe, args):
+    """The prefill path against the decode path: the same calls (replica-rotating
+    chains, HIP events on the launch stream), the same algorithmic bytes (packed
+    weights, scales and biases of the touched experts, x, logits, out)."""
+    from workloads import get_config, make_inputs
+    cfg = get_config("widek" if args.config == "gptoss20b" else args.config)
+    tokens = [int(t) for t in args.tokens.split(",")] if args.tokens else [t for t in cfg.tokens if t > 64] or [256]
+    K, I = cfg.K, cfg.I
+    per_expert = cfg.bytes_per_expert()
+    t_min = min(tokens)
+    exp_touched = cfg.E_local * (1 - (1 - cfg.top_k / cfg.E_global) ** t_min)
+    L = min(max(2, math.ceil(args.rotate_mb * 1e6 / max(1.0, exp_touched * per_expert))), args.steps)
+    reps = [Replica(torch, cfg, i) for i in range(L)]
+    if args.layout == "tile16":
+        for r in reps:
+            moe.moe_mxfp4_tile_weights(r.w13p)
+            moe.moe_mxfp4_tile_weights(r.w2p)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    per_t = {}
+    for T in tokens:
+        d = moe.make_desc(T=T, K=K, I=I, E_global=cfg.E_global, E_local=cfg.E_local, top_k=cfg.top_k,
+                          expert_offset=cfg.expert_offset, scoring=cfg.scoring, activation=cfg.activation,
+                          swiglu_alpha=cfg.swiglu_alpha, swiglu_limit=cfg.swiglu_limit, weight_layout=args.layout)
+        inputs = [make_inputs(cfg, T, call=i) for i in range(L)]
+        xs = [torch.from_numpy(inp.x.view(np.int16)).cuda().view(torch.bfloat16) for inp in inputs]
+        lg = [torch.from_numpy(inp.logits).cuda() for inp in inputs]
+        nb = moe.moe_mxfp4_prefill_workspace_bytes(d)
+        wss = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(L)]
+        outs = [torch.empty((T, K), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+
+        def call(fn):
+            def f(i, s):
+                r = reps[i % L]
+                fn(d, xs[i % L], r.w13p, r.w13s, r.w2p, r.w2s, outs[i % L], router_logits=lg[i % L],
+                   w13_bias=r.b13, w2_bias=r.b2, workspace=wss[i % L], stream=s)
+            return f
+
+        timing = {}
+        for name, fn in (("decode", moe.moe_mxfp4_decode), ("prefill", moe.moe_mxfp4_prefill)):
+            f = call(fn)
+            with torch.cuda.stream(stream):
+                for i in range(L):
+                    f(i, stream)
+            stream.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(args.steps):
+                    f(i, stream)
+            with torch.cuda.stream(stream):
+                for _ in range(args.warmup):
+                    g.replay()
+                stream.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            timing[name] = e0.elapsed_time(e1) * 1000.0 / args.steps
+            del g
+        touched = [int(wss[i][:4].view(torch.int32).item()) for i in range(L)]
+        calls = [i % L for i in range(args.steps)]
+        bytes_call = float(np.mean([touched[c] * per_expert + 4 * T * K + 4 * T * cfg.E_global for c in calls]))
+        unpacked = float(np.mean([touched[c] * 3 * I * K * 2 for c in calls]))
+        per_t[str(T)] = dict(touched_experts=round(float(np.mean([touched[c] for c in calls])), 2),
+                             bytes_per_call=int(bytes_call), unpacked_bf16_bytes=int(unpacked),
+                             us_decode=round(timing["decode"], 2), us_prefill=round(timing["prefill"], 2),
+                             gbs_decode=round(bytes_call / timing["decode"] / 1e3, 1),
+                             gbs_prefill=round(bytes_call / timing["prefill"] / 1e3, 1))
+        log(f"T={T}: {json.dumps(per_t[str(T)])}")
+        del wss, outs
+        torch.cuda.synchronize()
+    us_p = sum(v["us_prefill"] for v in per_t.values())
+    us_d = sum(v["us_decode"] for v in per_t.values())
+    nbytes = sum(v["bytes_per_call"] for v in per_t.values())
+    return {"metric": "MoE prefill-path us/call and GB/s of touched-expert packed bytes (vs the decode path)",
+            "value": round(nbytes / us_p / 1e3, 1), "unit": "GB/s", "decode_path_gbs": round(nbytes / us_d / 1e3, 1),
+            "steps": args.steps, "warmup": args.warmup,
+            "config": {"workload": f"{cfg.description}; one call at each T in {tokens}", "replicas": L,
+                       "weight_layout": args.layout},
+            "per_T": per_t}
 
 
 def measured_traffic(cfg, tokens, layout, w13_order="gate_up"):

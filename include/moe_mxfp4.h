@@ -235,6 +235,43 @@ int moe_mxfp4_down_routes(const moe_mxfp4_desc* desc, const uint16_t* a,
                           float* out_routes, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Prefill path ("MXFP4 MoE decode kernels", Prefill: unpack once, then the
+ * stock op): the touched experts' weights are unpacked to bf16 in the
+ * workspace in one pass, then grouped MFMA GEMMs read the bf16 weights.  Same
+ * arguments and results as moe_mxfp4_decode (the products are the same in
+ * the same order: outputs are bit-identical to moe_mxfp4_decode wherever the
+ * latter takes its MFMA path), with a larger workspace:
+ * moe_mxfp4_prefill_workspace_bytes() = the decode workspace plus
+ * E_local * 3 * I * K bf16 values (the unpacked w13 and w2 of every local
+ * expert; untouched experts' regions are left unwritten).  This path moves
+ * about five times the bytes of the decode path (unpacked bf16 weights are
+ * read back after being written) and exists for callers that want the
+ * pages' prefill structure; moe_mxfp4_decode serves every token count.
+ */
+int moe_mxfp4_prefill_workspace_bytes(const moe_mxfp4_desc* desc, size_t* bytes);
+int moe_mxfp4_prefill(const moe_mxfp4_desc* desc,
+                      const uint16_t* x,
+                      const float* router_logits,
+                      const int32_t* topk_ids, const float* topk_weights,
+                      const uint8_t* w13_packed, const uint8_t* w13_scales, const uint16_t* w13_bias,
+                      const uint8_t* w2_packed, const uint8_t* w2_scales, const uint16_t* w2_bias,
+                      uint16_t* out,
+                      void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * The unpack step alone: for every local expert with a route in the plan held
+ * in `workspace` (moe_mxfp4_plan first), w13_out bf16 [E_local, 2I, K] and
+ * w2_out bf16 [E_local, K, I] get the exact values of the packed weights
+ * (every E2M1 x E8M0 product is a bf16 value), in the stored row order and
+ * the row layout whatever desc->weight_layout says; other experts' rows are
+ * not written.  Pointers 16-byte aligned.
+ */
+int moe_mxfp4_unpack(const moe_mxfp4_desc* desc, const uint8_t* w13_packed, const uint8_t* w13_scales,
+                     const uint8_t* w2_packed, const uint8_t* w2_scales, uint16_t* w13_out, uint16_t* w2_out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Routing step alone (test hook): router logits fp32 [T, E_global] ->
  * ids int32 [T, top_k] (logit descending, ties to the lower id) and
  * weights fp32 [T, top_k] (softmax over the selected logits, or sigmoid

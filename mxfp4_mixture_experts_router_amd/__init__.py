@@ -255,6 +255,61 @@ def moe_mxfp4_down_routes(desc: MoeDesc, w2_packed, w2_scales, out_routes, works
         wsp, wsn, _stream(stream)), "moe_mxfp4_down_routes")
 
 
+def moe_mxfp4_prefill_workspace_bytes(desc: MoeDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.lib().moe_mxfp4_prefill_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)),
+           "moe_mxfp4_prefill_workspace_bytes")
+    return n.value
+
+
+def moe_mxfp4_prefill(desc: MoeDesc, x, w13_packed, w13_scales, w2_packed, w2_scales, out,
+                      router_logits=None, topk_ids=None, topk_weights=None, w13_bias=None, w2_bias=None,
+                      workspace=None, stream=None):
+    """The prefill path (unpack the touched experts to bf16, then bf16 MFMA GEMMs);
+    same results as ``moe_mxfp4_decode``.  Returns the workspace used."""
+    torch = _torch()
+    d = desc
+    s13p, s13s, s13b, s2p, s2s, s2b = _weights_shapes(d)
+    need = moe_mxfp4_prefill_workspace_bytes(d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    if workspace.dtype != torch.uint8 or workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 device tensor")
+    _check(_lib.lib().moe_mxfp4_prefill(
+        ctypes.byref(d),
+        _ptr(x, torch.bfloat16, (d.T, d.K), "x"),
+        _ptr(router_logits, torch.float32, (d.T, d.E_global), "router_logits", True),
+        _ptr(topk_ids, torch.int32, (d.T, d.top_k), "topk_ids", True),
+        _ptr(topk_weights, torch.float32, (d.T, d.top_k), "topk_weights", True),
+        _ptr(w13_packed, torch.uint8, s13p, "w13_packed"),
+        _ptr(w13_scales, torch.uint8, s13s, "w13_scales"),
+        _ptr(w13_bias, torch.bfloat16, s13b, "w13_bias", True),
+        _ptr(w2_packed, torch.uint8, s2p, "w2_packed"),
+        _ptr(w2_scales, torch.uint8, s2s, "w2_scales"),
+        _ptr(w2_bias, torch.bfloat16, s2b, "w2_bias", True),
+        _ptr(out, torch.bfloat16, (d.T, d.K), "out"),
+        workspace.data_ptr(), workspace.numel(), _stream(stream)), "moe_mxfp4_prefill")
+    return workspace
+
+
+def moe_mxfp4_unpack(desc: MoeDesc, w13_packed, w13_scales, w2_packed, w2_scales, w13_out, w2_out, workspace,
+                     stream=None):
+    """bf16 values of the packed weights of every expert the plan in ``workspace`` touches."""
+    torch = _torch()
+    d = desc
+    s13p, s13s, _, s2p, s2s, _ = _weights_shapes(d)
+    ws, wsp, wsn = _workspace(d, workspace, w13_out.device)
+    _check(_lib.lib().moe_mxfp4_unpack(
+        ctypes.byref(d),
+        _ptr(w13_packed, torch.uint8, s13p, "w13_packed"),
+        _ptr(w13_scales, torch.uint8, s13s, "w13_scales"),
+        _ptr(w2_packed, torch.uint8, s2p, "w2_packed"),
+        _ptr(w2_scales, torch.uint8, s2s, "w2_scales"),
+        _ptr(w13_out, torch.bfloat16, (d.E_local, 2 * d.I, d.K), "w13_out"),
+        _ptr(w2_out, torch.bfloat16, (d.E_local, d.K, d.I), "w2_out"),
+        wsp, wsn, _stream(stream)), "moe_mxfp4_unpack")
+
+
 def moe_mxfp4_route(desc: MoeDesc, router_logits, topk_ids, topk_weights, stream=None):
     torch = _torch()
     d = desc

@@ -47,6 +47,9 @@ EXPORTED = (
     "moe_mxfp4_down",
     "moe_mxfp4_decode_routes",
     "moe_mxfp4_down_routes",
+    "moe_mxfp4_prefill_workspace_bytes",
+    "moe_mxfp4_prefill",
+    "moe_mxfp4_unpack",
     "moe_mxfp4_dequant",
     "moe_mxfp4_tile_weights",
     "moe_mxfp4_encode",
@@ -88,6 +91,9 @@ _SIGNATURES = {
     "moe_mxfp4_down": (_I32, [_DESC, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_mxfp4_decode_routes": (_I32, [_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_mxfp4_down_routes": (_I32, [_DESC, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_mxfp4_prefill_workspace_bytes": (_I32, [_DESC, ctypes.POINTER(_SZ)]),
+    "moe_mxfp4_prefill": (_I32, [_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_mxfp4_unpack": (_I32, [_DESC, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_mxfp4_route": (_I32, [_DESC, _P, _P, _P, _P]),
     "moe_mxfp4_bucket": (_I32, [_DESC, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_mxfp4_dequant": (_I32, [_P, _P, _I64, _I64, _I32, _P, _P]),

@@ -275,11 +275,17 @@ __global__ __launch_bounds__(256, 4) void gemv_kernel(ExpertArgs A) {
 // kRing chunks deep, with the loop unrolled by the ring depth so every slot
 // stays in its own registers and the compiler can count outstanding loads
 // exactly.  One LDS-only barrier per chunk; no branches inside the ring.
-template <bool kGateUp, int kGroups>
+//
+// kBf16W (prefill): the weights come unpacked to bf16 (row layout, A.wbf);
+// lane (r, q) loads the 64 bytes of block q of its row per chunk and feeds
+// its g-th 16 bytes to MFMA g: the operands the MXFP4 path decodes, in the
+// same order, so both give the same bits.
+template <bool kGateUp, int kGroups, bool kBf16W>
 __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertArgs A) {
   constexpr int kTokens = 16 * kGroups;
   constexpr int kBuf = kTokens * kXRowBytes;
-  constexpr int kRing = kGroups == 1 ? 5 : 4;  // chunks in flight per wave
+  constexpr int kRing = kBf16W ? 2 : (kGroups == 1 ? 5 : 4);  // chunks in flight per wave
+  constexpr int kWv = kBf16W ? 4 : 1;                         // 16-byte weight loads per lane and chunk
   extern __shared__ __align__(16) unsigned char lds[];  // [2][kTokens][kXRowBytes], then the scale strips
 
   const int tiles = (A.rows + kMfmaRows - 1) / kMfmaRows;
@@ -296,19 +302,24 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
   const int red = A.red, RB = red >> 5;
   const int NC = (RB + kChunkBlocks - 1) / kChunkBlocks;
   const int rows_e = kGateUp ? 2 * A.rows : A.rows;
-  const uint8_t* __restrict__ wbase = A.wp + static_cast<size_t>(we.e) * rows_e * (red >> 1);
+  const uint8_t* __restrict__ wbase =
+      kBf16W ? reinterpret_cast<const uint8_t*>(A.wbf) + static_cast<size_t>(we.e) * rows_e * red * 2
+             : A.wp + static_cast<size_t>(we.e) * rows_e * (red >> 1);
   const uint8_t* __restrict__ sbase = A.ws + static_cast<size_t>(we.e) * rows_e * RB;
   const int il = kGateUp ? A.il : 0;                // interleaved w13 rows
-  const uint32_t wo0 = row_offset(kGateUp ? gate_row(wrow, il) : wrow, red >> 1, A.tiled);
-  const uint32_t wo1 = row_offset(up_row(wrow, A.rows, il), red >> 1, A.tiled);
-  const uint32_t bstride = block_stride(A.tiled);
+  const int wr0 = kGateUp ? gate_row(wrow, il) : wrow, wr1 = up_row(wrow, A.rows, il);
+  const uint32_t wo0 = kBf16W ? static_cast<uint32_t>(wr0) * red * 2 : row_offset(wr0, red >> 1, A.tiled);
+  const uint32_t wo1 = kBf16W ? static_cast<uint32_t>(wr1) * red * 2 : row_offset(wr1, red >> 1, A.tiled);
+  const uint32_t bstride = kBf16W ? 64u : block_stride(A.tiled);
   // scale strips of the tile's rows (clamped to the expert), staged in LDS once:
   // [kMfmaRows][RB] (gate/single), then up; interleaved w13: the tile's stored
   // rows (gate, up alternating) in one strip
   const int srows = min(kMfmaRows, A.rows - tile * kMfmaRows);
   unsigned char* sstrip = lds + 2 * kBuf;
   const int strip = kMfmaRows * RB;
-  if (il) {
+  if (kBf16W) {
+    // unpacked weights carry their scales
+  } else if (il) {
     dma_strip(sbase + static_cast<size_t>(2 * tile * kMfmaRows) * RB, sstrip, 2 * srows * RB);
   } else {
     dma_strip(sbase + static_cast<size_t>(tile * kMfmaRows) * RB, sstrip, srows * RB);
@@ -360,11 +371,14 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
       acc1[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    uint4 rw0[kRing], rw1[kRing], rx[kRing][kGroups];
+    uint4 rw0[kRing][kWv], rw1[kRing][kWv], rx[kRing][kGroups];
     auto wload = [&](int c, int slot) {
       const int b = min(c * kChunkBlocks + q, RB - 1);
-      rw0[slot] = *reinterpret_cast<const uint4*>(wbase + wo0 + bstride * b);
-      if (kGateUp) rw1[slot] = *reinterpret_cast<const uint4*>(wbase + wo1 + bstride * b);
+#pragma unroll
+      for (int v = 0; v < kWv; ++v) {
+        rw0[slot][v] = *reinterpret_cast<const uint4*>(wbase + wo0 + bstride * b + 16 * v);
+        if (kGateUp) rw1[slot][v] = *reinterpret_cast<const uint4*>(wbase + wo1 + bstride * b + 16 * v);
+      }
     };
 
     // prologue: chunks 0..kRing-1 in flight, chunk 0 staged in LDS
@@ -385,24 +399,38 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
         const bool valid = c * kChunkBlocks + q < RB;  // false past the row and past the last chunk
         // a zero scale turns a ragged-tail block into zeros
         const int bs = min(c * kChunkBlocks + q, RB - 1);
-        const float sc0 = valid ? e8m0_to_f32(sstrip[srow_l * s0i + bs]) : 0.0f;
-        const float sc1 = (kGateUp && valid) ? e8m0_to_f32(sstrip[s1b + srow_l * s0i + bs]) : 0.0f;
-        const uint32_t d0[4] = {rw0[s].x, rw0[s].y, rw0[s].z, rw0[s].w};
+        const float sc0 = (!kBf16W && valid) ? e8m0_to_f32(sstrip[srow_l * s0i + bs]) : 0.0f;
+        const float sc1 = (!kBf16W && kGateUp && valid) ? e8m0_to_f32(sstrip[s1b + srow_l * s0i + bs]) : 0.0f;
+        const uint32_t d0[4] = {rw0[s][0].x, rw0[s][0].y, rw0[s][0].z, rw0[s][0].w};
         uint32_t d1[4] = {0, 0, 0, 0};
         if (kGateUp) {
-          d1[0] = rw1[s].x;
-          d1[1] = rw1[s].y;
-          d1[2] = rw1[s].z;
-          d1[3] = rw1[s].w;
+          d1[0] = rw1[s][0].x;
+          d1[1] = rw1[s][0].y;
+          d1[2] = rw1[s][0].z;
+          d1[3] = rw1[s][0].w;
+        }
+        uint4 u0[kWv], u1[kWv];
+#pragma unroll
+        for (int v = 0; v < kWv; ++v) {
+          u0[v] = rw0[s][v];
+          u1[v] = kGateUp ? rw1[s][v] : make_uint4(0, 0, 0, 0);
         }
         wload(c + kRing, s);
         const unsigned char* xb = lds + (c & 1) * kBuf + q * 64;
         // decode each 8-value operand right before its MFMAs (keeps few registers live)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const bf16x8 a0 = decode_dword_bf16x8(d0[g], sc0);
-          bf16x8 a1;
-          if (kGateUp) a1 = decode_dword_bf16x8(d1[g], sc1);
+          bf16x8 a0, a1;
+          if constexpr (kBf16W) {
+            // the unpacked values of elements 8g..8g+7 of the block; a block past
+            // the row (clamped load) contributes zeros, as a zero scale does
+            const uint4 z = make_uint4(0, 0, 0, 0);
+            a0 = __builtin_bit_cast(bf16x8, valid ? u0[g] : z);
+            if (kGateUp) a1 = __builtin_bit_cast(bf16x8, valid ? u1[g] : z);
+          } else {
+            a0 = decode_dword_bf16x8(d0[g], sc0);
+            if (kGateUp) a1 = decode_dword_bf16x8(d1[g], sc1);
+          }
 #pragma unroll
           for (int tg = 0; tg < kGroups; ++tg) {
             if (tg < NG) {
@@ -462,12 +490,18 @@ template __global__ void gemv_kernel<true, 16>(ExpertArgs);
 template __global__ void gemv_kernel<true, 32>(ExpertArgs);
 template __global__ void gemv_kernel<false, 16>(ExpertArgs);
 template __global__ void gemv_kernel<false, 32>(ExpertArgs);
-template __global__ void mfma_kernel<true, 1>(ExpertArgs);
-template __global__ void mfma_kernel<true, 2>(ExpertArgs);
-template __global__ void mfma_kernel<true, 4>(ExpertArgs);
-template __global__ void mfma_kernel<false, 1>(ExpertArgs);
-template __global__ void mfma_kernel<false, 2>(ExpertArgs);
-template __global__ void mfma_kernel<false, 4>(ExpertArgs);
+template __global__ void mfma_kernel<true, 1, false>(ExpertArgs);
+template __global__ void mfma_kernel<true, 1, true>(ExpertArgs);
+template __global__ void mfma_kernel<true, 2, false>(ExpertArgs);
+template __global__ void mfma_kernel<true, 2, true>(ExpertArgs);
+template __global__ void mfma_kernel<true, 4, false>(ExpertArgs);
+template __global__ void mfma_kernel<true, 4, true>(ExpertArgs);
+template __global__ void mfma_kernel<false, 1, false>(ExpertArgs);
+template __global__ void mfma_kernel<false, 1, true>(ExpertArgs);
+template __global__ void mfma_kernel<false, 2, false>(ExpertArgs);
+template __global__ void mfma_kernel<false, 2, true>(ExpertArgs);
+template __global__ void mfma_kernel<false, 4, false>(ExpertArgs);
+template __global__ void mfma_kernel<false, 4, true>(ExpertArgs);
 
 // y[t, :] from the per-route down projections (combine4).
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs A) {
@@ -597,6 +631,48 @@ __global__ __launch_bounds__(256) void route_rows_kernel(const float* __restrict
     *dst = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   } else if (!in_place) {
     *dst = *reinterpret_cast<const float4*>(o + static_cast<size_t>(p) * K + k4);
+  }
+}
+
+// Prefill unpack ("MXFP4 MoE decode kernels", Prefill: unpack once): one
+// thread per 32-value block of one expert.  Row layout: consecutive threads
+// take consecutive blocks of a row; tiled layout: consecutive threads take the
+// 16 rows of one block of a 16-row group, so the packed reads stay contiguous
+// either way.  The output is always the row layout, in the stored row order.
+__global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* __restrict__ packed,
+                                                     const uint8_t* __restrict__ scales, int rows, int cols,
+                                                     int tiled, const int32_t* __restrict__ counts,
+                                                     uint16_t* __restrict__ out) {
+  const int e = blockIdx.y;
+  if (counts != nullptr && counts[e] == 0) return;  // an untouched expert: nothing written
+  const int RB = cols >> 5;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(rows) * RB) return;
+  int n, b;
+  if (tiled) {
+    const int64_t gb = i >> 4;  // (group, block) pair
+    n = static_cast<int>(gb / RB) * 16 + static_cast<int>(i & 15);
+    b = static_cast<int>(gb % RB);
+  } else {
+    n = static_cast<int>(i / RB);
+    b = static_cast<int>(i % RB);
+  }
+  const uint32_t row_bytes = static_cast<uint32_t>(cols >> 1);
+  const uint8_t* pe = packed + static_cast<size_t>(e) * rows * row_bytes;
+  const uint4 q = *reinterpret_cast<const uint4*>(pe + row_offset(n, row_bytes, tiled) + block_stride(tiled) * b);
+  const size_t row = static_cast<size_t>(e) * rows + n;
+  const float s = e8m0_to_f32(scales[row * RB + b]);
+  bf16x2 v[16];
+  decode_block_bf16(q, s, v);
+  uint4* o = reinterpret_cast<uint4*>(out + row * cols + 32 * static_cast<size_t>(b));
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint4 u;
+    u.x = __builtin_bit_cast(uint32_t, v[4 * c + 0]);
+    u.y = __builtin_bit_cast(uint32_t, v[4 * c + 1]);
+    u.z = __builtin_bit_cast(uint32_t, v[4 * c + 2]);
+    u.w = __builtin_bit_cast(uint32_t, v[4 * c + 3]);
+    o[c] = u;
   }
 }
 

@@ -69,6 +69,7 @@ struct PlanArgs {
   const float* w_in;       // caller's weights to copy into the workspace (ids mode), or nullptr
   int T, top_k, E_global, E_local, offset, scoring;
   int mfma_enabled;        // the MFMA kernels run for this call (T > kGemvMaxTokens); else all experts go to GEMV
+  int gemv_max;            // with mfma_enabled: experts with more routes than this go to the MFMA list
   int lists;               // build the GEMV / MFMA work lists (some projection uses the list kernels)
   int32_t* ids_ws;         // [R] routed ids (logits mode)
   float* weights_ws;       // [R] routing weights
@@ -113,6 +114,7 @@ struct ExpertArgs {
   int rows;                // output rows per expert: I row pairs (gate/up) or K (down)
   int tiled;               // packed weights in the tiled layout
   int il;                  // gate/up: w13 rows interleaved (gate_row / up_row)
+  const uint16_t* wbf;     // prefill: the weights unpacked to bf16 [E_l][rows_e][red] (MFMA kernel), else nullptr
   uint16_t* a_out;         // gate/up output [R, I] bf16
   float* o_out;            // down output [R, K] fp32
   int act_kind;
@@ -191,9 +193,15 @@ __global__ void plan_kernel(PlanArgs P);
 // a workgroup of 256 lanes covers 256 / kLanesPerRow rows of one expert.
 template <bool kGateUp, int kLanesPerRow>
 __global__ void gemv_kernel(ExpertArgs A);
-// MFMA regime: 64 rows of one expert per workgroup, kGroups groups of 16 tokens per pass.
-template <bool kGateUp, int kGroups>
+// MFMA regime: 64 rows of one expert per workgroup, kGroups groups of 16 tokens per pass;
+// kBf16W reads the bf16-unpacked weights (prefill) instead of decoding MXFP4.
+template <bool kGateUp, int kGroups, bool kBf16W>
 __global__ void mfma_kernel(ExpertArgs A);
+// Prefill unpack: packed [E_l][rows][cols/2] (row or tiled layout) + scales
+// -> bf16 [E_l][rows][cols] in the row layout, for the experts with
+// counts[e] > 0 (all when counts is nullptr); grid (ceil(rows * cols/32 / 256), E_l).
+__global__ void unpack_kernel(const uint8_t* packed, const uint8_t* scales, int rows, int cols, int tiled,
+                              const int32_t* counts, uint16_t* out);
 // Decode regime: kSplit waves share one 16-row sub-tile and split the
 // reduction (kSplit = 4, 2 or 1 for up to 4, 8 or 16 routes per pass); with
 // kPair (down projection, rows % 32 == 0) a wave's sub-tile is 32 rows.

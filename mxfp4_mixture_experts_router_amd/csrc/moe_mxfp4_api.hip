@@ -153,6 +153,7 @@ moe::PlanArgs plan_args(const moe_mxfp4_desc& d, void* ws) {
   P.offset = d.expert_offset;
   P.scoring = d.scoring;
   P.mfma_enabled = mfma_enabled(d) ? 1 : 0;
+  P.gemv_max = moe::kGemvMaxTokens;
   P.lists = 1;
   P.ids_ws = at<int32_t>(ws, L.ids);
   P.weights_ws = at<float>(ws, L.weights);
@@ -167,11 +168,16 @@ moe::PlanArgs plan_args(const moe_mxfp4_desc& d, void* ws) {
 }
 
 // Routing and bucketing into the workspace.  Small calls route inside the
-// plan kernel; larger ones route with one wave per token first.
+// plan kernel; larger ones route with one wave per token first.  The prefill
+// path puts every touched expert in the MFMA list and needs no pass list.
 void enqueue_plan(const moe_mxfp4_desc& d, const float* logits, const int32_t* ids, const float* wts, void* ws,
-                  hipStream_t s) {
+                  hipStream_t s, bool prefill = false) {
   moe::PlanArgs P = plan_args(d, ws);
-  const int split = stream_split(d);
+  const int split = prefill ? 0 : stream_split(d);
+  if (prefill) {
+    P.mfma_enabled = 1;
+    P.gemv_max = 0;
+  }
   if (split > 0) {
     P.passes = at<moe::PassEntry>(ws, make_layout(d).passes);
     P.pass_shift = split == 4 ? 2 : (split == 2 ? 3 : 4);  // kStreamPassTokens / split routes per pass
@@ -240,14 +246,60 @@ void enqueue_expert_pair(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs 
                        static_cast<size_t>(gate_up ? 2 : 1) * moe::kMfmaRows * (red / 32);
     const dim3 g(static_cast<unsigned>(grid));
     if (gate_up) {
-      if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<true, 1>), g, dim3(256), lds, s, M);
-      else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<true, 2>), g, dim3(256), lds, s, M);
-      else hipLaunchKernelGGL((moe::mfma_kernel<true, 4>), g, dim3(256), lds, s, M);
+      if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<true, 1, false>), g, dim3(256), lds, s, M);
+      else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<true, 2, false>), g, dim3(256), lds, s, M);
+      else hipLaunchKernelGGL((moe::mfma_kernel<true, 4, false>), g, dim3(256), lds, s, M);
     } else {
-      if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<false, 1>), g, dim3(256), lds, s, M);
-      else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<false, 2>), g, dim3(256), lds, s, M);
-      else hipLaunchKernelGGL((moe::mfma_kernel<false, 4>), g, dim3(256), lds, s, M);
+      if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<false, 1, false>), g, dim3(256), lds, s, M);
+      else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<false, 2, false>), g, dim3(256), lds, s, M);
+      else hipLaunchKernelGGL((moe::mfma_kernel<false, 4, false>), g, dim3(256), lds, s, M);
     }
+  }
+}
+
+// Prefill: the touched experts' weights, unpacked to bf16 in the workspace
+// past the decode layout (w13 [E_l][2I][K], then w2 [E_l][K][I]).
+struct PrefillLayout {
+  size_t w13, w2, total;
+};
+PrefillLayout prefill_layout(const moe_mxfp4_desc& d) {
+  PrefillLayout P;
+  P.w13 = make_layout(d).total;
+  P.w2 = align_up(P.w13 + static_cast<size_t>(d.E_local) * 2 * d.I * d.K * 2, 256);
+  P.total = align_up(P.w2 + static_cast<size_t>(d.E_local) * d.K * d.I * 2, 256);
+  return P;
+}
+
+void enqueue_unpack(const moe_mxfp4_desc& d, const uint8_t* w13p, const uint8_t* w13s, const uint8_t* w2p,
+                    const uint8_t* w2s, const int32_t* counts, uint16_t* w13_out, uint16_t* w2_out, hipStream_t s) {
+  const int tiled = d.weight_layout == MOE_LAYOUT_TILE16;
+  const int64_t b13 = static_cast<int64_t>(2) * d.I * (d.K / 32), b2 = static_cast<int64_t>(d.K) * (d.I / 32);
+  hipLaunchKernelGGL(moe::unpack_kernel, dim3(static_cast<unsigned>((b13 + 255) / 256), d.E_local), dim3(256), 0, s,
+                     w13p, w13s, 2 * d.I, d.K, tiled, counts, w13_out);
+  hipLaunchKernelGGL(moe::unpack_kernel, dim3(static_cast<unsigned>((b2 + 255) / 256), d.E_local), dim3(256), 0, s,
+                     w2p, w2s, d.K, d.I, tiled, counts, w2_out);
+}
+
+// The MFMA kernel on the unpacked weights for every touched expert (the plan
+// of the prefill path lists them all).
+void enqueue_mfma_bf16(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs M, const Layout& L, void* ws,
+                       hipStream_t s) {
+  const int64_t R = static_cast<int64_t>(d.T) * d.top_k;
+  const int64_t experts = std::min<int64_t>(d.E_local, R);
+  M.list = at<moe::WorkEntry>(ws, L.mfma_list);
+  const int64_t grid = std::max<int64_t>(1, experts * ((M.rows + moe::kMfmaRows - 1) / moe::kMfmaRows));
+  const int groups = d.T <= 32 ? 1 : (d.T <= 64 ? 2 : 4);
+  const size_t lds = 2 * static_cast<size_t>(16 * groups) * moe::kXRowBytes +
+                     static_cast<size_t>(gate_up ? 2 : 1) * moe::kMfmaRows * (M.red / 32);
+  const dim3 g(static_cast<unsigned>(grid));
+  if (gate_up) {
+    if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<true, 1, true>), g, dim3(256), lds, s, M);
+    else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<true, 2, true>), g, dim3(256), lds, s, M);
+    else hipLaunchKernelGGL((moe::mfma_kernel<true, 4, true>), g, dim3(256), lds, s, M);
+  } else {
+    if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<false, 1, true>), g, dim3(256), lds, s, M);
+    else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<false, 2, true>), g, dim3(256), lds, s, M);
+    else hipLaunchKernelGGL((moe::mfma_kernel<false, 4, true>), g, dim3(256), lds, s, M);
   }
 }
 
@@ -475,6 +527,93 @@ int moe_mxfp4_decode_routes(const moe_mxfp4_desc* desc, const uint16_t* x, const
   enqueue_plan(d, router_logits, topk_ids, topk_weights, workspace, s);
   enqueue_w13(d, x, w13_packed, w13_scales, w13_bias, nullptr, workspace, s);
   enqueue_w2(d, nullptr, w2_packed, w2_scales, w2_bias, nullptr, out_routes, workspace, s);
+  return launch_status();
+}
+
+int moe_mxfp4_prefill_workspace_bytes(const moe_mxfp4_desc* desc, size_t* bytes) {
+  const int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (bytes == nullptr) return MOE_ERR_NULL;
+  *bytes = prefill_layout(*desc).total;
+  return MOE_OK;
+}
+
+int moe_mxfp4_prefill(const moe_mxfp4_desc* desc, const uint16_t* x, const float* router_logits,
+                      const int32_t* topk_ids, const float* topk_weights, const uint8_t* w13_packed,
+                      const uint8_t* w13_scales, const uint16_t* w13_bias, const uint8_t* w2_packed,
+                      const uint8_t* w2_scales, const uint16_t* w2_bias, uint16_t* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const moe_mxfp4_desc& d = *desc;
+  if ((st = check_routing(d, router_logits, topk_ids, topk_weights)) != MOE_OK) return st;
+  if (d.T == 0) return MOE_OK;
+  if (!x || !w13_packed || !w13_scales || !w2_packed || !w2_scales || !out) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w13_packed) || !aligned16(w2_packed) || !aligned16(out) || !aligned16(w13_scales) ||
+      !aligned16(w2_scales) || !aligned16(w13_bias) || !aligned16(w2_bias))
+    return MOE_ERR_ALIGN;
+  if (workspace == nullptr) return MOE_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MOE_ERR_ALIGN;
+  const PrefillLayout PL = prefill_layout(d);
+  if (workspace_bytes < PL.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Layout L = make_layout(d);
+  uint16_t* w13u = at<uint16_t>(workspace, PL.w13);
+  uint16_t* w2u = at<uint16_t>(workspace, PL.w2);
+  enqueue_plan(d, router_logits, topk_ids, topk_weights, workspace, s, true);
+  enqueue_unpack(d, w13_packed, w13_scales, w2_packed, w2_scales, at<int32_t>(workspace, L.counts), w13u, w2u, s);
+  moe::ExpertArgs A{};
+  A.in = x;
+  A.routes = at<int32_t>(workspace, L.routes);
+  A.top_k = d.top_k;
+  A.ws = w13_scales;
+  A.bias = w13_bias;
+  A.plan = at<Plan>(workspace, L.plan);
+  A.red = d.K;
+  A.rows = d.I;
+  A.il = d.w13_order == MOE_W13_INTERLEAVED;
+  A.wbf = w13u;
+  A.a_out = at<uint16_t>(workspace, L.a);
+  A.act_kind = d.activation;
+  A.alpha = d.swiglu_alpha;
+  A.limit = d.swiglu_limit;
+  enqueue_mfma_bf16(d, true, A, L, workspace, s);
+  moe::ExpertArgs B{};
+  B.in = A.a_out;
+  B.top_k = d.top_k;
+  B.ws = w2_scales;
+  B.bias = w2_bias;
+  B.plan = A.plan;
+  B.red = d.I;
+  B.rows = d.K;
+  B.wbf = w2u;
+  B.o_out = at<float>(workspace, L.o);
+  enqueue_mfma_bf16(d, false, B, L, workspace, s);
+  moe::CombineArgs C;
+  C.o = B.o_out;
+  C.pos = at<int32_t>(workspace, L.pos);
+  C.weights = at<float>(workspace, L.weights);
+  C.out = out;
+  C.T = d.T;
+  C.K = d.K;
+  C.top_k = d.top_k;
+  C.by_route = 0;
+  hipLaunchKernelGGL(moe::combine_kernel, dim3((d.K / 4 + 255) / 256, d.T), dim3(256), 0, s, C);
+  return launch_status();
+}
+
+int moe_mxfp4_unpack(const moe_mxfp4_desc* desc, const uint8_t* w13_packed, const uint8_t* w13_scales,
+                     const uint8_t* w2_packed, const uint8_t* w2_scales, uint16_t* w13_out, uint16_t* w2_out,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (desc->T == 0) return MOE_OK;
+  if (!w13_packed || !w13_scales || !w2_packed || !w2_scales || !w13_out || !w2_out) return MOE_ERR_NULL;
+  if (!aligned16(w13_packed) || !aligned16(w2_packed) || !aligned16(w13_out) || !aligned16(w2_out))
+    return MOE_ERR_ALIGN;
+  if ((st = check_workspace(*desc, workspace, workspace_bytes)) != MOE_OK) return st;
+  enqueue_unpack(*desc, w13_packed, w13_scales, w2_packed, w2_scales,
+                 at<int32_t>(workspace, make_layout(*desc).counts), w13_out, w2_out, static_cast<hipStream_t>(stream));
   return launch_status();
 }
 

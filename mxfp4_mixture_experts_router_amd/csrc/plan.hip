@@ -357,7 +357,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
     for (int e0 = 0; e0 < E_l; e0 += 64) {
       const int e = e0 + lane;
       const int cnt = e < E_l ? base_e[e + 1] - base_e[e] : 0;
-      const bool hm = P.mfma_enabled && cnt > kGemvMaxTokens;
+      const bool hm = P.mfma_enabled && cnt > P.gemv_max;
       const bool hg = cnt > 0 && !hm;
       const uint64_t lt = (1ull << lane) - 1ull;
       const uint64_t mg = __ballot(hg);

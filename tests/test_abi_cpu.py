@@ -152,6 +152,35 @@ def test_route_output_error_paths():
     assert down(ctypes.byref(_desc(T=0)), None, A, A, None, None, A, 1 << 40, None) == E.MOE_OK
 
 
+def test_prefill_and_unpack_error_paths():
+    d = _desc()
+    E, L = _lib, _lib.lib()
+    n = ctypes.c_size_t(0)
+    assert L.moe_mxfp4_prefill_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == E.MOE_OK
+    _, dec = _ws_bytes(d)
+    assert n.value >= dec + d.E_local * 3 * d.I * d.K * 2
+    pf = L.moe_mxfp4_prefill
+
+    def call(**kw):
+        a = dict(x=A, logits=A, ids=None, wts=None, w13p=A, w13s=A, b13=None, w2p=A, w2s=A, b2=None,
+                 out=A, ws=A, ws_bytes=n.value)
+        a.update(kw)
+        return pf(ctypes.byref(kw.pop("desc", d)), a["x"], a["logits"], a["ids"], a["wts"], a["w13p"], a["w13s"],
+                  a["b13"], a["w2p"], a["w2s"], a["b2"], a["out"], a["ws"], a["ws_bytes"], None)
+
+    assert call(ws_bytes=dec) == E.MOE_ERR_WORKSPACE          # the decode workspace is too small here
+    assert call(ws=None) == E.MOE_ERR_WORKSPACE
+    assert call(ws=A_MIS) == E.MOE_ERR_ALIGN
+    assert call(logits=None) == E.MOE_ERR_MODE
+    assert call(out=None) == E.MOE_ERR_NULL
+    assert call(w2p=A_MIS) == E.MOE_ERR_ALIGN
+    un = L.moe_mxfp4_unpack
+    assert un(ctypes.byref(d), A, A, A, A, None, A, A, 1 << 40, None) == E.MOE_ERR_NULL
+    assert un(ctypes.byref(d), A, A, A, A, A_MIS, A, A, 1 << 40, None) == E.MOE_ERR_ALIGN
+    assert un(ctypes.byref(d), A, A, A, A, A, A, A, dec - 1, None) == E.MOE_ERR_WORKSPACE
+    assert un(ctypes.byref(_desc(T=0)), None, None, None, None, None, None, None, 0, None) == E.MOE_OK
+
+
 def test_tile_weights_error_paths():
     L, E = _lib.lib(), _lib
     assert L.moe_mxfp4_tile_weights(A, 24, 64, 0, None) == E.MOE_ERR_SHAPE      # rows not a multiple of 16

@@ -499,6 +499,81 @@ def test_route_outputs_match_oracle(case):
     assert oracle.rel_l2(y, ysum) <= 3e-3, name
 
 
+# prefill path: unpack the touched experts to bf16, then bf16 MFMA GEMMs
+@pytest.mark.parametrize("layout", ["rows", "tile16"])
+def test_unpack_touched_experts_bit_exact(layout):
+    t = torch()
+    cfg = _cfg(K=544, I=320, E_global=8, E_local=6, expert_offset=1, top_k=2)
+    w = make_weights(cfg)
+    inp = make_topk_inputs(cfg, 3, seed=5)
+    d = desc_for(cfg, 3, weight_layout=layout)
+    layer = DeviceLayer(w, layout=layout)
+    ws = moe.moe_mxfp4_plan(d, topk_ids=dev_i32(inp.topk_ids), topk_weights=dev_f32(inp.topk_weights))
+    sentinel = 0x7FBF                                   # a NaN pattern the unpack never writes
+    w13o = t.full((cfg.E_local, 2 * cfg.I, cfg.K), 0, dtype=t.int16, device="cuda")
+    w2o = t.full((cfg.E_local, cfg.K, cfg.I), 0, dtype=t.int16, device="cuda")
+    w13o.fill_(sentinel)
+    w2o.fill_(sentinel)
+    moe.moe_mxfp4_unpack(d, layer.w13p, layer.w13s, layer.w2p, layer.w2s, w13o.view(t.bfloat16),
+                         w2o.view(t.bfloat16), ws)
+    t.cuda.synchronize()
+    g13 = w13o.cpu().numpy().view(np.uint16)
+    g2 = w2o.cpu().numpy().view(np.uint16)
+    ids = inp.topk_ids.ravel()
+    touched = {int(i) - cfg.expert_offset for i in ids if cfg.expert_offset <= i < cfg.expert_offset + cfg.E_local}
+    assert 0 < len(touched) < cfg.E_local
+    for e in range(cfg.E_local):
+        if e in touched:
+            assert np.array_equal(g13[e], oracle.unpack_bf16(w.w13_packed[e], w.w13_scales[e])), e
+            assert np.array_equal(g2[e], oracle.unpack_bf16(w.w2_packed[e], w.w2_scales[e])), e
+        else:
+            assert (g13[e] == sentinel).all() and (g2[e] == sentinel).all(), e
+
+
+def _run_prefill(cfg, layer, inp, w13_order="gate_up"):
+    t = torch()
+    T = inp.x.shape[0]
+    d = desc_for(cfg, T, E_local=layer.E_local, weight_layout=layer.layout, w13_order=w13_order)
+    out = t.full((T, cfg.K), float("nan"), dtype=t.bfloat16, device="cuda")
+    kw = {"router_logits": dev_f32(inp.logits)} if inp.logits is not None else {
+        "topk_ids": dev_i32(inp.topk_ids), "topk_weights": dev_f32(inp.topk_weights)}
+    moe.moe_mxfp4_prefill(d, dev_bf16(inp.x), layer.w13p, layer.w13s, layer.w2p, layer.w2s, out,
+                          w13_bias=layer.b13, w2_bias=layer.b2, **kw)
+    t.cuda.synchronize()
+    return out
+
+
+PREFILL_CASES = [
+    # (name, config, T, layout, w13 order, decode takes the MFMA path for every touched expert)
+    ("mfma-both", dict(K=1024, I=512, E_global=16, E_local=8, expert_offset=4, top_k=4, scoring="sigmoid"),
+     96, "rows", "gate_up", True),
+    ("mfma-both-tiled-il", dict(K=768, I=1056, E_global=4, E_local=4, top_k=2, activation="swiglu_oai", bias=True,
+                                scale_lo=115, scale_hi=127), 80, "tile16", "interleaved", True),
+    ("groups4-ragged", dict(K=544, I=608, E_global=2, E_local=2, top_k=2, bias=True), 300, "rows", "gate_up", True),
+    ("small-T", dict(K=1120, I=1056, E_global=8, E_local=4, expert_offset=2, top_k=2, bias=True), 6, "tile16",
+     "gate_up", False),
+    ("tiny", dict(), 4, "rows", "gate_up", False),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PREFILL_CASES)))
+def test_prefill_matches_oracle_and_decode(case):
+    name, kw, T, layout, order, same_path = PREFILL_CASES[case]
+    cfg = _cfg(**kw)
+    w = make_weights(cfg)
+    if order == "interleaved":
+        w = _interleaved_weights(w, cfg.I)
+    inp = make_inputs(cfg, T, t_index=case)
+    layer = DeviceLayer(w, layout=layout)
+    y = _run_prefill(cfg, layer, inp, order)
+    ref = oracle.moe_forward_cfg(cfg, w, inp, w13_order=order)
+    _assert_close(bf16_to_np(y), ref["y"], name)
+    if same_path:
+        assert int(ref["counts"][ref["counts"] > 0].min()) > 2, name   # decode's MFMA regime for every expert
+        yd = run_decode(cfg, layer, inp, w13_order=order)
+        assert np.array_equal(bf16_bits_np(y), bf16_bits_np(yd)), name
+
+
 def test_layer_ids_mode_with_padding_and_foreign_ids():
     cfg = _cfg(K=2880, I=2880, E_global=32, E_local=5, expert_offset=3, top_k=4, activation="swiglu_oai",
                bias=True, scale_lo=115, scale_hi=127)
