@@ -289,11 +289,17 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
   extern __shared__ __align__(16) unsigned char lds[];  // [2][kTokens][kXRowBytes], then the scale strips
 
   const int tiles = (A.rows + kMfmaRows - 1) / kMfmaRows;
-  const int item = blockIdx.x / tiles;         // < E_local: the entry load is always in bounds
+  // XCD-aware order: block b runs on XCD b % 8, so XCD x takes list entries
+  // x, x + 8, ..., each with all of its row tiles in dispatch order.  The
+  // tiles of one expert then stage the same activation rows through one L2
+  // (a few experts at a time per XCD), instead of every XCD reading every
+  // expert's rows.  The host pads the grid to 8 * tiles * ceil(experts / 8).
+  const int xcd = static_cast<int>(blockIdx.x) & 7, kx = static_cast<int>(blockIdx.x) >> 3;
+  const int item = xcd + 8 * (kx / tiles);
+  const int tile = kx - (kx / tiles) * tiles;
   const int n_items = A.plan->n_mfma;
-  const WorkEntry we = A.list[item];
+  const WorkEntry we = A.list[min(item, A.list_cap - 1)];  // in bounds; used only when item < n_items
   if (item >= n_items) return;  // whole workgroup
-  const int tile = blockIdx.x - item * tiles;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, q = lane >> 4;
   const int wrow0 = tile * kMfmaRows + wave * 16;

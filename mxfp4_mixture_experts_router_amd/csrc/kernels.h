@@ -109,6 +109,7 @@ struct ExpertArgs {
   const uint8_t* ws;       // scales
   const uint16_t* bias;    // bf16 bias or nullptr
   const WorkEntry* list;   // the kernel's expert list
+  int list_cap;            // entries the list has room for (E_local)
   const Plan* plan;
   int red;                 // reduction length: K (gate/up) or I (down)
   int rows;                // output rows per expert: I row pairs (gate/up) or K (down)

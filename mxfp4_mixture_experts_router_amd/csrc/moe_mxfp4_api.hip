@@ -240,7 +240,8 @@ void enqueue_expert_pair(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs 
   if (mfma_experts > 0 && mfma_enabled(d)) {
     moe::ExpertArgs M = A;
     M.list = at<moe::WorkEntry>(ws, L.mfma_list);
-    const int64_t grid = mfma_experts * ((rows + moe::kMfmaRows - 1) / moe::kMfmaRows);
+    M.list_cap = d.E_local;
+    const int64_t grid = (mfma_experts + 7) / 8 * 8 * ((rows + moe::kMfmaRows - 1) / moe::kMfmaRows);
     const int groups = d.T <= 32 ? 1 : (d.T <= 64 ? 2 : 4);
     const size_t lds = 2 * static_cast<size_t>(16 * groups) * moe::kXRowBytes +
                        static_cast<size_t>(gate_up ? 2 : 1) * moe::kMfmaRows * (red / 32);
@@ -287,7 +288,8 @@ void enqueue_mfma_bf16(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs M,
   const int64_t R = static_cast<int64_t>(d.T) * d.top_k;
   const int64_t experts = std::min<int64_t>(d.E_local, R);
   M.list = at<moe::WorkEntry>(ws, L.mfma_list);
-  const int64_t grid = std::max<int64_t>(1, experts * ((M.rows + moe::kMfmaRows - 1) / moe::kMfmaRows));
+  M.list_cap = d.E_local;
+  const int64_t grid = std::max<int64_t>(1, (experts + 7) / 8 * 8 * ((M.rows + moe::kMfmaRows - 1) / moe::kMfmaRows));
   const int groups = d.T <= 32 ? 1 : (d.T <= 64 ? 2 : 4);
   const size_t lds = 2 * static_cast<size_t>(16 * groups) * moe::kXRowBytes +
                      static_cast<size_t>(gate_up ? 2 : 1) * moe::kMfmaRows * (M.red / 32);
