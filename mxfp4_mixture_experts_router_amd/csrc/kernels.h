@@ -36,10 +36,10 @@ struct WorkEntry {
 };
 static_assert(sizeof(WorkEntry) == 32, "WorkEntry is 32 bytes");
 
-// Decode regime (T <= kStreamMaxTokens): one persistent kernel per
-// projection walks work items (expert pass x row tile).  A pass is up to
-// kStreamPassTokens routes of one expert; the plan kernel lists the passes of
-// every touched expert in expert order.
+// Stream regime (T <= kStreamMaxTokens, or few routes per expert; the host
+// decides): one persistent kernel per projection walks work items (expert
+// pass x row tile).  A pass is up to kStreamPassTokens routes of one expert;
+// the plan kernel lists the passes of every touched expert in expert order.
 constexpr int kStreamMaxTokens = 64;
 constexpr int kStreamPassTokens = 16;
 

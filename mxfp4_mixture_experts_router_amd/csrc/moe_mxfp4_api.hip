@@ -19,6 +19,8 @@ namespace {
 using moe::Plan;
 
 
+bool stream_regime(const moe_mxfp4_desc& d);
+
 struct Layout {
   size_t plan, ids, weights, counts, offsets, gemv_list, mfma_list, passes, routes, pos, a, o, total;
 };
@@ -42,7 +44,7 @@ Layout make_layout(const moe_mxfp4_desc& d) {
   L.gemv_list = take(static_cast<size_t>(d.E_local) * sizeof(moe::WorkEntry));
   L.mfma_list = take(static_cast<size_t>(d.E_local) * sizeof(moe::WorkEntry));
   // decode regime: at most one pass per route
-  L.passes = take(d.T <= moe::kStreamMaxTokens ? R * sizeof(moe::PassEntry) : 0);
+  L.passes = take(stream_regime(d) ? R * sizeof(moe::PassEntry) : 0);
   L.routes = take(R * 4);
   L.pos = take(R * 4);
   L.a = take(R * d.I * 2);
@@ -96,17 +98,34 @@ int tokens_bound(const moe_mxfp4_desc& d) {
 // kernel and the launches below apply the same rule.
 bool mfma_enabled(const moe_mxfp4_desc& d) { return d.T > moe::kGemvMaxTokens; }
 
-// Decode regime (T <= kStreamMaxTokens): the persistent stream kernel, whose
-// waves split the reduction kSplit ways with 16/kSplit routes per pass.  The
-// split follows T (4 up to 4 tokens, 2 up to 8, else 1) and is lowered until
-// every slice of both projections has at least kStreamRing steps; a
-// projection whose reduction is still too short for that uses the
-// GEMV/MFMA list kernels.
+// Stream regime: the persistent stream kernel, whose waves split the
+// reduction kSplit ways with 16/kSplit routes per pass.  It serves every call
+// with T <= kStreamMaxTokens, and larger calls while the routes per local
+// expert, expected under uniform routing (T * top_k / E_global), stay within
+// kStreamRoutesPerExpert: each pass of 16 routes streams its expert's weights
+// again, so calls with many routes per expert belong to the MFMA kernel (64
+// routes per weight pass).  Measured on the wide-K slice (48 of 384 experts,
+// top-8): 5 routes per expert (T = 256) run 1.4x faster here than on the
+// GEMV/MFMA lists, 43 (T = 2048) 1.5x slower.  A pass entry's route index is
+// 16-bit, hence T * top_k < 65536.
+// The split follows T (4 up to 4 tokens, 2 up to 8, else 1) and is lowered
+// until every slice of both projections has at least kStreamRing steps; a
+// projection whose reduction is still too short for that uses the GEMV/MFMA
+// list kernels.
+constexpr int kStreamRoutesPerExpert = 16;
+
+bool stream_regime(const moe_mxfp4_desc& d) {
+  if (d.T < 1) return false;
+  if (d.T <= moe::kStreamMaxTokens) return true;
+  const int64_t R = static_cast<int64_t>(d.T) * d.top_k;
+  return R < 65536 && R <= static_cast<int64_t>(kStreamRoutesPerExpert) * d.E_global;
+}
+
 int steps_per_slice(int red, int split) { return ((red / 32 + 3) / 4 + split - 1) / split; }
 bool stream_fits(int red, int split) { return split > 0 && steps_per_slice(red, split) >= moe::kStreamRing; }
 
 int stream_split(const moe_mxfp4_desc& d) {
-  if (d.T < 1 || d.T > moe::kStreamMaxTokens) return 0;
+  if (!stream_regime(d)) return 0;
   int split = d.T <= 4 ? 4 : (d.T <= 8 ? 2 : 1);
   while (split > 1 && !(stream_fits(d.K, split) && stream_fits(d.I, split))) split /= 2;
   return split;

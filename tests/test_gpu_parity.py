@@ -348,6 +348,12 @@ LAYER_CASES = [
     ("stream-gate-up-only", dict(K=2048, I=256, E_global=4, E_local=4, top_k=2, bias=True), 3, 1.0),
     ("stream-slice-sigmoid", dict(K=6144, I=2048, E_global=64, E_local=8, expert_offset=16, top_k=8,
                                   scoring="sigmoid", scale_lo=115, scale_hi=127), 32, 1.0),
+    # T > 64 with few routes per expert (T * top_k <= 16 * E_global): still the stream kernel,
+    # routing in its own kernel, passes of 16 routes, an expert with several passes
+    ("stream-regime-large-T", dict(K=512, I=768, E_global=64, E_local=16, expert_offset=8, top_k=2, bias=True,
+                                   activation="swiglu_oai"), 200, 1.0),
+    ("stream-regime-large-T-sigmoid", dict(K=1024, I=512, E_global=32, E_local=32, top_k=4, scoring="sigmoid"),
+     128, 1.0),
 ]
 
 
