@@ -104,7 +104,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this layer slice runs on a single MI355X "
-              f"(--gpus {args.gpus} is not supported; expert-parallel sharding is described in DESIGN.md)",
+              f"(--gpus {args.gpus} is not supported: a G-GPU job runs this call on each GPU's slice of "
+              f"E_global / G experts and sums the partial outputs with one all-reduce)",
               file=sys.stderr)
         sys.exit(2)
 

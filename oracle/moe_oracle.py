@@ -30,7 +30,7 @@ Sources (page title, then section):
   weights and a bf16 intermediate, rounded to bf16 once.
 * "GLM-5.3-Flash on Gaudi 2", Why (model table): top-8 sigmoid scoring.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 
 * E2M1 magnitudes are the OCP table {0, 0.5, 1, 1.5, 2, 3, 4, 6}, bit 3 the
   sign; code 8 decodes to -0.0.
