@@ -94,7 +94,9 @@ extern "C" {
 
 /* ---- layer descriptor --------------------------------------------------- */
 typedef struct moe_mxfp4_desc {
-    int32_t T;              /* tokens in the call, >= 0 (T = 0 is a no-op)               */
+    int32_t T;              /* tokens in the call, >= 0 (T = 0 is a no-op); T * top_k
+                               <= 2^24, and x (T * K) and the intermediate
+                               (T * top_k * I, bf16) each below 2 GiB                   */
     int32_t K;              /* hidden size, multiple of 32, 32..8192                      */
     int32_t I;              /* intermediate size per expert, multiple of 32, 32..8192     */
     int32_t E_global;       /* experts the router scores, >= 1 (<= 1024 with logits)     */

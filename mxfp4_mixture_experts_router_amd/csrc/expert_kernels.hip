@@ -69,6 +69,13 @@ __device__ __forceinline__ void dma_strip(const uint8_t* __restrict__ src, unsig
   }
 }
 
+constexpr uint32_t kOob = 0x80000000u;  // buffer offset past every range: the load returns zeros
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const __attribute__((ext_vector_type(4))) uint32_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
@@ -308,9 +315,17 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
   const int red = A.red, RB = red >> 5;
   const int NC = (RB + kChunkBlocks - 1) / kChunkBlocks;
   const int rows_e = kGateUp ? 2 * A.rows : A.rows;
+  // weights of expert we.e and the activation rows through buffer resources:
+  // blocks past a row and pieces of tokens past the pass use an out-of-range
+  // offset and read zeros (no clamping, no masks)
+  const uint32_t expert_bytes = static_cast<uint32_t>(rows_e) * static_cast<uint32_t>(kBf16W ? red * 2 : red >> 1);
   const uint8_t* __restrict__ wbase =
-      kBf16W ? reinterpret_cast<const uint8_t*>(A.wbf) + static_cast<size_t>(we.e) * rows_e * red * 2
-             : A.wp + static_cast<size_t>(we.e) * rows_e * (red >> 1);
+      kBf16W ? reinterpret_cast<const uint8_t*>(A.wbf) + static_cast<size_t>(we.e) * expert_bytes
+             : A.wp + static_cast<size_t>(we.e) * expert_bytes;
+  const __amdgpu_buffer_rsrc_t wrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wbase), 0, expert_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A.in), 0, A.in_bytes, 0x00020000);
   const uint8_t* __restrict__ sbase = A.ws + static_cast<size_t>(we.e) * rows_e * RB;
   const int il = kGateUp ? A.il : 0;                // interleaved w13 rows
   const int wr0 = kGateUp ? gate_row(wrow, il) : wrow, wr1 = up_row(wrow, A.rows, il);
@@ -339,34 +354,30 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
     const int NG = (nt + 15) >> 4;
 
     // staging role: uint4 piece u = tid + 256*k of the chunk's [kTokens][16]
-    // pieces.  Loads are unconditional (tokens past the pass read the first
-    // token's row, chunks past the row read the last chunk); the mask is
-    // applied when the piece is written to LDS.
-    const uint4* srow[kGroups];
-    int spiece[kGroups];
-    bool stok[kGroups];
+    // pieces (group k < NG only: the MFMAs read no column group past the
+    // pass).  Pieces of tokens past the pass and of blocks past the row read
+    // zeros through an out-of-range offset.
+    uint32_t sxoff[kGroups];
+    const int spiece = tid & 15;
 #pragma unroll
     for (int k = 0; k < kGroups; ++k) {
-      const int u = tid + 256 * k;
-      const int st = u >> 4;
-      spiece[k] = u & 15;
-      stok[k] = st < nt;
+      const int st = (tid + 256 * k) >> 4;
       const int p = we.p0 + tp0 + (st < nt ? st : 0);
       const int row = A.routes != nullptr ? A.routes[p] / A.top_k : p;
-      srow[k] = reinterpret_cast<const uint4*>(A.in + static_cast<size_t>(row) * red);
+      sxoff[k] = st < nt ? static_cast<uint32_t>(row) * static_cast<uint32_t>(red) * 2u : kOob;
     }
-    const int last_piece = (red >> 3) - 1;  // last uint4 of an activation row
     auto xload = [&](int c, uint4 (&dst)[kGroups]) {
+      const bool bok = c * kChunkBlocks + (spiece >> 2) < RB;
+      const uint32_t po = static_cast<uint32_t>((c * 16 + spiece) * 16);
 #pragma unroll
-      for (int k = 0; k < kGroups; ++k) dst[k] = srow[k][min(c * 16 + spiece[k], last_piece)];
+      for (int k = 0; k < kGroups; ++k)
+        if (k < NG) dst[k] = buffer_load16(xrs, bok && sxoff[k] != kOob ? sxoff[k] + po : kOob);
     };
     auto xstore = [&](int c, const uint4 (&src)[kGroups]) {
 #pragma unroll
       for (int k = 0; k < kGroups; ++k) {
         const int u = tid + 256 * k;
-        const bool ok = stok[k] && c * kChunkBlocks + (spiece[k] >> 2) < RB;
-        *reinterpret_cast<uint4*>(lds + (c & 1) * kBuf + (u >> 4) * kXRowBytes + (u & 15) * 16) =
-            ok ? src[k] : make_uint4(0, 0, 0, 0);
+        if (k < NG) *reinterpret_cast<uint4*>(lds + (c & 1) * kBuf + (u >> 4) * kXRowBytes + (u & 15) * 16) = src[k];
       }
     };
 
@@ -379,11 +390,12 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
 
     uint4 rw0[kRing][kWv], rw1[kRing][kWv], rx[kRing][kGroups];
     auto wload = [&](int c, int slot) {
-      const int b = min(c * kChunkBlocks + q, RB - 1);
+      const int b = c * kChunkBlocks + q;
+      const bool ok = b < RB;
 #pragma unroll
       for (int v = 0; v < kWv; ++v) {
-        rw0[slot][v] = *reinterpret_cast<const uint4*>(wbase + wo0 + bstride * b + 16 * v);
-        if (kGateUp) rw1[slot][v] = *reinterpret_cast<const uint4*>(wbase + wo1 + bstride * b + 16 * v);
+        rw0[slot][v] = buffer_load16(wrs, ok ? wo0 + bstride * b + 16 * v : kOob);
+        if (kGateUp) rw1[slot][v] = buffer_load16(wrs, ok ? wo1 + bstride * b + 16 * v : kOob);
       }
     };
 

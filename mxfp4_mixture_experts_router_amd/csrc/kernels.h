@@ -103,6 +103,7 @@ __device__ __forceinline__ int up_row(int n, int rows, int il) { return il ? 2 *
 
 struct ExpertArgs {
   const uint16_t* in;      // gate/up: x [T, K]; down: a [R, I]  (bf16)
+  uint32_t in_bytes;       // size of `in` (MFMA kernel: out-of-range loads read zeros)
   const int32_t* routes;   // gate/up: activation row of position p is routes[p] / top_k; down: nullptr (row p)
   int top_k;
   const uint8_t* wp;       // packed weights

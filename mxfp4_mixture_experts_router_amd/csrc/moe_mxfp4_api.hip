@@ -65,6 +65,10 @@ int check_desc(const moe_mxfp4_desc* d) {
   if (d->expert_offset < 0 || d->expert_offset > d->E_global - d->E_local) return MOE_ERR_SHAPE;
   if (d->top_k < 1 || d->top_k > moe::kMaxTopK || d->top_k > d->E_global) return MOE_ERR_SHAPE;
   if (static_cast<int64_t>(d->T) * d->top_k > (int64_t{1} << 24)) return MOE_ERR_SHAPE;
+  // the kernels address x [T, K] and the intermediate [T*top_k, I] (bf16)
+  // with 32-bit buffer offsets, out-of-range offsets reading zeros
+  if (static_cast<int64_t>(d->T) * d->K * 2 >= (int64_t{1} << 31)) return MOE_ERR_SHAPE;
+  if (static_cast<int64_t>(d->T) * d->top_k * d->I * 2 >= (int64_t{1} << 31)) return MOE_ERR_SHAPE;
   if (d->scoring != MOE_SCORING_SOFTMAX && d->scoring != MOE_SCORING_SIGMOID) return MOE_ERR_MODE;
   if (d->activation != MOE_ACT_SILU_MUL && d->activation != MOE_ACT_SWIGLU_OAI) return MOE_ERR_MODE;
   if (d->weight_layout != MOE_LAYOUT_ROWS && d->weight_layout != MOE_LAYOUT_TILE16) return MOE_ERR_MODE;
@@ -399,6 +403,7 @@ void enqueue_w13(const moe_mxfp4_desc& d, const uint16_t* x, const uint8_t* w13p
   const Layout L = make_layout(d);
   moe::ExpertArgs A{};
   A.in = x;
+  A.in_bytes = static_cast<uint32_t>(static_cast<size_t>(d.T) * d.K * 2);
   A.routes = at<int32_t>(ws, L.routes);
   A.top_k = d.top_k;
   A.wp = w13p;
@@ -439,6 +444,7 @@ void enqueue_w2(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_t* w2p, 
   const Layout L = make_layout(d);
   moe::ExpertArgs A{};
   A.in = a != nullptr ? a : at<uint16_t>(ws, L.a);
+  A.in_bytes = static_cast<uint32_t>(static_cast<size_t>(d.T) * d.top_k * d.I * 2);
   A.routes = nullptr;
   A.top_k = d.top_k;
   A.wp = w2p;
@@ -585,6 +591,7 @@ int moe_mxfp4_prefill(const moe_mxfp4_desc* desc, const uint16_t* x, const float
   enqueue_unpack(d, w13_packed, w13_scales, w2_packed, w2_scales, at<int32_t>(workspace, L.counts), w13u, w2u, s);
   moe::ExpertArgs A{};
   A.in = x;
+  A.in_bytes = static_cast<uint32_t>(static_cast<size_t>(d.T) * d.K * 2);
   A.routes = at<int32_t>(workspace, L.routes);
   A.top_k = d.top_k;
   A.ws = w13_scales;
@@ -601,6 +608,7 @@ int moe_mxfp4_prefill(const moe_mxfp4_desc* desc, const uint16_t* x, const float
   enqueue_mfma_bf16(d, true, A, L, workspace, s);
   moe::ExpertArgs B{};
   B.in = A.a_out;
+  B.in_bytes = static_cast<uint32_t>(static_cast<size_t>(d.T) * d.top_k * d.I * 2);
   B.top_k = d.top_k;
   B.ws = w2_scales;
   B.bias = w2_bias;

@@ -75,6 +75,8 @@ def test_workspace_query():
     (dict(top_k=0), _lib.MOE_ERR_SHAPE),
     (dict(top_k=9), _lib.MOE_ERR_SHAPE),
     (dict(E_global=600, E_local=513), _lib.MOE_ERR_SHAPE),
+    (dict(T=131072, K=8192), _lib.MOE_ERR_SHAPE),           # x reaches 2 GiB
+    (dict(T=32768, top_k=8, I=4096), _lib.MOE_ERR_SHAPE),   # the intermediate reaches 2 GiB
     (dict(scoring=2), _lib.MOE_ERR_MODE),
     (dict(activation=-1), _lib.MOE_ERR_MODE),
     (dict(w13_order=2), _lib.MOE_ERR_MODE),
@@ -83,6 +85,11 @@ def test_workspace_query():
 def test_bad_descriptors_are_refused(bad, code):
     st, _ = _ws_bytes(_desc(**bad))
     assert st == code
+
+
+def test_largest_activation_buffers_are_accepted():
+    assert _ws_bytes(_desc(T=131071, K=8192))[0] == _lib.MOE_OK
+    assert _ws_bytes(_desc(T=32767, top_k=8, I=4096))[0] == _lib.MOE_OK
 
 
 # fake, never-dereferenced addresses: every call below must fail in the host checks
