@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 #include "kernels.h"
 #include "moe_mxfp4.h"
@@ -142,7 +143,8 @@ size_t stream_lds_bytes(int red, bool gate_up, int split) {
          moe::kStreamMaxItems * sizeof(moe::PassEntry);
 }
 
-// Resident workgroups of a kernel on the current device (cached per device and kernel).
+// Resident workgroups of a kernel on the current device (cached per device
+// and kernel; calls from several host threads share the cache under a lock).
 template <typename K>
 int resident_workgroups(K kernel, size_t lds) {
   struct Entry {
@@ -153,9 +155,11 @@ int resident_workgroups(K kernel, size_t lds) {
   };
   static Entry cache[64];
   static int used = 0;
+  static std::mutex lock;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   const void* fn = reinterpret_cast<const void*>(kernel);
+  const std::lock_guard<std::mutex> guard(lock);
   for (int i = 0; i < used; ++i)
     if (cache[i].fn == fn && cache[i].lds == lds && cache[i].dev == dev) return cache[i].n;
   int cus = 0, per_cu = 0;

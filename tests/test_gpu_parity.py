@@ -505,6 +505,44 @@ def test_route_outputs_match_oracle(case):
     assert oracle.rel_l2(y, ysum) <= 3e-3, name
 
 
+# Calls from two host threads at once, each on its own stream and workspace,
+# give the bits of the same calls made one after the other.
+def test_concurrent_calls_from_two_threads():
+    import threading
+    t = torch()
+    cfg = _cfg(K=2880, I=2880, E_global=32, E_local=32, top_k=4, activation="swiglu_oai", bias=True,
+               scale_lo=115, scale_hi=127)
+    w = make_weights(cfg)
+    layer = DeviceLayer(w, layout="tile16")
+    cases = [(T, make_inputs(cfg, T, t_index=T)) for T in (1, 4, 16, 32)]
+    want = {T: bf16_bits_np(run_decode(cfg, layer, inp)) for T, inp in cases}
+    got, errors = {}, []
+
+    def worker(sub):
+        try:
+            s = t.cuda.Stream()
+            for T, inp in sub:
+                d = desc_for(cfg, T, weight_layout="tile16")
+                x, lg = dev_bf16(inp.x), dev_f32(inp.logits)
+                out = t.empty((T, cfg.K), dtype=t.bfloat16, device="cuda")
+                for _ in range(3):
+                    moe.moe_mxfp4_decode(d, x, layer.w13p, layer.w13s, layer.w2p, layer.w2s, out, router_logits=lg,
+                                         w13_bias=layer.b13, w2_bias=layer.b2, stream=s)
+                s.synchronize()
+                got[T] = bf16_bits_np(out)
+        except Exception as e:  # reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(cases[i::2],)) for i in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    for T, _ in cases:
+        assert np.array_equal(got[T], want[T]), T
+
+
 # prefill path: unpack the touched experts to bf16, then bf16 MFMA GEMMs
 @pytest.mark.parametrize("layout", ["rows", "tile16"])
 def test_unpack_touched_experts_bit_exact(layout):
