@@ -74,11 +74,12 @@ extern "C" {
 #define MOE_LAYOUT_ROWS    0    /* the served layout of "Read the served layout"      */
 #define MOE_LAYOUT_TILE16  1
 
-/* Row pairing of the down projection at decode token counts (a performance
- * control; the results are bit-identical either way).  Paired, each wave of
- * the stream kernel computes two 16-row sets 16 rows apart, so every step
- * loads two weight blocks per lane, as the gate/up projection does; it needs
- * K % 32 == 0.  AUTO pairs when the paired work items still fill every
+/* Row pairing of the down projection (a performance control; the results
+ * are bit-identical either way).  Paired, each wave of the stream kernel, or
+ * of the MFMA kernel at many routes per expert, computes two 16-row sets 16
+ * rows apart, so every step loads two weight blocks per lane and each
+ * activation fragment feeds two MFMAs, as in the gate/up projection; it
+ * needs K % 32 == 0.  AUTO pairs when the paired work items still fill every
  * resident workgroup slot of the GPU.                                        */
 /* Row order of w13_packed, w13_scales and w13_bias ("MXFP4 MoE decode
  * kernels", Beyond gpt-oss: kernels for [gate; up] rows and for interleaved

@@ -287,15 +287,23 @@ __global__ __launch_bounds__(256, 4) void gemv_kernel(ExpertArgs A) {
 // lane (r, q) loads the 64 bytes of block q of its row per chunk and feeds
 // its g-th 16 bytes to MFMA g: the operands the MXFP4 path decodes, in the
 // same order, so both give the same bits.
-template <bool kGateUp, int kGroups, bool kBf16W>
+//
+// kPair (down projection, rows % 32 == 0): a wave computes two 16-row sets
+// 16 rows apart (a workgroup 128 rows), so each activation operand read from
+// LDS feeds two MFMAs, as the gate and up rows of the gate/up projection do.
+template <bool kGateUp, int kGroups, bool kBf16W, bool kPair>
 __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertArgs A) {
+  static_assert(!(kGateUp && kPair), "pairing is for the down projection");
+  constexpr bool kTwo = kGateUp || kPair;           // two weight row sets per wave
+  constexpr int kWaveRows = kPair ? 32 : 16;
+  constexpr int kTileRows = 4 * kWaveRows;          // rows of a work item
   constexpr int kTokens = 16 * kGroups;
   constexpr int kBuf = kTokens * kXRowBytes;
   constexpr int kRing = kBf16W ? 2 : (kGroups == 1 ? 5 : 4);  // chunks in flight per wave
   constexpr int kWv = kBf16W ? 4 : 1;                         // 16-byte weight loads per lane and chunk
   extern __shared__ __align__(16) unsigned char lds[];  // [2][kTokens][kXRowBytes], then the scale strips
 
-  const int tiles = (A.rows + kMfmaRows - 1) / kMfmaRows;
+  const int tiles = (A.rows + kTileRows - 1) / kTileRows;
   // XCD-aware order: block b runs on XCD b % 8, so XCD x takes list entries
   // x, x + 8, ..., each with all of its row tiles in dispatch order.  The
   // tiles of one expert then stage the same activation rows through one L2
@@ -309,7 +317,7 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
   if (item >= n_items) return;  // whole workgroup
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, q = lane >> 4;
-  const int wrow0 = tile * kMfmaRows + wave * 16;
+  const int wrow0 = tile * kTileRows + wave * kWaveRows;
   const bool wave_ok = wrow0 < A.rows;              // rows past the end: staging and barriers only
   const int wrow = min(wrow0 + r, A.rows - 1);      // clamped so that every load stays in the expert
   const int red = A.red, RB = red >> 5;
@@ -328,26 +336,29 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A.in), 0, A.in_bytes, 0x00020000);
   const uint8_t* __restrict__ sbase = A.ws + static_cast<size_t>(we.e) * rows_e * RB;
   const int il = kGateUp ? A.il : 0;                // interleaved w13 rows
-  const int wr0 = kGateUp ? gate_row(wrow, il) : wrow, wr1 = up_row(wrow, A.rows, il);
+  const int wr0 = kGateUp ? gate_row(wrow, il) : wrow;
+  const int wr1 = kGateUp ? up_row(wrow, A.rows, il) : min(wrow0 + 16 + r, A.rows - 1);
   const uint32_t wo0 = kBf16W ? static_cast<uint32_t>(wr0) * red * 2 : row_offset(wr0, red >> 1, A.tiled);
   const uint32_t wo1 = kBf16W ? static_cast<uint32_t>(wr1) * red * 2 : row_offset(wr1, red >> 1, A.tiled);
   const uint32_t bstride = kBf16W ? 64u : block_stride(A.tiled);
   // scale strips of the tile's rows (clamped to the expert), staged in LDS once:
-  // [kMfmaRows][RB] (gate/single), then up; interleaved w13: the tile's stored
-  // rows (gate, up alternating) in one strip
-  const int srows = min(kMfmaRows, A.rows - tile * kMfmaRows);
+  // [kTileRows][RB] (gate/single, both sets of a paired wave), then up;
+  // interleaved w13: the tile's stored rows (gate, up alternating) in one strip
+  const int srows = min(kTileRows, A.rows - tile * kTileRows);
   unsigned char* sstrip = lds + 2 * kBuf;
-  const int strip = kMfmaRows * RB;
+  const int strip = kTileRows * RB;
   if (kBf16W) {
     // unpacked weights carry their scales
   } else if (il) {
-    dma_strip(sbase + static_cast<size_t>(2 * tile * kMfmaRows) * RB, sstrip, 2 * srows * RB);
+    dma_strip(sbase + static_cast<size_t>(2 * tile * kTileRows) * RB, sstrip, 2 * srows * RB);
   } else {
-    dma_strip(sbase + static_cast<size_t>(tile * kMfmaRows) * RB, sstrip, srows * RB);
-    if (kGateUp) dma_strip(sbase + static_cast<size_t>(tile * kMfmaRows + A.rows) * RB, sstrip + strip, srows * RB);
+    dma_strip(sbase + static_cast<size_t>(tile * kTileRows) * RB, sstrip, srows * RB);
+    if (kGateUp) dma_strip(sbase + static_cast<size_t>(tile * kTileRows + A.rows) * RB, sstrip + strip, srows * RB);
   }
-  const int s0i = il ? 2 * RB : RB, s1b = il ? RB : strip;  // scale of set j, strip row l: [j * s1b + l * s0i]
-  const int srow_l = min(wave * 16 + r, srows - 1);  // this lane's row in the strips
+  // scale of set j, strip row l: [j * s1b + l * s0i]; a paired wave's second
+  // set is 16 strip rows below its first
+  const int s0i = il ? 2 * RB : RB, s1b = il ? RB : (kPair ? 16 * RB : strip);
+  const int srow_l = min(wave * kWaveRows + r, srows - 1);  // this lane's (first) row in the strips
 
   for (int tp0 = 0; tp0 < we.Te; tp0 += kTokens) {
     const int nt = min(kTokens, we.Te - tp0);
@@ -395,7 +406,7 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
 #pragma unroll
       for (int v = 0; v < kWv; ++v) {
         rw0[slot][v] = buffer_load16(wrs, ok ? wo0 + bstride * b + 16 * v : kOob);
-        if (kGateUp) rw1[slot][v] = buffer_load16(wrs, ok ? wo1 + bstride * b + 16 * v : kOob);
+        if (kTwo) rw1[slot][v] = buffer_load16(wrs, ok ? wo1 + bstride * b + 16 * v : kOob);
       }
     };
 
@@ -418,10 +429,10 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
         // a zero scale turns a ragged-tail block into zeros
         const int bs = min(c * kChunkBlocks + q, RB - 1);
         const float sc0 = (!kBf16W && valid) ? e8m0_to_f32(sstrip[srow_l * s0i + bs]) : 0.0f;
-        const float sc1 = (!kBf16W && kGateUp && valid) ? e8m0_to_f32(sstrip[s1b + srow_l * s0i + bs]) : 0.0f;
+        const float sc1 = (!kBf16W && kTwo && valid) ? e8m0_to_f32(sstrip[s1b + srow_l * s0i + bs]) : 0.0f;
         const uint32_t d0[4] = {rw0[s][0].x, rw0[s][0].y, rw0[s][0].z, rw0[s][0].w};
         uint32_t d1[4] = {0, 0, 0, 0};
-        if (kGateUp) {
+        if (kTwo) {
           d1[0] = rw1[s][0].x;
           d1[1] = rw1[s][0].y;
           d1[2] = rw1[s][0].z;
@@ -431,7 +442,7 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
 #pragma unroll
         for (int v = 0; v < kWv; ++v) {
           u0[v] = rw0[s][v];
-          u1[v] = kGateUp ? rw1[s][v] : make_uint4(0, 0, 0, 0);
+          u1[v] = kTwo ? rw1[s][v] : make_uint4(0, 0, 0, 0);
         }
         wload(c + kRing, s);
         const unsigned char* xb = lds + (c & 1) * kBuf + q * 64;
@@ -444,17 +455,17 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
             // the row (clamped load) contributes zeros, as a zero scale does
             const uint4 z = make_uint4(0, 0, 0, 0);
             a0 = __builtin_bit_cast(bf16x8, valid ? u0[g] : z);
-            if (kGateUp) a1 = __builtin_bit_cast(bf16x8, valid ? u1[g] : z);
+            if (kTwo) a1 = __builtin_bit_cast(bf16x8, valid ? u1[g] : z);
           } else {
             a0 = decode_dword_bf16x8(d0[g], sc0);
-            if (kGateUp) a1 = decode_dword_bf16x8(d1[g], sc1);
+            if (kTwo) a1 = decode_dword_bf16x8(d1[g], sc1);
           }
 #pragma unroll
           for (int tg = 0; tg < kGroups; ++tg) {
             if (tg < NG) {
               const bf16x8 bx = *reinterpret_cast<const bf16x8*>(xb + (tg * 16 + r) * kXRowBytes + g * 16);
               acc0[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bx, acc0[tg], 0, 0, 0);
-              if (kGateUp) acc1[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bx, acc1[tg], 0, 0, 0);
+              if (kTwo) acc1[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bx, acc1[tg], 0, 0, 0);
             }
           }
         }
@@ -476,6 +487,7 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
         for (int i = 0; i < 4; ++i) {
           b0[i] = bf16_bits_to_f32(A.bias[bb + (kGateUp ? gate_row(rowbase + i, il) : rowbase + i)]);
           if (kGateUp) b1[i] = bf16_bits_to_f32(A.bias[bb + up_row(rowbase + i, A.rows, il)]);
+          if (kPair) b1[i] = bf16_bits_to_f32(A.bias[bb + rowbase + 16 + i]);
         }
       }
 #pragma unroll
@@ -496,6 +508,9 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
           } else {
             *reinterpret_cast<float4*>(A.o_out + p * A.rows + rowbase) =
                 make_float4(acc0[tg][0] + b0[0], acc0[tg][1] + b0[1], acc0[tg][2] + b0[2], acc0[tg][3] + b0[3]);
+            if (kPair)
+              *reinterpret_cast<float4*>(A.o_out + p * A.rows + rowbase + 16) =
+                  make_float4(acc1[tg][0] + b1[0], acc1[tg][1] + b1[1], acc1[tg][2] + b1[2], acc1[tg][3] + b1[3]);
           }
         }
       }
@@ -508,18 +523,21 @@ template __global__ void gemv_kernel<true, 16>(ExpertArgs);
 template __global__ void gemv_kernel<true, 32>(ExpertArgs);
 template __global__ void gemv_kernel<false, 16>(ExpertArgs);
 template __global__ void gemv_kernel<false, 32>(ExpertArgs);
-template __global__ void mfma_kernel<true, 1, false>(ExpertArgs);
-template __global__ void mfma_kernel<true, 1, true>(ExpertArgs);
-template __global__ void mfma_kernel<true, 2, false>(ExpertArgs);
-template __global__ void mfma_kernel<true, 2, true>(ExpertArgs);
-template __global__ void mfma_kernel<true, 4, false>(ExpertArgs);
-template __global__ void mfma_kernel<true, 4, true>(ExpertArgs);
-template __global__ void mfma_kernel<false, 1, false>(ExpertArgs);
-template __global__ void mfma_kernel<false, 1, true>(ExpertArgs);
-template __global__ void mfma_kernel<false, 2, false>(ExpertArgs);
-template __global__ void mfma_kernel<false, 2, true>(ExpertArgs);
-template __global__ void mfma_kernel<false, 4, false>(ExpertArgs);
-template __global__ void mfma_kernel<false, 4, true>(ExpertArgs);
+template __global__ void mfma_kernel<true, 1, false, false>(ExpertArgs);
+template __global__ void mfma_kernel<true, 1, true, false>(ExpertArgs);
+template __global__ void mfma_kernel<true, 2, false, false>(ExpertArgs);
+template __global__ void mfma_kernel<true, 2, true, false>(ExpertArgs);
+template __global__ void mfma_kernel<true, 4, false, false>(ExpertArgs);
+template __global__ void mfma_kernel<true, 4, true, false>(ExpertArgs);
+template __global__ void mfma_kernel<false, 1, false, false>(ExpertArgs);
+template __global__ void mfma_kernel<false, 1, true, false>(ExpertArgs);
+template __global__ void mfma_kernel<false, 2, false, false>(ExpertArgs);
+template __global__ void mfma_kernel<false, 2, true, false>(ExpertArgs);
+template __global__ void mfma_kernel<false, 4, false, false>(ExpertArgs);
+template __global__ void mfma_kernel<false, 4, true, false>(ExpertArgs);
+template __global__ void mfma_kernel<false, 1, false, true>(ExpertArgs);
+template __global__ void mfma_kernel<false, 2, false, true>(ExpertArgs);
+template __global__ void mfma_kernel<false, 4, false, true>(ExpertArgs);
 
 // y[t, :] from the per-route down projections (combine4).
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs A) {

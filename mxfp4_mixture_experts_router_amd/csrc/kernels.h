@@ -195,9 +195,10 @@ __global__ void plan_kernel(PlanArgs P);
 // a workgroup of 256 lanes covers 256 / kLanesPerRow rows of one expert.
 template <bool kGateUp, int kLanesPerRow>
 __global__ void gemv_kernel(ExpertArgs A);
-// MFMA regime: 64 rows of one expert per workgroup, kGroups groups of 16 tokens per pass;
+// MFMA regime: 64 rows of one expert per workgroup (128 with kPair, the down
+// projection in pairs of 16-row sets), kGroups groups of 16 tokens per pass;
 // kBf16W reads the bf16-unpacked weights (prefill) instead of decoding MXFP4.
-template <bool kGateUp, int kGroups, bool kBf16W>
+template <bool kGateUp, int kGroups, bool kBf16W, bool kPair>
 __global__ void mfma_kernel(ExpertArgs A);
 // Prefill unpack: packed [E_l][rows][cols/2] (row or tiled layout) + scales
 // -> bf16 [E_l][rows][cols] in the row layout, for the experts with

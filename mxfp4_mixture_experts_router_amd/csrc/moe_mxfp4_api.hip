@@ -268,19 +268,41 @@ void enqueue_expert_pair(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs 
     moe::ExpertArgs M = A;
     M.list = at<moe::WorkEntry>(ws, L.mfma_list);
     M.list_cap = d.E_local;
-    const int64_t grid = (mfma_experts + 7) / 8 * 8 * ((rows + moe::kMfmaRows - 1) / moe::kMfmaRows);
     const int groups = d.T <= 32 ? 1 : (d.T <= 64 ? 2 : 4);
+    // two weight row sets per wave: gate and up rows, or (down) a pair of
+    // 16-row sets, which then halves the grid; under MOE_PAIRING_AUTO the
+    // down projection pairs when the halved grid still fills every resident
+    // workgroup slot
     const size_t lds = 2 * static_cast<size_t>(16 * groups) * moe::kXRowBytes +
-                       static_cast<size_t>(gate_up ? 2 : 1) * moe::kMfmaRows * (red / 32);
-    const dim3 g(static_cast<unsigned>(grid));
+                       static_cast<size_t>(2) * moe::kMfmaRows * (red / 32);
+    const size_t lds1 = 2 * static_cast<size_t>(16 * groups) * moe::kXRowBytes +
+                        static_cast<size_t>(moe::kMfmaRows) * (red / 32);
+    const int64_t slots = (mfma_experts + 7) / 8 * 8;
     if (gate_up) {
-      if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<true, 1, false>), g, dim3(256), lds, s, M);
-      else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<true, 2, false>), g, dim3(256), lds, s, M);
-      else hipLaunchKernelGGL((moe::mfma_kernel<true, 4, false>), g, dim3(256), lds, s, M);
+      const dim3 g(static_cast<unsigned>(slots * ((rows + moe::kMfmaRows - 1) / moe::kMfmaRows)));
+      if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<true, 1, false, false>), g, dim3(256), lds, s, M);
+      else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<true, 2, false, false>), g, dim3(256), lds, s, M);
+      else hipLaunchKernelGGL((moe::mfma_kernel<true, 4, false, false>), g, dim3(256), lds, s, M);
+      return;
+    }
+    bool pair = rows % 32 == 0 && d.down_pairing != MOE_PAIRING_OFF;
+    const int64_t grid2 = slots * ((rows + 2 * moe::kMfmaRows - 1) / (2 * moe::kMfmaRows));
+    if (pair && d.down_pairing == MOE_PAIRING_AUTO) {
+      const int resident = groups == 1   ? resident_workgroups(moe::mfma_kernel<false, 1, false, true>, lds)
+                           : groups == 2 ? resident_workgroups(moe::mfma_kernel<false, 2, false, true>, lds)
+                                         : resident_workgroups(moe::mfma_kernel<false, 4, false, true>, lds);
+      pair = grid2 >= resident;
+    }
+    if (pair) {
+      const dim3 g(static_cast<unsigned>(grid2));
+      if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<false, 1, false, true>), g, dim3(256), lds, s, M);
+      else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<false, 2, false, true>), g, dim3(256), lds, s, M);
+      else hipLaunchKernelGGL((moe::mfma_kernel<false, 4, false, true>), g, dim3(256), lds, s, M);
     } else {
-      if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<false, 1, false>), g, dim3(256), lds, s, M);
-      else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<false, 2, false>), g, dim3(256), lds, s, M);
-      else hipLaunchKernelGGL((moe::mfma_kernel<false, 4, false>), g, dim3(256), lds, s, M);
+      const dim3 g(static_cast<unsigned>(slots * ((rows + moe::kMfmaRows - 1) / moe::kMfmaRows)));
+      if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<false, 1, false, false>), g, dim3(256), lds1, s, M);
+      else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<false, 2, false, false>), g, dim3(256), lds1, s, M);
+      else hipLaunchKernelGGL((moe::mfma_kernel<false, 4, false, false>), g, dim3(256), lds1, s, M);
     }
   }
 }
@@ -322,13 +344,13 @@ void enqueue_mfma_bf16(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs M,
                      static_cast<size_t>(gate_up ? 2 : 1) * moe::kMfmaRows * (M.red / 32);
   const dim3 g(static_cast<unsigned>(grid));
   if (gate_up) {
-    if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<true, 1, true>), g, dim3(256), lds, s, M);
-    else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<true, 2, true>), g, dim3(256), lds, s, M);
-    else hipLaunchKernelGGL((moe::mfma_kernel<true, 4, true>), g, dim3(256), lds, s, M);
+    if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<true, 1, true, false>), g, dim3(256), lds, s, M);
+    else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<true, 2, true, false>), g, dim3(256), lds, s, M);
+    else hipLaunchKernelGGL((moe::mfma_kernel<true, 4, true, false>), g, dim3(256), lds, s, M);
   } else {
-    if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<false, 1, true>), g, dim3(256), lds, s, M);
-    else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<false, 2, true>), g, dim3(256), lds, s, M);
-    else hipLaunchKernelGGL((moe::mfma_kernel<false, 4, true>), g, dim3(256), lds, s, M);
+    if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<false, 1, true, false>), g, dim3(256), lds, s, M);
+    else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<false, 2, true, false>), g, dim3(256), lds, s, M);
+    else hipLaunchKernelGGL((moe::mfma_kernel<false, 4, true, false>), g, dim3(256), lds, s, M);
   }
 }
 

@@ -403,6 +403,10 @@ PAIRING_CASES = [
     ("split2", dict(K=1120, I=1056, E_global=4, E_local=4, top_k=2, bias=True), 7, "tile16"),
     ("split1", dict(K=544, I=608, E_global=4, E_local=4, top_k=2), 20, "rows"),
     ("split1-multipass", dict(K=640, I=512, E_global=2, E_local=2, top_k=2, bias=True), 40, "tile16"),
+    # many routes per expert: the MFMA list kernel, 128-row paired down tiles
+    ("mfma-lists", dict(K=512, I=768, E_global=2, E_local=2, top_k=2, bias=True), 80, "tile16"),
+    ("mfma-lists-ragged-tile", dict(K=416, I=544, E_global=3, E_local=3, top_k=2, activation="swiglu_oai",
+                                    bias=True), 150, "rows"),
 ]
 
 
