@@ -67,6 +67,8 @@ def parse():
     p.add_argument("--prefill", action="store_true",
                    help="time the prefill path (unpack the touched experts to bf16, then bf16 MFMA GEMMs) "
                         "against the decode path on the same calls (default: the wide-K slice at T=256, 2048)")
+    p.add_argument("--down-pairing", default="auto", choices=("auto", "on", "off"),
+                   help="row pairing of the down projection (a performance control; same results)")
     p.add_argument("--per-route", action="store_true",
                    help="per-route output: fp32 [T*top_k, K] rows instead of the bf16 token sums")
     return p.parse_args()
@@ -164,7 +166,7 @@ def main():
         d = moe.make_desc(T=T, K=K, I=I, E_global=cfg.E_global, E_local=cfg.E_local, top_k=cfg.top_k,
                           expert_offset=cfg.expert_offset, scoring=cfg.scoring, activation=cfg.activation,
                           swiglu_alpha=cfg.swiglu_alpha, swiglu_limit=cfg.swiglu_limit, weight_layout=args.layout,
-                          w13_order=args.w13_order)
+                          w13_order=args.w13_order, down_pairing=args.down_pairing)
         ws_bytes = moe.moe_mxfp4_workspace_bytes(d)
         inputs = [make_inputs(cfg, T, call=i) for i in range(L)]
         xs = [torch.from_numpy(inp.x.view(np.int16)).cuda().view(torch.bfloat16) for inp in inputs]
@@ -269,6 +271,7 @@ def main():
         "config": {"workload": f"{cfg.description}; one call at each T in {tokens} per step",
                    "K": K, "I": I, "E_global": cfg.E_global, "E_local": cfg.E_local, "top_k": cfg.top_k,
                    "tokens": tokens, "replicas": L, "weight_layout": args.layout, "w13_order": args.w13_order,
+                   "down_pairing": args.down_pairing,
                    "output": "per-route fp32 rows" if args.per_route else "token sums bf16",
                    "parallelism": "single GPU"},
         "pct_peak": round(100 * value / HBM_PEAK_GBS, 1),
