@@ -285,7 +285,7 @@ def main():
         "device": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline and not args.per_route and args.w13_order == "gate_up":
-        line["cpu_baseline"] = cpu_baseline(cfg, w0, reps[0], torch, moe, args.layout)
+        line["cpu_baseline"] = cpu_baseline(cfg, w0, reps[0], torch, moe, args.layout, tuple(tokens))
     print(json.dumps(line), flush=True)
 
 
@@ -425,8 +425,8 @@ def measured_traffic(cfg, tokens, layout, w13_order="gate_up"):
     return int(np.mean([per_t[str(t)] for t in tokens]))
 
 
-def cpu_baseline(cfg, w0, rep0, torch, moe, layout):
-    """The CPU oracle, as it stands, on a bounded sample: one call at T=1 and one at T=4."""
+def cpu_baseline(cfg, w0, rep0, torch, moe, layout, tokens=(1, 4, 16, 32)):
+    """The CPU oracle, as it stands, on a bounded sample: one call at each T of the sweep."""
     import oracle
     from workloads import make_inputs
 
@@ -436,7 +436,7 @@ def cpu_baseline(cfg, w0, rep0, torch, moe, layout):
     except Exception:
         cores = 1
     total_s, total_bytes, checks = 0.0, 0, {}
-    for T in (1, 4):
+    for T in tokens:
         inp = make_inputs(cfg, T, call=0)
         t0 = time.perf_counter()
         ref = oracle.moe_forward_cfg(cfg, w0, inp)
@@ -457,9 +457,9 @@ def cpu_baseline(cfg, w0, rep0, torch, moe, layout):
         checks[str(T)] = {"rel_l2": float(f"{oracle.rel_l2(y, ref['y']):.3e}"),
                           "cosine": float(f"{oracle.cosine(y, ref['y']):.7f}")}
     return {"value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "us_per_call": round(total_s / 2 * 1e6, 1),
+            "us_per_call": round(total_s / len(tokens) * 1e6, 1),
             "sample": f"numpy oracle (fp32, full dequantise of touched experts, BLAS {cores} threads), "
-                      f"one call at T=1 and one at T=4 of replica 0: {total_s:.1f} s",
+                      f"one call at each T in {list(tokens)} of replica 0: {total_s:.1f} s",
             "parity_vs_gpu": checks}
 
 
