@@ -170,6 +170,135 @@ __device__ __forceinline__ void route_tokens(const PlanArgs& P, int* ids_s, int 
   }
 }
 
+// Local routes of lanes in `loc` whose expert compares below / equal to this
+// lane's key: one ballot per expert-id bit, most significant first (bit b
+// splits the lanes still equal above b).
+struct KeyCompare {
+  uint64_t less, equal;
+};
+__device__ __forceinline__ KeyCompare compare_keys(uint64_t loc, const uint64_t (&bit_ballots)[10], int bits, int key) {
+  uint64_t less = 0, eq = loc;
+#pragma unroll
+  for (int b = 9; b >= 0; --b) {  // unrolled: the ballots stay in registers
+    if (b < bits) {
+      const uint64_t one = bit_ballots[b];
+      if ((key >> b) & 1) {
+        less |= eq & ~one;
+        eq &= one;
+      } else {
+        eq &= ~one;
+      }
+    }
+  }
+  return KeyCompare{less, eq};
+}
+
+// Bucketing of R <= 64 routes by one wave: the counting sort of the general
+// path, written out with ballots.  Lane r holds route r; its plan position is
+// the number of local routes to lower experts plus its rank among the routes
+// to its own expert (stable).  The sorted order is staged in LDS (scratch,
+// 128 ints), from which lane j reads the route at position j to cut passes
+// and to list the touched experts.
+__device__ void bucket_one_wave(const PlanArgs& P, const int32_t* ids, int R, int lane, int* scratch) {
+  const int E_l = P.E_local;
+  const bool in = lane < R;
+  const int e = in ? ids[lane] - P.offset : -1;
+  const bool loc = in && static_cast<unsigned>(e) < static_cast<unsigned>(E_l);
+  const int bits = 32 - __clz(max(E_l - 1, 1));  // <= 9 (E_l <= 512)
+  const uint64_t lt = (1ull << lane) - 1ull, le = lt | (1ull << lane);
+  const uint64_t locm = __ballot(loc);
+  uint64_t bb[10];
+#pragma unroll
+  for (int b = 0; b < 10; ++b) bb[b] = b < bits ? __ballot(loc && ((e >> b) & 1)) : 0ull;
+  const KeyCompare c = compare_keys(locm, bb, bits, e);
+  const int p = __popcll(c.less) + __popcll(c.equal & lt);
+  const int Rl = __popcll(locm);
+  if (in) P.pos[lane] = loc ? p : -1;
+  if (loc) {
+    P.routes[p] = lane;
+    scratch[p] = lane;
+    scratch[64 + p] = e;
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // the sorted view: position j = lane
+  const int j = lane;
+  const bool jin = j < Rl;
+  const int rj = jin ? scratch[j] : 0;
+  const int ej = jin ? scratch[64 + j] : -1;
+  const int eprev = (jin && j > 0) ? scratch[64 + j - 1] : -1;
+  const bool first = jin && ej != eprev;
+  const uint64_t fm = __ballot(first);
+  const uint64_t upto = fm & le, after = fm & ~le;
+  const int start = upto ? 63 - __clzll(upto) : 0;         // first position of this expert
+  const int end = after ? __ffsll(static_cast<unsigned long long>(after)) - 1 : Rl;
+  const int rank = j - start, cnt = end - start;
+
+  // counts and offsets of every local expert: a touched one from its first
+  // position, an untouched one from the next touched expert
+  uint64_t lb[10];
+#pragma unroll
+  for (int b = 0; b < 10; ++b) lb[b] = b < bits ? __ballot(first && ((ej >> b) & 1)) : 0ull;
+  for (int e0 = 0; e0 < E_l; e0 += 64) {
+    const int ee = e0 + lane;
+    if (ee < E_l) {
+      const KeyCompare k = compare_keys(fm, lb, bits, ee);
+      const uint64_t ge = fm & ~k.less;  // leaders of experts >= ee (a suffix of the positions)
+      const int at = ge ? __ffsll(static_cast<unsigned long long>(ge)) - 1 : Rl;
+      int n = 0;
+      if (k.equal) {
+        const uint64_t nxt = fm & ~((k.equal << 1) - 1ull);
+        n = (nxt ? __ffsll(static_cast<unsigned long long>(nxt)) - 1 : Rl) - at;
+      }
+      P.counts[ee] = n;
+      P.offsets[ee] = at;
+    }
+  }
+  if (lane == 0) {
+    P.offsets[E_l] = Rl;
+    P.plan->n_touched = __popcll(fm);
+    P.plan->R_local = Rl;
+  }
+
+  if (P.passes != nullptr) {
+    const int sh = P.pass_shift, tp = 1 << sh;
+    const uint64_t psm = __ballot(jin && (rank & (tp - 1)) == 0);
+    if (jin) {
+      PassEntry* pe = P.passes + (__popcll(psm & le) - 1);
+      pe->rte[rank & (tp - 1)] = static_cast<uint16_t>(rj);
+      if ((rank & (tp - 1)) == 0) {
+        pe->e = ej;
+        pe->nt = min(tp, cnt - rank);
+        pe->p = j;
+      }
+    }
+    if (lane == 0) P.plan->n_passes = __popcll(psm);
+  }
+
+  if (P.lists) {
+    const bool hm = first && P.mfma_enabled && cnt > P.gemv_max;
+    const bool hg = first && !hm;
+    const uint64_t mg = __ballot(hg), mm = __ballot(hm);
+    if (hg || hm) {
+      WorkEntry we;
+      we.e = ej;
+      we.p0 = j;
+      we.Te = cnt;
+#pragma unroll
+      for (int t = 0; t < kGemvMaxTokens; ++t) we.tok[t] = t < cnt ? scratch[j + t] / P.top_k : 0;
+#pragma unroll
+      for (int t = 0; t < 8 - 3 - kGemvMaxTokens; ++t) we.pad[t] = 0;
+      if (hg) P.gemv_list[__popcll(mg & lt)] = we;
+      else P.mfma_list[__popcll(mm & lt)] = we;
+    }
+    if (lane == 0) {
+      P.plan->n_gemv = __popcll(mg);
+      P.plan->n_mfma = __popcll(mm);
+    }
+  }
+  if (P.routes_out != nullptr && in) P.routes_out[lane] = jin ? rj : -1;
+}
+
 }  // namespace
 
 // One wave per token, for calls too large to route inside the plan kernel.
@@ -229,6 +358,13 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
   }
   for (int i = tid; i < kPlanWaves * E_l; i += blockDim.x) hist[i] = 0;
   __syncthreads();
+
+  if (R <= 64) {
+    // at most 64 routes: one wave buckets them, with the same results as the
+    // general path below and no workgroup barrier
+    if (wave == 0) bucket_one_wave(P, fused ? ids_s : P.ids_in, R, lane, hist);
+    return;
+  }
 
   // the R routes in 16 contiguous segments, one per wave, 64 at a time
   const int seg = (R + kPlanWaves - 1) / kPlanWaves;

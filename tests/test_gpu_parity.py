@@ -212,6 +212,8 @@ def test_route_ties_break_to_lower_id():
 BUCKET_CASES = [
     (8, 8, 0, 2, 4, 0.0), (32, 32, 0, 4, 1, 0.0), (128, 128, 0, 4, 32, 0.0), (256, 32, 64, 8, 32, 0.1),
     (384, 48, 336, 8, 2048, 0.05), (384, 48, 0, 8, 2047, 0.0), (512, 512, 0, 8, 300, 0.0), (16, 4, 12, 16, 3, 0.3),
+    # up to 64 routes: the plan kernel's one-wave bucketing (512 experts: 9 id bits; one expert: 1 bit)
+    (512, 512, 0, 8, 8, 0.0), (64, 16, 48, 4, 16, 0.2), (1, 1, 0, 1, 64, 0.0), (600, 512, 88, 2, 32, 0.1),
 ]
 
 
