@@ -549,6 +549,38 @@ def test_concurrent_calls_from_two_threads():
         assert np.array_equal(got[T], want[T]), T
 
 
+# A decode call captured in a HIP graph: every replay, with eager calls on
+# other inputs in between, gives the eager result's bits (stream kernels at
+# reduction splits 4 / 2 / 1, and the GEMV/MFMA list path).
+@pytest.mark.parametrize("T", [1, 8, 32, 100])
+def test_graph_capture_replays_match_eager(T):
+    t = torch()
+    cfg = _cfg(K=1024, I=1024, E_global=16, E_local=16, top_k=4, activation="swiglu_oai", bias=True,
+               scale_lo=115, scale_hi=127)
+    w = make_weights(cfg)
+    layer = DeviceLayer(w, layout="tile16")
+    inp = make_inputs(cfg, T, t_index=T)
+    other = make_inputs(cfg, T, t_index=T + 1)
+    want = bf16_bits_np(run_decode(cfg, layer, inp))
+    d = desc_for(cfg, T, weight_layout="tile16")
+    x, lg = dev_bf16(inp.x), dev_f32(inp.logits)
+    ws = t.empty(moe.moe_mxfp4_workspace_bytes(d), dtype=t.uint8, device="cuda")
+    out = t.empty((T, cfg.K), dtype=t.bfloat16, device="cuda")
+    s = t.cuda.Stream()
+    s.wait_stream(t.cuda.current_stream())
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g, stream=s):
+        moe.moe_mxfp4_decode(d, x, layer.w13p, layer.w13s, layer.w2p, layer.w2s, out, router_logits=lg,
+                             w13_bias=layer.b13, w2_bias=layer.b2, workspace=ws, stream=s)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        assert np.array_equal(bf16_bits_np(out), want), (T, rep)
+        run_decode(cfg, layer, other)  # eager work on other inputs between replays
+
+
 # prefill path: unpack the touched experts to bf16, then bf16 MFMA GEMMs
 @pytest.mark.parametrize("layout", ["rows", "tile16"])
 def test_unpack_touched_experts_bit_exact(layout):
