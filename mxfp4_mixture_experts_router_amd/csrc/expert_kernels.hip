@@ -29,6 +29,8 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace moe {
 
 namespace {
@@ -377,143 +379,161 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
       const int row = A.routes != nullptr ? A.routes[p] / A.top_k : p;
       sxoff[k] = st < nt ? static_cast<uint32_t>(row) * static_cast<uint32_t>(red) * 2u : kOob;
     }
-    auto xload = [&](int c, uint4 (&dst)[kGroups]) {
-      const bool bok = c * kChunkBlocks + (spiece >> 2) < RB;
-      const uint32_t po = static_cast<uint32_t>((c * 16 + spiece) * 16);
-#pragma unroll
-      for (int k = 0; k < kGroups; ++k)
-        if (k < NG) dst[k] = buffer_load16(xrs, bok && sxoff[k] != kOob ? sxoff[k] + po : kOob);
-    };
-    auto xstore = [&](int c, const uint4 (&src)[kGroups]) {
-#pragma unroll
-      for (int k = 0; k < kGroups; ++k) {
-        const int u = tid + 256 * k;
-        if (k < NG) *reinterpret_cast<uint4*>(lds + (c & 1) * kBuf + (u >> 4) * kXRowBytes + (u & 15) * 16) = src[k];
-      }
-    };
-
-    f32x4 acc0[kGroups], acc1[kGroups];
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-      acc0[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      acc1[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-
-    uint4 rw0[kRing][kWv], rw1[kRing][kWv], rx[kRing][kGroups];
-    auto wload = [&](int c, int slot) {
-      const int b = c * kChunkBlocks + q;
-      const bool ok = b < RB;
-#pragma unroll
-      for (int v = 0; v < kWv; ++v) {
-        rw0[slot][v] = buffer_load16(wrs, ok ? wo0 + bstride * b + 16 * v : kOob);
-        if (kTwo) rw1[slot][v] = buffer_load16(wrs, ok ? wo1 + bstride * b + 16 * v : kOob);
-      }
-    };
-
-    // prologue: chunks 0..kRing-1 in flight, chunk 0 staged in LDS
-#pragma unroll
-    for (int s = 0; s < kRing; ++s) {
-      wload(s, s);
-      xload(s, rx[s]);
-    }
-    xstore(0, rx[0]);
-    xload(kRing, rx[0]);
-    lds_barrier();
-
-    const int rounds = (NC + kRing - 1) / kRing;
-    for (int c0 = 0; c0 < rounds * kRing; c0 += kRing) {
-#pragma unroll
-      for (int s = 0; s < kRing; ++s) {
-        const int c = c0 + s;
-        const bool valid = c * kChunkBlocks + q < RB;  // false past the row and past the last chunk
-        // a zero scale turns a ragged-tail block into zeros
-        const int bs = min(c * kChunkBlocks + q, RB - 1);
-        const float sc0 = (!kBf16W && valid) ? e8m0_to_f32(sstrip[srow_l * s0i + bs]) : 0.0f;
-        const float sc1 = (!kBf16W && kTwo && valid) ? e8m0_to_f32(sstrip[s1b + srow_l * s0i + bs]) : 0.0f;
-        const uint32_t d0[4] = {rw0[s][0].x, rw0[s][0].y, rw0[s][0].z, rw0[s][0].w};
-        uint32_t d1[4] = {0, 0, 0, 0};
-        if (kTwo) {
-          d1[0] = rw1[s][0].x;
-          d1[1] = rw1[s][0].y;
-          d1[2] = rw1[s][0].z;
-          d1[3] = rw1[s][0].w;
+    // The chunk loop is instantiated per column-group count, so that no
+    // branch separates the MFMAs of one chunk: the compiler then batches
+    // the LDS reads of the activation operands instead of waiting for
+    // each one before its two MFMAs.
+    auto pass = [&](auto ng) {
+      constexpr int kNG = decltype(ng)::value;
+      auto xload = [&](int c, uint4 (&dst)[kGroups]) {
+        const bool bok = c * kChunkBlocks + (spiece >> 2) < RB;
+        const uint32_t po = static_cast<uint32_t>((c * 16 + spiece) * 16);
+  #pragma unroll
+        for (int k = 0; k < kGroups; ++k)
+          if (k < kNG) dst[k] = buffer_load16(xrs, bok && sxoff[k] != kOob ? sxoff[k] + po : kOob);
+      };
+      auto xstore = [&](int c, const uint4 (&src)[kGroups]) {
+  #pragma unroll
+        for (int k = 0; k < kGroups; ++k) {
+          const int u = tid + 256 * k;
+          if (k < kNG) *reinterpret_cast<uint4*>(lds + (c & 1) * kBuf + (u >> 4) * kXRowBytes + (u & 15) * 16) = src[k];
         }
-        uint4 u0[kWv], u1[kWv];
-#pragma unroll
+      };
+
+      f32x4 acc0[kGroups], acc1[kGroups];
+  #pragma unroll
+      for (int g = 0; g < kGroups; ++g) {
+        acc0[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        acc1[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+
+      uint4 rw0[kRing][kWv], rw1[kRing][kWv], rx[kRing][kGroups];
+      auto wload = [&](int c, int slot) {
+        const int b = c * kChunkBlocks + q;
+        const bool ok = b < RB;
+  #pragma unroll
         for (int v = 0; v < kWv; ++v) {
-          u0[v] = rw0[s][v];
-          u1[v] = kTwo ? rw1[s][v] : make_uint4(0, 0, 0, 0);
+          rw0[slot][v] = buffer_load16(wrs, ok ? wo0 + bstride * b + 16 * v : kOob);
+          if (kTwo) rw1[slot][v] = buffer_load16(wrs, ok ? wo1 + bstride * b + 16 * v : kOob);
         }
-        wload(c + kRing, s);
-        const unsigned char* xb = lds + (c & 1) * kBuf + q * 64;
-        // decode each 8-value operand right before its MFMAs (keeps few registers live)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          bf16x8 a0, a1;
-          if constexpr (kBf16W) {
-            // the unpacked values of elements 8g..8g+7 of the block; a block past
-            // the row (clamped load) contributes zeros, as a zero scale does
-            const uint4 z = make_uint4(0, 0, 0, 0);
-            a0 = __builtin_bit_cast(bf16x8, valid ? u0[g] : z);
-            if (kTwo) a1 = __builtin_bit_cast(bf16x8, valid ? u1[g] : z);
-          } else {
-            a0 = decode_dword_bf16x8(d0[g], sc0);
-            if (kTwo) a1 = decode_dword_bf16x8(d1[g], sc1);
+      };
+
+      // prologue: chunks 0..kRing-1 in flight, chunk 0 staged in LDS
+  #pragma unroll
+      for (int s = 0; s < kRing; ++s) {
+        wload(s, s);
+        xload(s, rx[s]);
+      }
+      xstore(0, rx[0]);
+      xload(kRing, rx[0]);
+      lds_barrier();
+
+      const int rounds = (NC + kRing - 1) / kRing;
+      for (int c0 = 0; c0 < rounds * kRing; c0 += kRing) {
+  #pragma unroll
+        for (int s = 0; s < kRing; ++s) {
+          const int c = c0 + s;
+          const bool valid = c * kChunkBlocks + q < RB;  // false past the row and past the last chunk
+          // blocks past the row were loaded as zeros, which any finite scale
+          // keeps zero: the scale is read unconditionally (clamped index), so
+          // that no exec-masked branch splits the chunk
+          const int bs = min(c * kChunkBlocks + q, RB - 1);
+          const float sc0 = kBf16W ? 0.0f : e8m0_to_f32(sstrip[srow_l * s0i + bs]);
+          const float sc1 = (!kBf16W && kTwo) ? e8m0_to_f32(sstrip[s1b + srow_l * s0i + bs]) : 0.0f;
+          const uint32_t d0[4] = {rw0[s][0].x, rw0[s][0].y, rw0[s][0].z, rw0[s][0].w};
+          uint32_t d1[4] = {0, 0, 0, 0};
+          if (kTwo) {
+            d1[0] = rw1[s][0].x;
+            d1[1] = rw1[s][0].y;
+            d1[2] = rw1[s][0].z;
+            d1[3] = rw1[s][0].w;
           }
-#pragma unroll
-          for (int tg = 0; tg < kGroups; ++tg) {
-            if (tg < NG) {
-              const bf16x8 bx = *reinterpret_cast<const bf16x8*>(xb + (tg * 16 + r) * kXRowBytes + g * 16);
-              acc0[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bx, acc0[tg], 0, 0, 0);
-              if (kTwo) acc1[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bx, acc1[tg], 0, 0, 0);
+          uint4 u0[kWv], u1[kWv];
+  #pragma unroll
+          for (int v = 0; v < kWv; ++v) {
+            u0[v] = rw0[s][v];
+            u1[v] = kTwo ? rw1[s][v] : make_uint4(0, 0, 0, 0);
+          }
+          wload(c + kRing, s);
+          const unsigned char* xb = lds + (c & 1) * kBuf + q * 64;
+          // decode each 8-value operand right before its MFMAs (keeps few registers live)
+  #pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            bf16x8 a0, a1;
+            if constexpr (kBf16W) {
+              // the unpacked values of elements 8g..8g+7 of the block; a block past
+              // the row (clamped load) contributes zeros, as a zero scale does
+              const uint4 z = make_uint4(0, 0, 0, 0);
+              a0 = __builtin_bit_cast(bf16x8, valid ? u0[g] : z);
+              if (kTwo) a1 = __builtin_bit_cast(bf16x8, valid ? u1[g] : z);
+            } else {
+              a0 = decode_dword_bf16x8(d0[g], sc0);
+              if (kTwo) a1 = decode_dword_bf16x8(d1[g], sc1);
+            }
+  #pragma unroll
+            for (int tg = 0; tg < kGroups; ++tg) {
+              if (tg < kNG) {
+                const bf16x8 bx = *reinterpret_cast<const bf16x8*>(xb + (tg * 16 + r) * kXRowBytes + g * 16);
+                acc0[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bx, acc0[tg], 0, 0, 0);
+                if (kTwo) acc1[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bx, acc1[tg], 0, 0, 0);
+              }
+            }
+          }
+          // stage chunk c+1 (loaded kRing-1 chunks ago) and refill its register slot
+          const int sn = (s + 1) % kRing;  // compile-time after unrolling
+          xstore(c + 1, rx[sn]);
+          xload(c + 1 + kRing, rx[sn]);
+          lds_barrier();
+        }
+      }
+
+      // epilogue: lane holds rows wrow0 + 4q + i (i < 4) of token tg*16 + r
+      if (wave_ok) {
+        const int rowbase = wrow0 + 4 * q;
+        float b0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, b1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (A.bias != nullptr) {
+          const size_t bb = static_cast<size_t>(we.e) * rows_e;
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            b0[i] = bf16_bits_to_f32(A.bias[bb + (kGateUp ? gate_row(rowbase + i, il) : rowbase + i)]);
+            if (kGateUp) b1[i] = bf16_bits_to_f32(A.bias[bb + up_row(rowbase + i, A.rows, il)]);
+            if (kPair) b1[i] = bf16_bits_to_f32(A.bias[bb + rowbase + 16 + i]);
+          }
+        }
+  #pragma unroll
+        for (int tg = 0; tg < kGroups; ++tg) {
+          const int tt = tg * 16 + r;
+          if (tg < kNG && tt < nt) {
+            const size_t p = static_cast<size_t>(we.p0 + tp0 + tt);
+            if (kGateUp) {
+              uint16_t h[4];
+  #pragma unroll
+              for (int i = 0; i < 4; ++i)
+                h[i] = f32_to_bf16_rne(
+                    activate(acc0[tg][i] + b0[i], acc1[tg][i] + b1[i], A.act_kind, A.alpha, A.limit));
+              uint2 pk;
+              pk.x = static_cast<uint32_t>(h[0]) | (static_cast<uint32_t>(h[1]) << 16);
+              pk.y = static_cast<uint32_t>(h[2]) | (static_cast<uint32_t>(h[3]) << 16);
+              *reinterpret_cast<uint2*>(A.a_out + p * A.rows + rowbase) = pk;
+            } else {
+              *reinterpret_cast<float4*>(A.o_out + p * A.rows + rowbase) =
+                  make_float4(acc0[tg][0] + b0[0], acc0[tg][1] + b0[1], acc0[tg][2] + b0[2], acc0[tg][3] + b0[3]);
+              if (kPair)
+                *reinterpret_cast<float4*>(A.o_out + p * A.rows + rowbase + 16) =
+                    make_float4(acc1[tg][0] + b1[0], acc1[tg][1] + b1[1], acc1[tg][2] + b1[2], acc1[tg][3] + b1[3]);
             }
           }
         }
-        // stage chunk c+1 (loaded kRing-1 chunks ago) and refill its register slot
-        const int sn = (s + 1) % kRing;  // compile-time after unrolling
-        xstore(c + 1, rx[sn]);
-        xload(c + 1 + kRing, rx[sn]);
-        lds_barrier();
       }
-    }
-
-    // epilogue: lane holds rows wrow0 + 4q + i (i < 4) of token tg*16 + r
-    if (wave_ok) {
-      const int rowbase = wrow0 + 4 * q;
-      float b0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, b1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (A.bias != nullptr) {
-        const size_t bb = static_cast<size_t>(we.e) * rows_e;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          b0[i] = bf16_bits_to_f32(A.bias[bb + (kGateUp ? gate_row(rowbase + i, il) : rowbase + i)]);
-          if (kGateUp) b1[i] = bf16_bits_to_f32(A.bias[bb + up_row(rowbase + i, A.rows, il)]);
-          if (kPair) b1[i] = bf16_bits_to_f32(A.bias[bb + rowbase + 16 + i]);
-        }
-      }
-#pragma unroll
-      for (int tg = 0; tg < kGroups; ++tg) {
-        const int tt = tg * 16 + r;
-        if (tg < NG && tt < nt) {
-          const size_t p = static_cast<size_t>(we.p0 + tp0 + tt);
-          if (kGateUp) {
-            uint16_t h[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              h[i] = f32_to_bf16_rne(
-                  activate(acc0[tg][i] + b0[i], acc1[tg][i] + b1[i], A.act_kind, A.alpha, A.limit));
-            uint2 pk;
-            pk.x = static_cast<uint32_t>(h[0]) | (static_cast<uint32_t>(h[1]) << 16);
-            pk.y = static_cast<uint32_t>(h[2]) | (static_cast<uint32_t>(h[3]) << 16);
-            *reinterpret_cast<uint2*>(A.a_out + p * A.rows + rowbase) = pk;
-          } else {
-            *reinterpret_cast<float4*>(A.o_out + p * A.rows + rowbase) =
-                make_float4(acc0[tg][0] + b0[0], acc0[tg][1] + b0[1], acc0[tg][2] + b0[2], acc0[tg][3] + b0[3]);
-            if (kPair)
-              *reinterpret_cast<float4*>(A.o_out + p * A.rows + rowbase + 16) =
-                  make_float4(acc1[tg][0] + b1[0], acc1[tg][1] + b1[1], acc1[tg][2] + b1[2], acc1[tg][3] + b1[3]);
-          }
-        }
-      }
+    };
+    if (NG >= kGroups) {
+      pass(std::integral_constant<int, kGroups>{});
+    } else if constexpr (kGroups == 4) {
+      if (NG == 3) pass(std::integral_constant<int, 3>{});
+      else if (NG == 2) pass(std::integral_constant<int, 2>{});
+      else pass(std::integral_constant<int, 1>{});
+    } else if constexpr (kGroups == 2) {
+      pass(std::integral_constant<int, 1>{});
     }
     if (tp0 + kTokens < we.Te) lds_barrier();  // the next pass restages the buffers
   }
