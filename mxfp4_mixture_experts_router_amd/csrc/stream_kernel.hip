@@ -265,11 +265,12 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
       asm volatile("" ::"v"(rw0[s].x), "v"(rw0[s].y), "v"(rw0[s].z), "v"(rw0[s].w) : "memory");
     }
     const unsigned char* strip = sbuf + ((ci & 1) * 4 + wave) * sw16;
-    const int b = (kp * NCp + cs) * 4 + q;
-    const bool valid = b < RB;
-    const int bs = valid ? b : 0;
-    const float sc0 = valid ? e8m0_to_f32(strip[r * srs + bs]) : 0.0f;
-    const float sc1 = (kNW == 2 && valid) ? e8m0_to_f32(strip[sub + r * srs + bs]) : 0.0f;
+    // blocks past the row were loaded as zeros, which any finite scale keeps
+    // zero: the scales are read unconditionally at a clamped index, so no
+    // exec-masked branch (and its own LDS wait) opens the step
+    const int bs = min((kp * NCp + cs) * 4 + q, RB - 1);
+    const float sc0 = e8m0_to_f32(strip[r * srs + bs]);
+    const float sc1 = kNW == 2 ? e8m0_to_f32(strip[sub + r * srs + bs]) : 0.0f;
     const unsigned char* xb = xbuf + (g & 1) * kXBufBytes + bts * kXRowBytes + q * 64;
     const uint32_t d0[4] = {rw0[s].x, rw0[s].y, rw0[s].z, rw0[s].w};
 #pragma unroll
