@@ -680,6 +680,34 @@ def test_layer_duplicate_ids_more_routes_than_tokens():
     _assert_close(y, ref["y"], "duplicate ids")
 
 
+# Routes per expert for the list path (T > 64, or a reduction too short for
+# the stream kernel): passes of every column-group count in one launch.
+GROUP_COUNT_CASES = [
+    # T = 100, 4 groups of 16 tokens per pass: 2 routes (GEMV), 18, 40, 55, 75
+    # (a full 64-route pass, then 11) and 10 give passes of 2, 3, 4 and 1
+    # groups; I = 384 and K = 512 leave ragged row tiles in both projections
+    (100, 512, 384, [2, 18, 40, 55, 75, 10, 0, 0]),
+    # T = 40 with K = I = 256 (too short for the stream kernel), 2 groups per
+    # pass: 1 route (GEMV), then 5 (1 group), 20, 30 and 24 (2 groups)
+    (40, 256, 256, [1, 5, 20, 30, 24, 0, 0, 0]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(GROUP_COUNT_CASES)))
+def test_mfma_lists_every_column_group_count(case):
+    T, K, I, counts = GROUP_COUNT_CASES[case]
+    cfg = _cfg(K=K, I=I, bias=True)
+    w = make_weights(cfg)
+    inp = make_topk_inputs(cfg, T, seed=17 + case)
+    slots = np.repeat(np.arange(8, dtype=np.int32), counts)
+    ids = np.stack([slots[:T], slots[T:]], axis=1)
+    assert (ids[:, 0] != ids[:, 1]).all()
+    inp.topk_ids[:] = ids
+    ref = oracle.moe_forward_cfg(cfg, w, inp)
+    y = bf16_to_np(run_decode(cfg, DeviceLayer(w), inp))
+    _assert_close(y, ref["y"], f"column group counts T={T}")
+
+
 def test_layer_no_local_route_writes_zeros():
     cfg = _cfg(E_global=16, E_local=4, expert_offset=12, top_k=2)
     w = make_weights(cfg)
