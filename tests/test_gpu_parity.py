@@ -214,6 +214,9 @@ BUCKET_CASES = [
     (384, 48, 336, 8, 2048, 0.05), (384, 48, 0, 8, 2047, 0.0), (512, 512, 0, 8, 300, 0.0), (16, 4, 12, 16, 3, 0.3),
     # up to 64 routes: the plan kernel's one-wave bucketing (512 experts: 9 id bits; one expert: 1 bit)
     (512, 512, 0, 8, 8, 0.0), (64, 16, 48, 4, 16, 0.2), (1, 1, 0, 1, 64, 0.0), (600, 512, 88, 2, 32, 0.1),
+    # 65 - 128 routes: the general path just above the one-wave limit
+    (32, 32, 0, 4, 32, 0.0), (8, 8, 0, 2, 33, 0.0), (512, 512, 0, 8, 16, 0.1), (64, 16, 48, 4, 20, 0.2),
+    (1, 1, 0, 1, 100, 0.0), (256, 32, 0, 8, 12, 0.0), (4, 4, 0, 1, 65, 0.0),
 ]
 
 
@@ -706,6 +709,18 @@ def test_mfma_lists_every_column_group_count(case):
     ref = oracle.moe_forward_cfg(cfg, w, inp)
     y = bf16_to_np(run_decode(cfg, DeviceLayer(w), inp))
     _assert_close(y, ref["y"], f"column group counts T={T}")
+
+
+def test_list_path_top1_just_above_one_wave_plan():
+    # T = 100, top-1 over 4 experts: 100 routes (just above the plan kernel's
+    # one-wave bucketing) and more than 16 per expert, so the MFMA lists take
+    # them
+    cfg = _cfg(K=512, I=512, E_global=4, E_local=4, top_k=1, bias=True)
+    w = make_weights(cfg)
+    inp = make_topk_inputs(cfg, 100, seed=23)
+    ref = oracle.moe_forward_cfg(cfg, w, inp)
+    y = bf16_to_np(run_decode(cfg, DeviceLayer(w), inp))
+    _assert_close(y, ref["y"], "two routes per lane, lists")
 
 
 def test_layer_no_local_route_writes_zeros():
