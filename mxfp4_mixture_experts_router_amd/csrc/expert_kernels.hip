@@ -107,168 +107,173 @@ __global__ __launch_bounds__(256, 4) void gemv_kernel(ExpertArgs A) {
   extern __shared__ uint4 xs[];  // [kGemvMaxTokens][red / 8], then the scale strips
 
   const int tiles = A.rows / kRowsPerWG;
-  const int item = blockIdx.x / tiles;         // < E_local: the entry load is always in bounds
-  const int n_items = A.plan->n_gemv;
-  const WorkEntry we = A.list[item];
-  if (item >= n_items) return;
-  const int tile = blockIdx.x - item * tiles;
-  const int tid = threadIdx.x, g = tid / kLanesPerRow, q = tid % kLanesPerRow;
-  const int red = A.red, RB = red >> 5, RV = red >> 3;
-  const int n = tile * kRowsPerWG + g;
-  // wave-uniform expert base pointers + 32-bit per-lane row offsets
-  const int rows_e = kGateUp ? 2 * A.rows : A.rows;
-  const uint8_t* __restrict__ wbase = A.wp + static_cast<size_t>(we.e) * rows_e * (red >> 1);
-  const uint8_t* __restrict__ sbase = A.ws + static_cast<size_t>(we.e) * rows_e * RB;
-  const int il = kGateUp ? A.il : 0;                             // interleaved w13 rows
-  const int nr0 = kGateUp ? gate_row(n, il) : n, nr1 = up_row(n, A.rows, il);
-  const uint32_t wo0 = row_offset(nr0, red >> 1, A.tiled), wo1 = row_offset(nr1, red >> 1, A.tiled);
-  const uint32_t bstride = block_stride(A.tiled);
-  const size_t row0 = static_cast<size_t>(we.e) * rows_e + nr0;  // bias index of the gate (or single) row
-  const size_t row1 = static_cast<size_t>(we.e) * rows_e + nr1;  // bias index of the up row
-  auto ldw = [&](uint32_t off, int b) { return *reinterpret_cast<const uint4*>(wbase + off + bstride * b); };
-  // scale strips of the tile's rows, staged in LDS: [kRowsPerWG][RB] (gate/single), then up;
-  // interleaved w13: the tile's 2 * kRowsPerWG stored rows in one strip
-  unsigned char* sstrip = reinterpret_cast<unsigned char*>(xs) + kGemvMaxTokens * red * 2;
-  const int strip = kRowsPerWG * RB;
-  const uint8_t* ss0 = sbase + static_cast<size_t>(tile * kRowsPerWG) * (il ? 2 : 1) * RB;
-  const uint8_t* ss1 = sbase + static_cast<size_t>(tile * kRowsPerWG + A.rows) * RB;
-  auto lds_scale = [&](int which, int b) -> uint32_t {
-    return il ? sstrip[(2 * g + which) * RB + b] : sstrip[which * strip + g * RB + b];
-  };
-  const int nmax = (RB + kLanesPerRow - 1) / kLanesPerRow;  // ring steps (uniform)
-  const int Te = we.Te;
+  // work units (list entry, row tile) of the plan's list, taken grid-stride:
+  // the host's grid is a bound on the units, capped near the resident count,
+  // so that a call whose list is short or empty launches few workgroups
+  const int n_units = A.plan->n_gemv * tiles;
+  for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
+    if (unit != static_cast<int>(blockIdx.x)) __syncthreads();  // LDS restaged for this unit
+    const int item = unit / tiles;               // < n_gemv <= E_local
+    const WorkEntry we = A.list[item];
+    const int tile = unit - item * tiles;
+    const int tid = threadIdx.x, g = tid / kLanesPerRow, q = tid % kLanesPerRow;
+    const int red = A.red, RB = red >> 5, RV = red >> 3;
+    const int n = tile * kRowsPerWG + g;
+    // wave-uniform expert base pointers + 32-bit per-lane row offsets
+    const int rows_e = kGateUp ? 2 * A.rows : A.rows;
+    const uint8_t* __restrict__ wbase = A.wp + static_cast<size_t>(we.e) * rows_e * (red >> 1);
+    const uint8_t* __restrict__ sbase = A.ws + static_cast<size_t>(we.e) * rows_e * RB;
+    const int il = kGateUp ? A.il : 0;                             // interleaved w13 rows
+    const int nr0 = kGateUp ? gate_row(n, il) : n, nr1 = up_row(n, A.rows, il);
+    const uint32_t wo0 = row_offset(nr0, red >> 1, A.tiled), wo1 = row_offset(nr1, red >> 1, A.tiled);
+    const uint32_t bstride = block_stride(A.tiled);
+    const size_t row0 = static_cast<size_t>(we.e) * rows_e + nr0;  // bias index of the gate (or single) row
+    const size_t row1 = static_cast<size_t>(we.e) * rows_e + nr1;  // bias index of the up row
+    auto ldw = [&](uint32_t off, int b) { return *reinterpret_cast<const uint4*>(wbase + off + bstride * b); };
+    // scale strips of the tile's rows, staged in LDS: [kRowsPerWG][RB] (gate/single), then up;
+    // interleaved w13: the tile's 2 * kRowsPerWG stored rows in one strip
+    unsigned char* sstrip = reinterpret_cast<unsigned char*>(xs) + kGemvMaxTokens * red * 2;
+    const int strip = kRowsPerWG * RB;
+    const uint8_t* ss0 = sbase + static_cast<size_t>(tile * kRowsPerWG) * (il ? 2 : 1) * RB;
+    const uint8_t* ss1 = sbase + static_cast<size_t>(tile * kRowsPerWG + A.rows) * RB;
+    auto lds_scale = [&](int which, int b) -> uint32_t {
+      return il ? sstrip[(2 * g + which) * RB + b] : sstrip[which * strip + g * RB + b];
+    };
+    const int nmax = (RB + kLanesPerRow - 1) / kLanesPerRow;  // ring steps (uniform)
+    const int Te = we.Te;
 
-  // Token passes of up to kGemvMaxTokens routes; one pass unless repeated ids
-  // gave the expert more routes while the MFMA regime is off.
-  for (int t0 = 0; t0 < Te; t0 += kGemvMaxTokens) {
-    const int nt = min(kGemvMaxTokens, Te - t0);
-    const int n_stage = nt * RV;
+    // Token passes of up to kGemvMaxTokens routes; one pass unless repeated ids
+    // gave the expert more routes while the MFMA regime is off.
+    for (int t0 = 0; t0 < Te; t0 += kGemvMaxTokens) {
+      const int nt = min(kGemvMaxTokens, Te - t0);
+      const int n_stage = nt * RV;
 
-    // 1. activation rows of the pass: direct global -> LDS copies (16 B per
-    //    lane; a wave's copy fills 1 KB of LDS contiguously), no registers
-    // activation row of each token of the pass (uniform)
-    const uint4* src_row[kGemvMaxTokens];
+      // 1. activation rows of the pass: direct global -> LDS copies (16 B per
+      //    lane; a wave's copy fills 1 KB of LDS contiguously), no registers
+      // activation row of each token of the pass (uniform)
+      const uint4* src_row[kGemvMaxTokens];
 #pragma unroll
-    for (int t = 0; t < kGemvMaxTokens; ++t) {
-      const int tt = min(t0 + t, Te - 1);
-      int row = we.p0 + tt;  // down projection: row of the intermediate
-      if (kGateUp) {
-        int tok = we.tok[0];
-#pragma unroll
-        for (int u = 1; u < kGemvMaxTokens; ++u) tok = tt == u ? we.tok[u] : tok;
-        row = tt < kGemvMaxTokens ? tok : A.routes[we.p0 + tt] / A.top_k;
-      }
-      src_row[t] = reinterpret_cast<const uint4*>(A.in + static_cast<size_t>(row) * red);
-    }
-#pragma unroll 1
-    for (int i = tid; i < n_stage; i += 256) {
-      {
-        int t = 0, c = i;
-#pragma unroll
-        for (int u = 1; u < kGemvMaxTokens; ++u) {
-          const bool next = c >= RV;
-          t = next ? u : t;
-          c = next ? c - RV : c;
-        }
-        const uint4* src = src_row[0];
-#pragma unroll
-        for (int u = 1; u < kGemvMaxTokens; ++u) src = t == u ? src_row[u] : src;
-        __builtin_amdgcn_global_load_lds(src + c,
-                                         reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                             reinterpret_cast<uintptr_t>(xs + (i & ~63))),
-                                         16, 0, 0);
-      }
-    }
-    if (t0 == 0) {
-      if (il) {
-        dma_strip(ss0, sstrip, 2 * strip);
-      } else {
-        dma_strip(ss0, sstrip, strip);
-        if (kGateUp) dma_strip(ss1, sstrip + strip, strip);
-      }
-    }
-    // 2. weight ring, unconditional (indices clamped to the row)
-    uint4 r0[kRing], r1[kRing];
-#pragma unroll
-    for (int j = 0; j < kRing; ++j) {
-      const int b = min(q + kLanesPerRow * j, RB - 1);
-      r0[j] = ldw(wo0, b);
-      if (kGateUp) r1[j] = ldw(wo1, b);
-    }
-    __syncthreads();
-
-    float acc0[kGemvMaxTokens], acc1[kGemvMaxTokens];
-#pragma unroll
-    for (int t = 0; t < kGemvMaxTokens; ++t) acc0[t] = acc1[t] = 0.0f;
-
-    for (int j0 = 0; j0 < nmax; j0 += kRing) {
-#pragma unroll
-      for (int s = 0; s < kRing; ++s) {
-        const int b = q + kLanesPerRow * (j0 + s);
-        const bool valid = b < RB;             // also false past the last ring step
-        const int bc = min(b, RB - 1);
-        // a zero scale turns a ragged-tail block into zeros
-        const float sc0 = valid ? e8m0_to_f32(lds_scale(0, bc)) : 0.0f;
-        const float sc1 = kGateUp && valid ? e8m0_to_f32(lds_scale(1, bc)) : 0.0f;
-        const uint32_t d0[4] = {r0[s].x, r0[s].y, r0[s].z, r0[s].w};
-        uint32_t d1[4] = {0, 0, 0, 0};
+      for (int t = 0; t < kGemvMaxTokens; ++t) {
+        const int tt = min(t0 + t, Te - 1);
+        int row = we.p0 + tt;  // down projection: row of the intermediate
         if (kGateUp) {
-          d1[0] = r1[s].x;
-          d1[1] = r1[s].y;
-          d1[2] = r1[s].z;
-          d1[3] = r1[s].w;
+          int tok = we.tok[0];
+#pragma unroll
+          for (int u = 1; u < kGemvMaxTokens; ++u) tok = tt == u ? we.tok[u] : tok;
+          row = tt < kGemvMaxTokens ? tok : A.routes[we.p0 + tt] / A.top_k;
         }
-        const int bn = min(b + kLanesPerRow * kRing, RB - 1);
-        r0[s] = ldw(wo0, bn);
-        if (kGateUp) r1[s] = ldw(wo1, bn);
+        src_row[t] = reinterpret_cast<const uint4*>(A.in + static_cast<size_t>(row) * red);
+      }
+#pragma unroll 1
+      for (int i = tid; i < n_stage; i += 256) {
+        {
+          int t = 0, c = i;
 #pragma unroll
-        for (int dw = 0; dw < 4; ++dw) {
-          const bf16x2 g0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d0[dw], sc0, 0);
-          const bf16x2 g1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d0[dw], sc0, 1);
-          const bf16x2 g2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d0[dw], sc0, 2);
-          const bf16x2 g3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d0[dw], sc0, 3);
-          bf16x2 u0, u1, u2, u3;
-          if (kGateUp) {
-            u0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d1[dw], sc1, 0);
-            u1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d1[dw], sc1, 1);
-            u2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d1[dw], sc1, 2);
-            u3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d1[dw], sc1, 3);
+          for (int u = 1; u < kGemvMaxTokens; ++u) {
+            const bool next = c >= RV;
+            t = next ? u : t;
+            c = next ? c - RV : c;
           }
+          const uint4* src = src_row[0];
 #pragma unroll
-          for (int t = 0; t < kGemvMaxTokens; ++t) {
-            if (t < nt) {
-              const uint4 xv = xs[t * RV + bc * 4 + dw];
-              acc0[t] = dot2(g3, xv.w, dot2(g2, xv.z, dot2(g1, xv.y, dot2(g0, xv.x, acc0[t]))));
-              if (kGateUp) acc1[t] = dot2(u3, xv.w, dot2(u2, xv.z, dot2(u1, xv.y, dot2(u0, xv.x, acc1[t]))));
+          for (int u = 1; u < kGemvMaxTokens; ++u) src = t == u ? src_row[u] : src;
+          __builtin_amdgcn_global_load_lds(src + c,
+                                           reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                               reinterpret_cast<uintptr_t>(xs + (i & ~63))),
+                                           16, 0, 0);
+        }
+      }
+      if (t0 == 0) {
+        if (il) {
+          dma_strip(ss0, sstrip, 2 * strip);
+        } else {
+          dma_strip(ss0, sstrip, strip);
+          if (kGateUp) dma_strip(ss1, sstrip + strip, strip);
+        }
+      }
+      // 2. weight ring, unconditional (indices clamped to the row)
+      uint4 r0[kRing], r1[kRing];
+#pragma unroll
+      for (int j = 0; j < kRing; ++j) {
+        const int b = min(q + kLanesPerRow * j, RB - 1);
+        r0[j] = ldw(wo0, b);
+        if (kGateUp) r1[j] = ldw(wo1, b);
+      }
+      __syncthreads();
+
+      float acc0[kGemvMaxTokens], acc1[kGemvMaxTokens];
+#pragma unroll
+      for (int t = 0; t < kGemvMaxTokens; ++t) acc0[t] = acc1[t] = 0.0f;
+
+      for (int j0 = 0; j0 < nmax; j0 += kRing) {
+#pragma unroll
+        for (int s = 0; s < kRing; ++s) {
+          const int b = q + kLanesPerRow * (j0 + s);
+          const bool valid = b < RB;             // also false past the last ring step
+          const int bc = min(b, RB - 1);
+          // a zero scale turns a ragged-tail block into zeros
+          const float sc0 = valid ? e8m0_to_f32(lds_scale(0, bc)) : 0.0f;
+          const float sc1 = kGateUp && valid ? e8m0_to_f32(lds_scale(1, bc)) : 0.0f;
+          const uint32_t d0[4] = {r0[s].x, r0[s].y, r0[s].z, r0[s].w};
+          uint32_t d1[4] = {0, 0, 0, 0};
+          if (kGateUp) {
+            d1[0] = r1[s].x;
+            d1[1] = r1[s].y;
+            d1[2] = r1[s].z;
+            d1[3] = r1[s].w;
+          }
+          const int bn = min(b + kLanesPerRow * kRing, RB - 1);
+          r0[s] = ldw(wo0, bn);
+          if (kGateUp) r1[s] = ldw(wo1, bn);
+#pragma unroll
+          for (int dw = 0; dw < 4; ++dw) {
+            const bf16x2 g0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d0[dw], sc0, 0);
+            const bf16x2 g1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d0[dw], sc0, 1);
+            const bf16x2 g2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d0[dw], sc0, 2);
+            const bf16x2 g3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d0[dw], sc0, 3);
+            bf16x2 u0, u1, u2, u3;
+            if (kGateUp) {
+              u0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d1[dw], sc1, 0);
+              u1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d1[dw], sc1, 1);
+              u2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d1[dw], sc1, 2);
+              u3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d1[dw], sc1, 3);
+            }
+#pragma unroll
+            for (int t = 0; t < kGemvMaxTokens; ++t) {
+              if (t < nt) {
+                const uint4 xv = xs[t * RV + bc * 4 + dw];
+                acc0[t] = dot2(g3, xv.w, dot2(g2, xv.z, dot2(g1, xv.y, dot2(g0, xv.x, acc0[t]))));
+                if (kGateUp) acc1[t] = dot2(u3, xv.w, dot2(u2, xv.z, dot2(u1, xv.y, dot2(u0, xv.x, acc1[t]))));
+              }
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);  // keep live ranges per ring slot
+        }
+      }
+
+#pragma unroll
+      for (int t = 0; t < kGemvMaxTokens; ++t) {
+        acc0[t] = row_sum<kLanesPerRow>(acc0[t]);
+        if (kGateUp) acc1[t] = row_sum<kLanesPerRow>(acc1[t]);
+      }
+      if (q == 0) {
+        const float b0 = A.bias != nullptr ? bf16_bits_to_f32(A.bias[row0]) : 0.0f;
+        const float b1 = (kGateUp && A.bias != nullptr) ? bf16_bits_to_f32(A.bias[row1]) : 0.0f;
+#pragma unroll
+        for (int t = 0; t < kGemvMaxTokens; ++t) {
+          if (t < nt) {
+            const size_t p = static_cast<size_t>(we.p0 + t0 + t);
+            if (kGateUp) {
+              A.a_out[p * A.rows + n] =
+                  f32_to_bf16_rne(activate(acc0[t] + b0, acc1[t] + b1, A.act_kind, A.alpha, A.limit));
+            } else {
+              A.o_out[p * A.rows + n] = acc0[t] + b0;
             }
           }
         }
-        __builtin_amdgcn_sched_barrier(0);  // keep live ranges per ring slot
       }
+      if (t0 + kGemvMaxTokens < Te) __syncthreads();  // xs is restaged by the next pass
     }
-
-#pragma unroll
-    for (int t = 0; t < kGemvMaxTokens; ++t) {
-      acc0[t] = row_sum<kLanesPerRow>(acc0[t]);
-      if (kGateUp) acc1[t] = row_sum<kLanesPerRow>(acc1[t]);
-    }
-    if (q == 0) {
-      const float b0 = A.bias != nullptr ? bf16_bits_to_f32(A.bias[row0]) : 0.0f;
-      const float b1 = (kGateUp && A.bias != nullptr) ? bf16_bits_to_f32(A.bias[row1]) : 0.0f;
-#pragma unroll
-      for (int t = 0; t < kGemvMaxTokens; ++t) {
-        if (t < nt) {
-          const size_t p = static_cast<size_t>(we.p0 + t0 + t);
-          if (kGateUp) {
-            A.a_out[p * A.rows + n] =
-                f32_to_bf16_rne(activate(acc0[t] + b0, acc1[t] + b1, A.act_kind, A.alpha, A.limit));
-          } else {
-            A.o_out[p * A.rows + n] = acc0[t] + b0;
-          }
-        }
-      }
-    }
-    if (t0 + kGemvMaxTokens < Te) __syncthreads();  // xs is restaged by the next pass
   }
 }
 

@@ -250,9 +250,16 @@ void enqueue_expert_pair(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs 
   {
     moe::ExpertArgs G = A;
     G.list = at<moe::WorkEntry>(ws, L.gemv_list);
-    const int64_t grid = std::max<int64_t>(1, touched * (rows / rows_per_wg));
     const size_t lds = static_cast<size_t>(moe::kGemvMaxTokens) * red * 2 +
                        static_cast<size_t>(gate_up ? 2 : 1) * rows_per_wg * (red / 32);
+    // the kernel takes its (entry, row tile) units grid-stride: the grid is
+    // the bound on the units, capped at the resident workgroup count
+    const int resident = gate_up ? (lanes == 16 ? resident_workgroups(moe::gemv_kernel<true, 16>, lds)
+                                                : resident_workgroups(moe::gemv_kernel<true, 32>, lds))
+                                 : (lanes == 16 ? resident_workgroups(moe::gemv_kernel<false, 16>, lds)
+                                                : resident_workgroups(moe::gemv_kernel<false, 32>, lds));
+    int64_t grid = std::max<int64_t>(1, touched * (rows / rows_per_wg));
+    if (resident > 0) grid = std::min<int64_t>(grid, resident);
     const dim3 g(static_cast<unsigned>(grid));
     if (gate_up) {
       if (lanes == 16) hipLaunchKernelGGL((moe::gemv_kernel<true, 16>), g, dim3(256), lds, s, G);

@@ -336,6 +336,8 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 //  5. (decode regime) each expert's routes, in plan order, are cut into
 //     passes of 2^pass_shift routes; every route writes its index into its
 //     pass entry as it is placed, and the pass's first route the header.
+constexpr int kIdBatch = 8;  // 64-route chunks whose ids a wave requests at once
+
 __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
   __shared__ int hist[kMaxLocalExperts * kPlanWaves];  // [expert][segment]
   __shared__ int base_e[kMaxLocalExperts + 1];
@@ -371,14 +373,41 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
   const int s0 = min(R, wave * seg), s1 = min(R, s0 + seg);
   const int bits = 32 - __clz(max(E_l - 1, 1));
   const uint64_t lt = (1ull << lane) - 1ull;
-  for (int b = s0; b < s1; b += 64) {
-    const int r = b + lane;
-    const int e = (r < s1) ? (fused ? ids_s[r] : P.ids_in[r]) - offset : -1;
-    const bool loc = (r < s1) && static_cast<unsigned>(e) < static_cast<unsigned>(E_l);
-    if (r < s1 && !loc) P.pos[r] = -1;
-    const uint64_t m = same_expert_lanes(loc, e, bits);
-    if (loc && (m & lt) == 0) hist[e * kPlanWaves + wave] += __popcll(m);  // the group's lowest lane
-    __builtin_amdgcn_wave_barrier();
+  // the ids of kIdBatch chunks are requested together, then the chunks are
+  // processed in order (one memory latency per batch instead of per chunk);
+  // the two sources are read in separate branches, unconditionally at a
+  // clamped index, so that each is a plain LDS or global load with no exec
+  // mask and no wait of its own (a pointer select between them would make
+  // them flat loads; a conditional use would sink each load into a branch)
+  auto load_ids = [&](int b0, int (&ev)[kIdBatch]) {
+    if (fused) {
+#pragma unroll
+      for (int u = 0; u < kIdBatch; ++u) {
+        const int r = b0 + 64 * u + lane;
+        ev[u] = ids_s[min(r, R - 1)] - offset;  // lanes past the segment are masked by r < s1
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kIdBatch; ++u) {
+        const int r = b0 + 64 * u + lane;
+        ev[u] = P.ids_in[min(r, R - 1)] - offset;
+      }
+    }
+  };
+  for (int b0 = s0; b0 < s1; b0 += 64 * kIdBatch) {
+    int ev[kIdBatch];
+    load_ids(b0, ev);
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      const int r = b0 + 64 * u + lane;
+      if (b0 + 64 * u >= s1) break;  // wave-uniform
+      const int e = ev[u];
+      const bool loc = (r < s1) && static_cast<unsigned>(e) < static_cast<unsigned>(E_l);
+      if (r < s1 && !loc) P.pos[r] = -1;
+      const uint64_t m = same_expert_lanes(loc, e, bits);
+      if (loc && (m & lt) == 0) hist[e * kPlanWaves + wave] += __popcll(m);  // the group's lowest lane
+      __builtin_amdgcn_wave_barrier();
+    }
   }
   __syncthreads();
 
@@ -457,31 +486,37 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
 
   // placement: a route's slot is its expert's segment base plus its rank
   // among the same-expert routes before it in the segment (stable)
-  for (int b = s0; b < s1; b += 64) {
-    const int r = b + lane;
-    const int e = (r < s1) ? (fused ? ids_s[r] : P.ids_in[r]) - offset : -1;
-    const bool loc = (r < s1) && static_cast<unsigned>(e) < static_cast<unsigned>(E_l);
-    const uint64_t m = same_expert_lanes(loc, e, bits);
-    if (loc) {
-      const int p = hist[e * kPlanWaves + wave] + __popcll(m & lt);
-      P.routes[p] = r;
-      P.pos[r] = p;
-      if (P.passes != nullptr) {
-        const int sh = P.pass_shift, tp = 1 << sh;
-        const int j = p - base_e[e];
-        const int pass = j >> sh, slot = j & (tp - 1);
-        PassEntry* pe = P.passes + pass_base[e] + pass;
-        pe->rte[slot] = static_cast<uint16_t>(r);
-        if (slot == 0) {
-          pe->e = e;
-          pe->nt = min(tp, base_e[e + 1] - base_e[e] - pass * tp);
-          pe->p = p;
+  for (int b0 = s0; b0 < s1; b0 += 64 * kIdBatch) {
+    int ev[kIdBatch];
+    load_ids(b0, ev);
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      if (b0 + 64 * u >= s1) break;  // wave-uniform
+      const int r = b0 + 64 * u + lane;
+      const int e = ev[u];
+      const bool loc = (r < s1) && static_cast<unsigned>(e) < static_cast<unsigned>(E_l);
+      const uint64_t m = same_expert_lanes(loc, e, bits);
+      if (loc) {
+        const int p = hist[e * kPlanWaves + wave] + __popcll(m & lt);
+        P.routes[p] = r;
+        P.pos[r] = p;
+        if (P.passes != nullptr) {
+          const int sh = P.pass_shift, tp = 1 << sh;
+          const int j = p - base_e[e];
+          const int pass = j >> sh, slot = j & (tp - 1);
+          PassEntry* pe = P.passes + pass_base[e] + pass;
+          pe->rte[slot] = static_cast<uint16_t>(r);
+          if (slot == 0) {
+            pe->e = e;
+            pe->nt = min(tp, base_e[e + 1] - base_e[e] - pass * tp);
+            pe->p = p;
+          }
         }
       }
+      __builtin_amdgcn_wave_barrier();
+      if (loc && (m & lt) == 0) hist[e * kPlanWaves + wave] += __popcll(m);  // next chunk of the segment
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_wave_barrier();
-    if (loc && (m & lt) == 0) hist[e * kPlanWaves + wave] += __popcll(m);  // next chunk of the segment
-    __builtin_amdgcn_wave_barrier();
   }
 
   __syncthreads();  // routes[] complete
