@@ -123,11 +123,22 @@ def moe_mxfp4_workspace_bytes(desc: MoeDesc) -> int:
     return n.value
 
 
-def _workspace(desc, workspace, device):
+def _workspace(desc, workspace, device, stream=None):
     torch = _torch()
     need = moe_mxfp4_workspace_bytes(desc)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+        # Allocated on the stream the call runs on: the caching allocator then
+        # hands the block out again only to later work on that same stream, so
+        # a workspace the caller drops is never given to another stream (or
+        # thread) while the call's kernels still read it.
+        if stream is None:
+            ts = torch.cuda.current_stream(device)
+        elif isinstance(stream, torch.cuda.Stream):
+            ts = stream
+        else:
+            ts = torch.cuda.ExternalStream(int(stream), device=device)
+        with torch.cuda.stream(ts):
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
     if workspace.dtype != torch.uint8 or workspace.device.type != "cuda" or not workspace.is_contiguous():
         raise TypeError("workspace must be a contiguous uint8 device tensor")
     return workspace, workspace.data_ptr(), workspace.numel()
@@ -146,7 +157,7 @@ def moe_mxfp4_decode(desc: MoeDesc, x, w13_packed, w13_scales, w2_packed, w2_sca
     torch = _torch()
     d = desc
     s13p, s13s, s13b, s2p, s2s, s2b = _weights_shapes(d)
-    ws, wsp, wsn = _workspace(d, workspace, x.device)
+    ws, wsp, wsn = _workspace(d, workspace, x.device, stream)
     _check(_lib.lib().moe_mxfp4_decode(
         ctypes.byref(d),
         _ptr(x, torch.bfloat16, (d.T, d.K), "x"),
@@ -170,7 +181,7 @@ def moe_mxfp4_plan(desc: MoeDesc, router_logits=None, topk_ids=None, topk_weight
     torch = _torch()
     d = desc
     dev = next((t.device for t in (router_logits, topk_ids, topk_weights) if t is not None), device)
-    ws, wsp, wsn = _workspace(d, workspace, dev)
+    ws, wsp, wsn = _workspace(d, workspace, dev, stream)
     _check(_lib.lib().moe_mxfp4_plan(
         ctypes.byref(d),
         _ptr(router_logits, torch.float32, (d.T, d.E_global), "router_logits", True),
@@ -185,7 +196,7 @@ def moe_mxfp4_gate_up(desc: MoeDesc, x, w13_packed, w13_scales, workspace, a=Non
     torch = _torch()
     d = desc
     s13p, s13s, s13b, _, _, _ = _weights_shapes(d)
-    ws, wsp, wsn = _workspace(d, workspace, x.device)
+    ws, wsp, wsn = _workspace(d, workspace, x.device, stream)
     _check(_lib.lib().moe_mxfp4_gate_up(
         ctypes.byref(d),
         _ptr(x, torch.bfloat16, (d.T, d.K), "x"),
@@ -201,7 +212,7 @@ def moe_mxfp4_down(desc: MoeDesc, w2_packed, w2_scales, out, workspace, a=None, 
     torch = _torch()
     d = desc
     _, _, _, s2p, s2s, s2b = _weights_shapes(d)
-    ws, wsp, wsn = _workspace(d, workspace, out.device)
+    ws, wsp, wsn = _workspace(d, workspace, out.device, stream)
     _check(_lib.lib().moe_mxfp4_down(
         ctypes.byref(d),
         _ptr(a, torch.bfloat16, (d.T * d.top_k, d.I), "a", True),
@@ -220,7 +231,7 @@ def moe_mxfp4_decode_routes(desc: MoeDesc, x, w13_packed, w13_scales, w2_packed,
     torch = _torch()
     d = desc
     s13p, s13s, s13b, s2p, s2s, s2b = _weights_shapes(d)
-    ws, wsp, wsn = _workspace(d, workspace, x.device)
+    ws, wsp, wsn = _workspace(d, workspace, x.device, stream)
     _check(_lib.lib().moe_mxfp4_decode_routes(
         ctypes.byref(d),
         _ptr(x, torch.bfloat16, (d.T, d.K), "x"),
@@ -244,7 +255,7 @@ def moe_mxfp4_down_routes(desc: MoeDesc, w2_packed, w2_scales, out_routes, works
     torch = _torch()
     d = desc
     _, _, _, s2p, s2s, s2b = _weights_shapes(d)
-    ws, wsp, wsn = _workspace(d, workspace, out_routes.device)
+    ws, wsp, wsn = _workspace(d, workspace, out_routes.device, stream)
     _check(_lib.lib().moe_mxfp4_down_routes(
         ctypes.byref(d),
         _ptr(a, torch.bfloat16, (d.T * d.top_k, d.I), "a", True),
@@ -298,7 +309,7 @@ def moe_mxfp4_unpack(desc: MoeDesc, w13_packed, w13_scales, w2_packed, w2_scales
     torch = _torch()
     d = desc
     s13p, s13s, _, s2p, s2s, _ = _weights_shapes(d)
-    ws, wsp, wsn = _workspace(d, workspace, w13_out.device)
+    ws, wsp, wsn = _workspace(d, workspace, w13_out.device, stream)
     _check(_lib.lib().moe_mxfp4_unpack(
         ctypes.byref(d),
         _ptr(w13_packed, torch.uint8, s13p, "w13_packed"),
@@ -324,7 +335,7 @@ def moe_mxfp4_route(desc: MoeDesc, router_logits, topk_ids, topk_weights, stream
 def moe_mxfp4_bucket(desc: MoeDesc, topk_ids, counts, offsets, routes, workspace=None, stream=None):
     torch = _torch()
     d = desc
-    ws, wsp, wsn = _workspace(d, workspace, topk_ids.device)
+    ws, wsp, wsn = _workspace(d, workspace, topk_ids.device, stream)
     _check(_lib.lib().moe_mxfp4_bucket(
         ctypes.byref(d),
         _ptr(topk_ids, torch.int32, (d.T, d.top_k), "topk_ids"),

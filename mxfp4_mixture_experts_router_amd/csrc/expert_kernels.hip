@@ -564,13 +564,107 @@ template __global__ void mfma_kernel<false, 1, false, true>(ExpertArgs);
 template __global__ void mfma_kernel<false, 2, false, true>(ExpertArgs);
 template __global__ void mfma_kernel<false, 4, false, true>(ExpertArgs);
 
-// y[t, :] from the per-route down projections (combine4).
+// out[t, :] = sum over j (ascending) of w[t, j] * o[route (t, j), :] over the
+// token's local routes (zeros without one), rounded to bf16.  Fixed order and
+// explicit roundings: the same bits wherever it runs.  Workgroup (t, y) takes
+// columns [W y, W y + W), W = 1024 kCols, of token t (tokens on x, whose grid
+// limit is the large one; small calls use kCols = 1, so that a token spreads
+// over several workgroups): one wave lists the token's
+// local routes (their o rows and weights, in j order) in LDS, then each
+// thread requests the rows of 4 listed routes for its kCols float4 column
+// groups (1024 columns apart) before it adds them, so a token costs
+// one memory latency per 4 local routes after the list.  Rows by route with
+// top_k <= 4 (the decode path) skip the list: the rows are known without
+// the positions, so both are requested at once (one latency in all).
+template <int kCols>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs A) {
-  const int t = blockIdx.y;
-  const int k4 = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  if (k4 >= A.K) return;
-  combine4(A, t, k4);
+  __shared__ size_t s_row[kMaxTopK];
+  __shared__ float s_w[kMaxTopK];
+  __shared__ int s_n;
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int k = A.top_k;
+  const int c0 = blockIdx.y * (1024 * kCols) + tid * 4;
+  float4 acc[kCols];
+#pragma unroll
+  for (int c = 0; c < kCols; ++c) acc[c] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  auto store = [&]() {
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) {
+      const int col = c0 + 1024 * c;
+      if (col < A.K) {
+        uint2 packed;
+        packed.x = static_cast<uint32_t>(f32_to_bf16_rne(acc[c].x)) |
+                   (static_cast<uint32_t>(f32_to_bf16_rne(acc[c].y)) << 16);
+        packed.y = static_cast<uint32_t>(f32_to_bf16_rne(acc[c].z)) |
+                   (static_cast<uint32_t>(f32_to_bf16_rne(acc[c].w)) << 16);
+        *reinterpret_cast<uint2*>(A.out + static_cast<size_t>(t) * A.K + col) = packed;
+      }
+    }
+  };
+  auto add = [&](float wt, const float4 (&o)[kCols]) {
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) {
+      acc[c].x = __fadd_rn(acc[c].x, __fmul_rn(wt, o[c].x));
+      acc[c].y = __fadd_rn(acc[c].y, __fmul_rn(wt, o[c].y));
+      acc[c].z = __fadd_rn(acc[c].z, __fmul_rn(wt, o[c].z));
+      acc[c].w = __fadd_rn(acc[c].w, __fmul_rn(wt, o[c].w));
+    }
+  };
+  if (A.by_route && k <= 4) {
+    int p[4];
+    float wt[4];
+    float4 o[4][kCols];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = t * k + min(i, k - 1);
+      p[i] = i < k ? A.pos[r] : -1;
+      wt[i] = A.weights[r];
+#pragma unroll
+      for (int c = 0; c < kCols; ++c)
+        o[i][c] = *reinterpret_cast<const float4*>(A.o + static_cast<size_t>(r) * A.K + min(c0 + 1024 * c, A.K - 4));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (p[i] >= 0) add(wt[i], o[i]);
+    store();
+    return;
+  }
+  if (tid < 64) {
+    // k <= 64: lane j holds route j of the token
+    const int p = tid < k ? A.pos[t * k + tid] : -1;
+    const uint64_t m = __ballot(p >= 0);
+    if (p >= 0) {
+      const int i = __popcll(m & ((1ull << tid) - 1ull));
+      // row of the route's down projection: by route index or by plan position
+      s_row[i] = static_cast<size_t>(A.by_route ? t * k + tid : p) * A.K;
+      s_w[i] = A.weights[t * k + tid];
+    }
+    if (tid == 0) s_n = __popcll(m);
+  }
+  __syncthreads();
+  const int n = s_n;
+  for (int j0 = 0; j0 < n; j0 += 4) {
+    float4 o[4][kCols];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t row = s_row[min(j0 + i, n - 1)];  // listed rows only; extra slots repeat the last
+#pragma unroll
+      for (int c = 0; c < kCols; ++c) {
+        const int col = min(c0 + 1024 * c, A.K - 4);  // in bounds; columns past K are not stored
+        o[i][c] = *reinterpret_cast<const float4*>(A.o + row + col);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (j0 + i >= n) break;
+      add(s_w[j0 + i], o[i]);
+    }
+  }
+  store();
 }
+
+template __global__ void combine_kernel<1>(CombineArgs);
+template __global__ void combine_kernel<4>(CombineArgs);
 
 // One thread per 32-value MX block: 16 packed bytes + 1 scale byte.
 // In place: the group's 16 * blocks pieces of 16 bytes are all read into

@@ -132,38 +132,6 @@ struct CombineArgs {
   int by_route;            // o rows indexed by route: their loads need not wait for pos
 };
 
-// out[t, k4..k4+3] = sum over j (ascending) of w[t, j] * o[route (t, j), k4..k4+3]
-// over the token's local routes (zeros without one), rounded to bf16.  Fixed
-// order and explicit roundings: the same bits wherever it runs.
-__device__ __forceinline__ void combine4(const CombineArgs& A, int t, int k4) {
-  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int j0 = 0; j0 < A.top_k; j0 += 4) {
-    int p[4];
-    float wt[4];
-    float4 o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = t * A.top_k + min(j0 + i, A.top_k - 1);
-      p[i] = j0 + i < A.top_k ? A.pos[r] : -1;
-      wt[i] = A.weights[r];
-      if (A.by_route) o[i] = *reinterpret_cast<const float4*>(A.o + static_cast<size_t>(r) * A.K + k4);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (p[i] < 0) continue;
-      if (!A.by_route) o[i] = *reinterpret_cast<const float4*>(A.o + static_cast<size_t>(p[i]) * A.K + k4);
-      acc.x = __fadd_rn(acc.x, __fmul_rn(wt[i], o[i].x));
-      acc.y = __fadd_rn(acc.y, __fmul_rn(wt[i], o[i].y));
-      acc.z = __fadd_rn(acc.z, __fmul_rn(wt[i], o[i].z));
-      acc.w = __fadd_rn(acc.w, __fmul_rn(wt[i], o[i].w));
-    }
-  }
-  uint2 packed;
-  packed.x = static_cast<uint32_t>(f32_to_bf16_rne(acc.x)) | (static_cast<uint32_t>(f32_to_bf16_rne(acc.y)) << 16);
-  packed.y = static_cast<uint32_t>(f32_to_bf16_rne(acc.z)) | (static_cast<uint32_t>(f32_to_bf16_rne(acc.w)) << 16);
-  *reinterpret_cast<uint2*>(A.out + static_cast<size_t>(t) * A.K + k4) = packed;
-}
-
 // Persistent decode-regime kernel: workgroup b of P takes items b, b+P, ...
 // of the n_passes x tiles items; item = (pass, tile of 64/kSplit rows).
 struct StreamArgs {
@@ -212,6 +180,9 @@ template <bool kGateUp, int kSplit, bool kPair>
 __global__ void stream_kernel(StreamArgs A);
 constexpr int kStreamRing = 4;   // steps (4 MX blocks per lane) in flight per wave
 constexpr int kStreamMaxItems = 32;  // items per workgroup (their entries live in LDS)
+// Token sums of the per-route rows; a workgroup takes 1024 * kCols columns of
+// one token (grid: T x column blocks).
+template <int kCols>
 __global__ void combine_kernel(CombineArgs A);
 // Per-route output rows [R, K] fp32: rows of routes outside the slice become
 // zeros; with in_place == 0 the others are copied from o (plan order) to

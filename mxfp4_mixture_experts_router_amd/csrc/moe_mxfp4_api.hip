@@ -470,6 +470,16 @@ void enqueue_w13(const moe_mxfp4_desc& d, const uint16_t* x, const uint8_t* w13p
   enqueue_expert_pair(d, true, A, L, ws, s);
 }
 
+// Token sums: 1024 columns of a token per workgroup for small calls (several
+// workgroups share a token), 4096 for large ones (fewer, longer workgroups).
+void launch_combine(const moe_mxfp4_desc& d, const moe::CombineArgs& C, hipStream_t s) {
+  if (d.T <= moe::kStreamMaxTokens) {
+    hipLaunchKernelGGL(moe::combine_kernel<1>, dim3(d.T, (d.K + 1023) / 1024), dim3(256), 0, s, C);
+  } else {
+    hipLaunchKernelGGL(moe::combine_kernel<4>, dim3(d.T, (d.K + 4095) / 4096), dim3(256), 0, s, C);
+  }
+}
+
 // The down projection, then either the per-token combine into out (bf16
 // [T, K]) or, with out_routes, the per-route rows (fp32 [T*top_k, K]).
 void enqueue_w2(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_t* w2p, const uint8_t* w2s,
@@ -521,7 +531,7 @@ void enqueue_w2(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_t* w2p, 
     hipLaunchKernelGGL(moe::route_rows_kernel, dim3((d.K / 4 + 255) / 256, R), dim3(256), 0, s, C.o, C.pos,
                        out_routes, R, d.K, C.by_route);
   } else {
-    hipLaunchKernelGGL(moe::combine_kernel, dim3((d.K / 4 + 255) / 256, d.T), dim3(256), 0, s, C);
+    launch_combine(d, C, s);
   }
 }
 
@@ -660,7 +670,7 @@ int moe_mxfp4_prefill(const moe_mxfp4_desc* desc, const uint16_t* x, const float
   C.K = d.K;
   C.top_k = d.top_k;
   C.by_route = 0;
-  hipLaunchKernelGGL(moe::combine_kernel, dim3((d.K / 4 + 255) / 256, d.T), dim3(256), 0, s, C);
+  launch_combine(d, C, s);
   return launch_status();
 }
 
