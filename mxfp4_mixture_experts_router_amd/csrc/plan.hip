@@ -321,9 +321,8 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 // Single workgroup of 16 waves.
 //  0. (router-logits mode, T <= kFusedRouteTokens) route every token, ids to LDS;
 //  1. the R = T*k routes are split into 16 contiguous segments, one per wave;
-//     per-segment histograms of local experts (LDS), counted per 64-route
-//     chunk by the lowest lane of each group of same-expert lanes (groups
-//     come from one ballot per expert-id bit);
+//     per-segment histograms of local experts (LDS), counted with one LDS
+//     atomic add per local route;
 //  2. per expert, exclusive prefix over segments (a 16-lane DPP row scan),
 //     then over experts, so that entry (e, w) becomes the first output slot of
 //     segment w's routes to e;
@@ -404,9 +403,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
       const int e = ev[u];
       const bool loc = (r < s1) && static_cast<unsigned>(e) < static_cast<unsigned>(E_l);
       if (r < s1 && !loc) P.pos[r] = -1;
-      const uint64_t m = same_expert_lanes(loc, e, bits);
-      if (loc && (m & lt) == 0) hist[e * kPlanWaves + wave] += __popcll(m);  // the group's lowest lane
-      __builtin_amdgcn_wave_barrier();
+      // counts only: an LDS atomic per local route (integer adds, any order)
+      if (loc) atomicAdd(&hist[e * kPlanWaves + wave], 1);
     }
   }
   __syncthreads();
