@@ -566,16 +566,17 @@ template __global__ void mfma_kernel<false, 4, false, true>(ExpertArgs);
 
 // out[t, :] = sum over j (ascending) of w[t, j] * o[route (t, j), :] over the
 // token's local routes (zeros without one), rounded to bf16.  Fixed order and
-// explicit roundings: the same bits wherever it runs.  Workgroup (t, y) takes
-// columns [W y, W y + W), W = 1024 kCols, of token t (tokens on x, whose grid
-// limit is the large one; small calls use kCols = 1, so that a token spreads
-// over several workgroups): one wave lists the token's
-// local routes (their o rows and weights, in j order) in LDS, then each
-// thread requests the rows of 4 listed routes for its kCols float4 column
-// groups (1024 columns apart) before it adds them, so a token costs
-// one memory latency per 4 local routes after the list.  Rows by route with
-// top_k <= 4 (the decode path) skip the list: the rows are known without
-// the positions, so both are requested at once (one latency in all).
+// explicit roundings: the same bits wherever it runs.
+//
+// Workgroup (t, y) takes columns [W y, W y + W), W = 1024 kCols, of token t
+// (tokens on x, whose grid limit is the large one; small calls use kCols = 1
+// so that a token spreads over several workgroups).  One wave lists the
+// token's local routes (o row and weight, in j order) in LDS; each thread
+// then requests the rows of 4 listed routes for its kCols float4 column
+// groups (1024 columns apart) before adding them: one memory latency per 4
+// local routes after the list.  Rows by route with top_k <= 4 (the decode
+// path) skip the list: their rows are known without the positions, so both
+// are requested at once (one latency in all).
 template <int kCols>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs A) {
   __shared__ size_t s_row[kMaxTopK];
