@@ -483,37 +483,72 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
   __syncthreads();
 
   // placement: a route's slot is its expert's segment base plus its rank
-  // among the same-expert routes before it in the segment (stable)
-  for (int b0 = s0; b0 < s1; b0 += 64 * kIdBatch) {
-    int ev[kIdBatch];
-    load_ids(b0, ev);
-#pragma unroll
-    for (int u = 0; u < kIdBatch; ++u) {
-      if (b0 + 64 * u >= s1) break;  // wave-uniform
-      const int r = b0 + 64 * u + lane;
-      const int e = ev[u];
-      const bool loc = (r < s1) && static_cast<unsigned>(e) < static_cast<unsigned>(E_l);
-      const uint64_t m = same_expert_lanes(loc, e, bits);
-      if (loc) {
-        const int p = hist[e * kPlanWaves + wave] + __popcll(m & lt);
-        P.routes[p] = r;
-        P.pos[r] = p;
-        if (P.passes != nullptr) {
-          const int sh = P.pass_shift, tp = 1 << sh;
-          const int j = p - base_e[e];
-          const int pass = j >> sh, slot = j & (tp - 1);
-          PassEntry* pe = P.passes + pass_base[e] + pass;
-          pe->rte[slot] = static_cast<uint16_t>(r);
-          if (slot == 0) {
-            pe->e = e;
-            pe->nt = min(tp, base_e[e + 1] - base_e[e] - pass * tp);
-            pe->p = p;
-          }
+  // among the same-expert routes before it in the segment (stable); one
+  // 64-lane chunk of local routes at a time
+  auto place = [&](bool loc, int r, int e) {
+    const uint64_t m = same_expert_lanes(loc, e, bits);
+    if (loc) {
+      const int p = hist[e * kPlanWaves + wave] + __popcll(m & lt);
+      P.routes[p] = r;
+      P.pos[r] = p;
+      if (P.passes != nullptr) {
+        const int sh = P.pass_shift, tp = 1 << sh;
+        const int j = p - base_e[e];
+        const int pass = j >> sh, slot = j & (tp - 1);
+        PassEntry* pe = P.passes + pass_base[e] + pass;
+        pe->rte[slot] = static_cast<uint16_t>(r);
+        if (slot == 0) {
+          pe->e = e;
+          pe->nt = min(tp, base_e[e + 1] - base_e[e] - pass * tp);
+          pe->p = p;
         }
       }
-      __builtin_amdgcn_wave_barrier();
-      if (loc && (m & lt) == 0) hist[e * kPlanWaves + wave] += __popcll(m);  // next chunk of the segment
-      __builtin_amdgcn_wave_barrier();
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (loc && (m & lt) == 0) hist[e * kPlanWaves + wave] += __popcll(m);  // next chunk of the segment
+    __builtin_amdgcn_wave_barrier();
+  };
+  if (!fused && R < (1 << 23)) {
+    // The routing buffer is free: each wave first packs the local routes of
+    // 4 chunks (route << 9 | expert, in segment order) into its 256 entries
+    // of it, then ranks only those, so a slice with few local routes (an
+    // expert-parallel shard) ranks a fraction of the chunks.
+    static_assert(kFusedRouteTokens * kMaxTopK >= kPlanWaves * 256, "256 entries per wave");
+    static_assert(kMaxLocalExperts <= 512, "9 bits of expert id");
+    uint32_t* cbuf = reinterpret_cast<uint32_t*>(ids_s) + wave * 256;
+    for (int b0 = s0; b0 < s1; b0 += 64 * kIdBatch) {
+      int ev[kIdBatch];
+      load_ids(b0, ev);
+#pragma unroll
+      for (int h = 0; h < kIdBatch; h += 4) {
+        int n = 0;
+#pragma unroll
+        for (int u = h; u < h + 4; ++u) {
+          const int r = b0 + 64 * u + lane;
+          const bool loc = (r < s1) && static_cast<unsigned>(ev[u]) < static_cast<unsigned>(E_l);
+          const uint64_t m = __ballot(loc);
+          if (loc) cbuf[n + __popcll(m & lt)] = (static_cast<uint32_t>(r) << 9) | static_cast<uint32_t>(ev[u]);
+          n += __popcll(m);
+        }
+        __builtin_amdgcn_wave_barrier();
+        for (int c = 0; c < n; c += 64) {
+          const bool loc = c + lane < n;
+          const uint32_t v = loc ? cbuf[c + lane] : 0u;
+          place(loc, static_cast<int>(v >> 9), static_cast<int>(v & 511u));
+        }
+      }
+    }
+  } else {
+    for (int b0 = s0; b0 < s1; b0 += 64 * kIdBatch) {
+      int ev[kIdBatch];
+      load_ids(b0, ev);
+#pragma unroll
+      for (int u = 0; u < kIdBatch; ++u) {
+        if (b0 + 64 * u >= s1) break;  // wave-uniform
+        const int r = b0 + 64 * u + lane;
+        const int e = ev[u];
+        place((r < s1) && static_cast<unsigned>(e) < static_cast<unsigned>(E_l), r, e);
+      }
     }
   }
 
