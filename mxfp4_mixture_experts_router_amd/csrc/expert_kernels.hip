@@ -299,14 +299,14 @@ __global__ __launch_bounds__(256, 4) void gemv_kernel(ExpertArgs A) {
 // 16 rows apart (a workgroup 128 rows), so each activation operand read from
 // LDS feeds two MFMAs, as the gate and up rows of the gate/up projection do.
 template <bool kGateUp, int kGroups, bool kBf16W, bool kPair>
-__global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertArgs A) {
+__global__ __launch_bounds__(256, (kGroups == 1 && !kBf16W) ? 3 : 2) void mfma_kernel(ExpertArgs A) {
   static_assert(!(kGateUp && kPair), "pairing is for the down projection");
   constexpr bool kTwo = kGateUp || kPair;           // two weight row sets per wave
   constexpr int kWaveRows = kPair ? 32 : 16;
   constexpr int kTileRows = 4 * kWaveRows;          // rows of a work item
   constexpr int kTokens = 16 * kGroups;
   constexpr int kBuf = kTokens * kXRowBytes;
-  constexpr int kRing = kBf16W ? 2 : (kGroups == 1 ? 5 : 4);  // chunks in flight per wave
+  constexpr int kRing = kBf16W ? 2 : 4;  // chunks in flight per wave
   constexpr int kWv = kBf16W ? 4 : 1;                         // 16-byte weight loads per lane and chunk
   extern __shared__ __align__(16) unsigned char lds[];  // [2][kTokens][kXRowBytes], then the scale strips
 
@@ -531,7 +531,9 @@ __global__ __launch_bounds__(256, kGroups == 1 ? 3 : 2) void mfma_kernel(ExpertA
         }
       }
     };
-    if (NG >= kGroups) {
+    if (NG >= kGroups || kBf16W) {
+      // (the bf16-weight prefill kernels keep one instantiation: groups past
+      // the pass load zeros and are not stored)
       pass(std::integral_constant<int, kGroups>{});
     } else if constexpr (kGroups == 4) {
       if (NG == 3) pass(std::integral_constant<int, 3>{});
