@@ -723,6 +723,19 @@ def test_list_path_top1_just_above_one_wave_plan():
     _assert_close(y, ref["y"], "two routes per lane, lists")
 
 
+@pytest.mark.parametrize("T", [3, 100])
+def test_layer_at_maximum_dimensions(T):
+    # K = I = 8192 (the largest the descriptor accepts), 2 experts, top-1:
+    # T = 3 runs the stream kernel, T = 100 (50 routes per expert) the MFMA
+    # lists with 4 column groups, whose LDS per workgroup is largest here
+    cfg = _cfg(K=8192, I=8192, E_global=2, E_local=2, top_k=1, bias=True)
+    w = make_weights(cfg)
+    inp = make_topk_inputs(cfg, T, seed=29 + T)
+    ref = oracle.moe_forward_cfg(cfg, w, inp)
+    y = bf16_to_np(run_decode(cfg, DeviceLayer(w), inp))
+    _assert_close(y, ref["y"], f"K = I = 8192, T = {T}")
+
+
 def test_layer_no_local_route_writes_zeros():
     cfg = _cfg(E_global=16, E_local=4, expert_offset=12, top_k=2)
     w = make_weights(cfg)
