@@ -25,6 +25,11 @@
  *    the caller; the library allocates nothing, never synchronises and never
  *    logs.  Work is enqueued on `stream` (a hipStream_t; NULL is the default
  *    stream) and runs asynchronously, like a kernel launch.
+ *  - A workspace is in use until the work enqueued with it has completed on
+ *    its stream: calls that may overlap (other streams or threads) need
+ *    distinct workspaces, and a workspace freed or reused elsewhere before
+ *    then gives wrong results or faults (the plan it holds is read by the
+ *    later kernels of the call).
  *  - bf16 tensors are passed as uint16_t bit patterns.
  *  - Every argument check runs on the host before anything is enqueued: on a
  *    non-zero status nothing has been launched and no output has been written.
