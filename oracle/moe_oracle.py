@@ -468,7 +468,12 @@ def moe_forward_cfg(cfg, weights, inputs, **kw):
 
 
 def rel_l2(test: np.ndarray, ref: np.ndarray) -> float:
-    """||test - ref||_2 / ||ref||_2 over the flattened arrays (fp64)."""
+    """||test - ref||_2 / ||ref||_2 over the flattened arrays (fp64).
+
+    "MXFP4 MoE decode kernels", Parity, reports rel_l2 without defining it;
+    the reading is the relative Euclidean error over the whole output.  An
+    all-zero reference scores the output's own norm (0 only for an all-zero
+    output)."""
     t = np.asarray(test, dtype=np.float64).ravel()
     r = np.asarray(ref, dtype=np.float64).ravel()
     den = np.linalg.norm(r)
@@ -476,6 +481,8 @@ def rel_l2(test: np.ndarray, ref: np.ndarray) -> float:
 
 
 def cosine(test: np.ndarray, ref: np.ndarray) -> float:
+    """<test, ref> / (||test|| ||ref||) over the flattened arrays (fp64); two
+    all-zero arrays count as a match (1.0), one all-zero array as none (0.0)."""
     t = np.asarray(test, dtype=np.float64).ravel()
     r = np.asarray(ref, dtype=np.float64).ravel()
     den = np.linalg.norm(t) * np.linalg.norm(r)

@@ -342,3 +342,113 @@ def test_encoder_error_bounds_and_quark_is_more_accurate():
         assert np.all(np.abs(d - w) <= bound * step + 1e-30), rule
         errs[rule] = np.linalg.norm(d - w) / np.linalg.norm(w)
     assert errs["quark"] < errs["ocp"], errs
+
+
+# --------------------------------------------------------------------------
+# acceptance metrics: hand-computed vectors with closed-form answers
+# --------------------------------------------------------------------------
+# Reading (the pages name rel_l2 and cosine without defining them): over the
+# flattened output, rel_l2 = ||test - ref||_2 / ||ref||_2 and
+# cosine = <test, ref> / (||test|| ||ref||).  The vectors below are chosen so
+# that the plausible mistakes give other values: a squared norm ratio, a
+# missing normalisation, a mean of element-wise relative errors, a norm
+# taken per row instead of over the whole array.
+
+def test_rel_l2_closed_forms():
+    # 3-4-5: the difference is an eighth of the reference -> exactly 0.125
+    # (a squared ratio would give 0.015625, an unnormalised norm 0.625)
+    assert oracle.rel_l2(np.array([3.375, 4.5]), np.array([3.0, 4.0])) == 0.125
+    # equal arrays -> 0
+    assert oracle.rel_l2(np.array([1.5, -2.0, 7.0]), np.array([1.5, -2.0, 7.0])) == 0.0
+    # one small element off by 100%, one large exact: 1 / sqrt(1 + 100^2),
+    # not the mean element-wise relative error 0.5
+    got = oracle.rel_l2(np.array([2.0, 100.0]), np.array([1.0, 100.0]))
+    assert got == pytest.approx(1.0 / math.sqrt(10001.0), rel=1e-15)
+    # the opposite sign: ||2 ref|| / ||ref|| = 2
+    assert oracle.rel_l2(np.array([-3.0, -4.0]), np.array([3.0, 4.0])) == 2.0
+    # norms over the whole [T, K] array, not per row: rows [3, 4] (error
+    # [0.375, 0.5]) and [0, 0] (exact) -> 0.625 / 5
+    t = np.array([[3.375, 4.5], [0.0, 0.0]])
+    r = np.array([[3.0, 4.0], [0.0, 0.0]])
+    assert oracle.rel_l2(t, r) == 0.125
+    # a second row with its own error adds in quadrature:
+    # ||[0.375, 0.5, 0, 12]|| / ||[3, 4, 0, 12]|| = sqrt(144.390625) / 13
+    t2 = np.array([[3.375, 4.5], [0.0, 24.0]])
+    r2 = np.array([[3.0, 4.0], [0.0, 12.0]])
+    assert oracle.rel_l2(t2, r2) == pytest.approx(math.sqrt(0.140625 + 0.25 + 144.0) / 13.0, rel=1e-15)
+
+
+def test_rel_l2_invariances_and_zero_reference():
+    rng = np.random.default_rng(5)
+    t, r = rng.standard_normal(1000), rng.standard_normal(1000)
+    # a power-of-two scale of both arrays changes nothing (exact in binary)
+    assert oracle.rel_l2(8.0 * t, 8.0 * r) == oracle.rel_l2(t, r)
+    # the reference's norm is the denominator: swapping the arguments changes the value
+    assert oracle.rel_l2(2.0 * r, r) == pytest.approx(1.0, rel=1e-15)
+    assert oracle.rel_l2(r, 2.0 * r) == pytest.approx(0.5, rel=1e-15)
+    # an all-zero reference (a slice with no local route): only an all-zero
+    # output scores 0; anything else scores its own norm, far above the bar
+    assert oracle.rel_l2(np.zeros(4), np.zeros(4)) == 0.0
+    assert oracle.rel_l2(np.array([3.0, 4.0, 0.0]), np.zeros(3)) == 5.0
+
+
+def test_cosine_closed_forms():
+    # parallel, anti-parallel, orthogonal
+    assert oracle.cosine(np.array([1.0, 2.0, 2.0]), np.array([2.0, 4.0, 4.0])) == 1.0
+    assert oracle.cosine(np.array([1.0, 2.0, 2.0]), np.array([-0.5, -1.0, -1.0])) == -1.0
+    assert oracle.cosine(np.array([1.0, 0.0]), np.array([0.0, 3.0])) == 0.0
+    # 3-4-5: <[3,4],[4,3]> / 25 = 0.96 (unnormalised: 24)
+    assert oracle.cosine(np.array([3.0, 4.0]), np.array([4.0, 3.0])) == pytest.approx(0.96, rel=1e-15)
+    # 45 degrees
+    assert oracle.cosine(np.array([1.0, 0.0]), np.array([1.0, 1.0])) == pytest.approx(1.0 / math.sqrt(2.0), rel=1e-15)
+    # over the whole [T, K] array: rows ([1,0],[0,2]) against ([1,0],[2,0]) ->
+    # 1 / (sqrt(5) sqrt(5)) = 0.2 (a mean of per-row cosines would give 0.5)
+    assert oracle.cosine(np.array([[1.0, 0.0], [0.0, 2.0]]), np.array([[1.0, 0.0], [2.0, 0.0]])) == \
+        pytest.approx(0.2, rel=1e-15)
+
+
+def test_cosine_invariances_and_zero_vectors():
+    rng = np.random.default_rng(6)
+    t, r = rng.standard_normal(1000), rng.standard_normal(1000)
+    c = oracle.cosine(t, r)
+    assert -1.0 <= c <= 1.0
+    # scale of either argument and the argument order do not matter
+    assert oracle.cosine(5.0 * t, r) == pytest.approx(c, rel=1e-12)
+    assert oracle.cosine(r, t) == pytest.approx(c, rel=1e-12)
+    # a small perturbation: 1 - cos = |e_perp|^2 / 2 to first order
+    e = 1e-3 * rng.standard_normal(1000)
+    e_perp = e - (e @ r) / (r @ r) * r
+    want = 1.0 - 0.5 * (e_perp @ e_perp) / (r @ r)
+    assert oracle.cosine(r + e, r) == pytest.approx(want, abs=1e-9)
+    # both all-zero counts as a match; one all-zero is no match
+    assert oracle.cosine(np.zeros(3), np.zeros(3)) == 1.0
+    assert oracle.cosine(np.zeros(3), np.array([1.0, 2.0, 3.0])) == 0.0
+
+
+def test_metric_pins_catch_planted_mistakes(monkeypatch):
+    real_rel, real_cos = oracle.rel_l2, oracle.cosine
+
+    def squared_rel(t, r):
+        return real_rel(t, r) ** 2
+
+    def mean_elementwise_rel(t, r):
+        t, r = np.ravel(t).astype(np.float64), np.ravel(r).astype(np.float64)
+        nz = r != 0
+        return float(np.mean(np.abs(t[nz] - r[nz]) / np.abs(r[nz]))) if nz.any() else float(np.abs(t).sum())
+
+    def unnormalised_cos(t, r):
+        return float(np.ravel(t).astype(np.float64) @ np.ravel(r).astype(np.float64))
+
+    def row_mean_cos(t, r):
+        t, r = np.atleast_2d(t), np.atleast_2d(r)
+        return float(np.mean([real_cos(a, b) for a, b in zip(t, r)]))
+
+    for planted in (squared_rel, mean_elementwise_rel):
+        monkeypatch.setattr(oracle, "rel_l2", planted)
+        with pytest.raises(AssertionError):
+            test_rel_l2_closed_forms()
+    monkeypatch.setattr(oracle, "rel_l2", real_rel)
+    for planted in (unnormalised_cos, row_mean_cos):
+        monkeypatch.setattr(oracle, "cosine", planted)
+        with pytest.raises(AssertionError):
+            test_cosine_closed_forms()
