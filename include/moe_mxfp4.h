@@ -31,8 +31,19 @@
  *    then gives wrong results or faults (the plan it holds is read by the
  *    later kernels of the call).
  *  - bf16 tensors are passed as uint16_t bit patterns.
- *  - Every argument check runs on the host before anything is enqueued: on a
- *    non-zero status nothing has been launched and no output has been written.
+ *  - Every argument check runs on the host before anything is enqueued: on
+ *    any status other than MOE_ERR_HIP nothing has been launched and no
+ *    output has been written.  MOE_ERR_HIP reports the first launch the HIP
+ *    runtime refused (each launch's own status; errors left by other work on
+ *    the thread are neither reported nor cleared); the launches of the call
+ *    before it stay enqueued, so outputs may be partly written.
+ *  - Size limits below (K, I <= 8192; E_local <= 512; top_k <= 64; E_global
+ *    <= 1024 in router-logits mode; T * top_k <= 2^24) are this library's,
+ *    not the pages': they size its on-chip buffers (per-row scale strips of
+ *    K/32 or I/32 bytes in LDS, one 16-lane histogram row per local expert,
+ *    one lane per route of a token, 16 logits per lane in the top-k wave)
+ *    and its 32-bit buffer offsets.  Calls outside them are refused with
+ *    MOE_ERR_SHAPE, never served by another path.
  *  - Status codes are the MOE_* values below; moe_mxfp4_status_string() names
  *    them.
  */
@@ -53,7 +64,7 @@ extern "C" {
 #define MOE_ERR_MODE      (-3)  /* both or neither routing input; bad enum value       */
 #define MOE_ERR_ALIGN     (-4)  /* a tensor pointer is not 16-byte aligned             */
 #define MOE_ERR_WORKSPACE (-5)  /* workspace NULL or smaller than the query says       */
-#define MOE_ERR_HIP       (-6)  /* the HIP runtime reported a launch error             */
+#define MOE_ERR_HIP       (-6)  /* the HIP runtime refused a launch of this call         */
 
 /* ---- enums ------------------------------------------------------------- */
 #define MOE_SCORING_SOFTMAX 0   /* softmax over the top_k selected logits             */
@@ -66,6 +77,10 @@ extern "C" {
 #define MOE_DTYPE_F32  0
 #define MOE_DTYPE_BF16 1
 
+/* Shared-exponent rule of the MXFP4 encoder (moe_mxfp4_encode).             */
+#define MOE_ENCODE_OCP     0    /* shared exponent floor(log2(amax)) - 2             */
+#define MOE_ENCODE_QUARK   1    /* the same, plus one when amax / 2^X >= 7           */
+
 /* Storage order of the packed weights w13_packed and w2_packed (scales always
  * keep the row layout).  MOE_LAYOUT_TILE16 is this library's own order, made
  * in place from the row layout by moe_mxfp4_tile_weights(): in every group of
@@ -73,19 +88,9 @@ extern "C" {
  * block-major, block b of row r at byte 256*b + 16*r of the group.  Each step
  * of the expert kernels then reads one contiguous 1 KB run per wave; the row
  * layout is read in 64-byte pieces of 16 rows.  Same bytes, one copy.       */
-#define MOE_ENCODE_OCP     0    /* shared exponent floor(log2(amax)) - 2             */
-#define MOE_ENCODE_QUARK   1    /* the same, plus one when amax / 2^X >= 7           */
-
 #define MOE_LAYOUT_ROWS    0    /* the served layout of "Read the served layout"      */
 #define MOE_LAYOUT_TILE16  1
 
-/* Row pairing of the down projection (a performance control; the results
- * are bit-identical either way).  Paired, each wave of the stream kernel, or
- * of the MFMA kernel at many routes per expert, computes two 16-row sets 16
- * rows apart, so every step loads two weight blocks per lane and each
- * activation fragment feeds two MFMAs, as in the gate/up projection; it
- * needs K % 32 == 0.  AUTO pairs when the paired work items still fill every
- * resident workgroup slot of the GPU.                                        */
 /* Row order of w13_packed, w13_scales and w13_bias ("MXFP4 MoE decode
  * kernels", Beyond gpt-oss: kernels for [gate; up] rows and for interleaved
  * gate/up rows).  GATE_UP: row n < I is gate row n, row I + n is up row n.
@@ -94,6 +99,13 @@ extern "C" {
 #define MOE_W13_GATE_UP      0
 #define MOE_W13_INTERLEAVED  1
 
+/* Row pairing of the down projection (a performance control; the results
+ * are bit-identical either way).  Paired, each wave of the stream kernel, or
+ * of the MFMA kernel at many routes per expert, computes two 16-row sets 16
+ * rows apart, so every step loads two weight blocks per lane and each
+ * activation fragment feeds two MFMAs, as in the gate/up projection; it
+ * needs K % 32 == 0.  AUTO pairs when the paired work items still fill every
+ * resident workgroup slot of the GPU.                                        */
 #define MOE_PAIRING_AUTO   0
 #define MOE_PAIRING_ON     1    /* whenever K % 32 == 0                               */
 #define MOE_PAIRING_OFF    2
@@ -280,10 +292,16 @@ int moe_mxfp4_unpack(const moe_mxfp4_desc* desc, const uint8_t* w13_packed, cons
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Routing step alone (test hook): router logits fp32 [T, E_global] ->
- * ids int32 [T, top_k] (logit descending, ties to the lower id) and
- * weights fp32 [T, top_k] (softmax over the selected logits, or sigmoid
- * renormalised over the selected, per desc->scoring).
+ * Routing step alone (test hook, the router of calls with T > 64; smaller
+ * calls route inside moe_mxfp4_plan with the same selection and weights):
+ * router logits fp32 [T, E_global] -> ids int32 [T, top_k] (logit
+ * descending, ties to the lower id; a NaN logit ranks below every number)
+ * and weights fp32 [T, top_k] (softmax over the selected logits, or sigmoid
+ * renormalised over the selected, per desc->scoring).  Sources: "MXFP4 MoE
+ * decode kernels", At a glance and Parity (gpt-oss's top-4 softmax routing);
+ * "GLM-5.3-Flash on Gaudi 2", Why (top-8 sigmoid scoring); "GLM-5.2 and
+ * GLM-5.3 (744B) in MXFP4 on Gaudi 2", Why it needed a port, item 4 (int32
+ * ids).  E_global <= 1024 (MOE_ERR_SHAPE); all pointers device pointers.
  */
 int moe_mxfp4_route(const moe_mxfp4_desc* desc, const float* router_logits,
                     int32_t* topk_ids, float* topk_weights, void* stream);
@@ -293,22 +311,48 @@ int moe_mxfp4_route(const moe_mxfp4_desc* desc, const float* router_logits,
  * counts int32 [E_local], exclusive offsets int32 [E_local + 1], and
  * routes int32 [T*top_k] whose first offsets[E_local] entries are the local
  * route indices r = t*top_k + j grouped by local expert, ascending r inside
- * each group (a stable counting sort); the remaining entries are -1.
- * Needs the workspace of moe_mxfp4_workspace_bytes().
+ * each group (a stable counting sort); the remaining entries are -1.  Ids
+ * outside [expert_offset, expert_offset + E_local) (including -1 padding)
+ * are not local.  Source: "MXFP4 MoE decode kernels", Design, Routing inside
+ * the kernel (routes counting-sorted by local expert, routes to other
+ * expert-parallel ranks skipped); "GLM-5.2 and GLM-5.3 (744B) in MXFP4 on
+ * Gaudi 2", Why it needed a port, item 2 (experts sliced by rank).  Needs
+ * the workspace of moe_mxfp4_workspace_bytes(); its contents afterwards hold
+ * no plan a layer step can use.
  */
 int moe_mxfp4_bucket(const moe_mxfp4_desc* desc, const int32_t* topk_ids,
                      int32_t* counts, int32_t* offsets, int32_t* routes,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * MXFP4 -> dense dequantisation (test hook, and the unpack a prefill path
- * would use): packed u8 [rows, cols/2] + scales u8 [rows, cols/32] ->
- * out [rows, cols] as fp32 (out_dtype MOE_DTYPE_F32) or bf16 bits
- * (MOE_DTYPE_BF16).  Value = E2M1(code) * 2^(scale - 127), scale 255 -> NaN,
- * computed with the same decode the layer kernels use.  cols % 32 == 0.
+ * MXFP4 -> dense dequantisation (test hook): packed u8 [rows, cols/2] (row
+ * layout) + scales u8 [rows, cols/32] -> out [rows, cols] as fp32
+ * (out_dtype MOE_DTYPE_F32) or bf16 bits (MOE_DTYPE_BF16).  Value =
+ * E2M1(code) * 2^(scale - 127) with code of element 2c the low nibble of
+ * byte c, scale 255 -> NaN, computed with the same decode the layer kernels
+ * use.  Sources: "GLM-5.2 and GLM-5.3 (744B) in MXFP4 on Gaudi 2", What was
+ * built, Byte-exact repack (E2M1 low nibble first, E8M0 scales, blocks of
+ * 32); "MXFP4 MoE decode kernels", The bottleneck (two values per byte, one
+ * scale per 32).  cols % 32 == 0 (MOE_ERR_SHAPE); packed and out 16-byte
+ * aligned (MOE_ERR_ALIGN).
  */
 int moe_mxfp4_dequant(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t cols,
                       int32_t out_dtype, void* out, void* stream);
+
+/*
+ * Copy of the plan a moe_mxfp4_plan (or a layer call) left in `workspace`
+ * (test hook: the routing and bucketing the layer kernels actually used):
+ * ids int32 [T, top_k] and weights fp32 [T, top_k] (logits mode: the
+ * router's choice, made inside the plan kernel for T <= 64; ids mode: the
+ * caller's), counts int32 [E_local], offsets int32 [E_local + 1] and routes
+ * int32 [T*top_k] (local route indices grouped by local expert, -1 past the
+ * local routes), as moe_mxfp4_route and moe_mxfp4_bucket define them.  Any
+ * output may be NULL (not written).  Same descriptor as the call that
+ * planned; enqueued on `stream` after it.
+ */
+int moe_mxfp4_plan_read(const moe_mxfp4_desc* desc, const void* workspace, size_t workspace_bytes,
+                        int32_t* topk_ids, float* topk_weights, int32_t* counts, int32_t* offsets,
+                        int32_t* routes, void* stream);
 
 /*
  * MXFP4 encoder ("GLM-5.2 and GLM-5.3 (744B) in MXFP4 on Gaudi 2", What was

@@ -43,6 +43,8 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "MoeDesc", "MoeError", "make_desc", "moe_mxfp4_workspace_bytes", "moe_mxfp4_decode",
     "moe_mxfp4_plan", "moe_mxfp4_gate_up", "moe_mxfp4_down", "moe_mxfp4_route", "moe_mxfp4_bucket",
+    "moe_mxfp4_plan_read", "moe_mxfp4_decode_routes", "moe_mxfp4_down_routes", "moe_mxfp4_prefill",
+    "moe_mxfp4_prefill_workspace_bytes", "moe_mxfp4_unpack",
     "moe_mxfp4_dequant", "moe_mxfp4_tile_weights", "moe_mxfp4_encode", "moe_mxfp4_status_string", "moe_mxfp4_version",
 ]
 
@@ -144,6 +146,20 @@ def _workspace(desc, workspace, device, stream=None):
     return workspace, workspace.data_ptr(), workspace.numel()
 
 
+def _planned_workspace(desc, workspace, name):
+    """The workspace of a step that reads a plan: it must be the caller's,
+    holding the plan of an earlier call (a fresh buffer holds none)."""
+    torch = _torch()
+    if workspace is None:
+        raise ValueError(f"{name} reads the plan held in a workspace: pass the workspace of the "
+                         "moe_mxfp4_plan (or layer) call that made it")
+    if workspace.dtype != torch.uint8 or workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 device tensor")
+    if workspace.numel() < moe_mxfp4_workspace_bytes(desc):
+        raise ValueError(f"{name}: workspace smaller than moe_mxfp4_workspace_bytes()")
+    return workspace, workspace.data_ptr(), workspace.numel()
+
+
 def _weights_shapes(d: MoeDesc, E: Optional[int] = None):
     E = d.E_local if E is None else E
     return ((E, 2 * d.I, d.K // 2), (E, 2 * d.I, d.K // 32), (E, 2 * d.I),
@@ -196,7 +212,7 @@ def moe_mxfp4_gate_up(desc: MoeDesc, x, w13_packed, w13_scales, workspace, a=Non
     torch = _torch()
     d = desc
     s13p, s13s, s13b, _, _, _ = _weights_shapes(d)
-    ws, wsp, wsn = _workspace(d, workspace, x.device, stream)
+    ws, wsp, wsn = _planned_workspace(d, workspace, "moe_mxfp4_gate_up")
     _check(_lib.lib().moe_mxfp4_gate_up(
         ctypes.byref(d),
         _ptr(x, torch.bfloat16, (d.T, d.K), "x"),
@@ -212,7 +228,7 @@ def moe_mxfp4_down(desc: MoeDesc, w2_packed, w2_scales, out, workspace, a=None, 
     torch = _torch()
     d = desc
     _, _, _, s2p, s2s, s2b = _weights_shapes(d)
-    ws, wsp, wsn = _workspace(d, workspace, out.device, stream)
+    ws, wsp, wsn = _planned_workspace(d, workspace, "moe_mxfp4_down")
     _check(_lib.lib().moe_mxfp4_down(
         ctypes.byref(d),
         _ptr(a, torch.bfloat16, (d.T * d.top_k, d.I), "a", True),
@@ -255,7 +271,7 @@ def moe_mxfp4_down_routes(desc: MoeDesc, w2_packed, w2_scales, out_routes, works
     torch = _torch()
     d = desc
     _, _, _, s2p, s2s, s2b = _weights_shapes(d)
-    ws, wsp, wsn = _workspace(d, workspace, out_routes.device, stream)
+    ws, wsp, wsn = _planned_workspace(d, workspace, "moe_mxfp4_down_routes")
     _check(_lib.lib().moe_mxfp4_down_routes(
         ctypes.byref(d),
         _ptr(a, torch.bfloat16, (d.T * d.top_k, d.I), "a", True),
@@ -309,7 +325,7 @@ def moe_mxfp4_unpack(desc: MoeDesc, w13_packed, w13_scales, w2_packed, w2_scales
     torch = _torch()
     d = desc
     s13p, s13s, _, s2p, s2s, _ = _weights_shapes(d)
-    ws, wsp, wsn = _workspace(d, workspace, w13_out.device, stream)
+    ws, wsp, wsn = _planned_workspace(d, workspace, "moe_mxfp4_unpack")
     _check(_lib.lib().moe_mxfp4_unpack(
         ctypes.byref(d),
         _ptr(w13_packed, torch.uint8, s13p, "w13_packed"),
@@ -344,6 +360,24 @@ def moe_mxfp4_bucket(desc: MoeDesc, topk_ids, counts, offsets, routes, workspace
         _ptr(routes, torch.int32, (d.T * d.top_k,), "routes"),
         wsp, wsn, _stream(stream)), "moe_mxfp4_bucket")
     return ws
+
+
+def moe_mxfp4_plan_read(desc: MoeDesc, workspace, topk_ids=None, topk_weights=None, counts=None, offsets=None,
+                        routes=None, stream=None):
+    """Copies of the routing (ids, weights [T, top_k]) and bucketing (counts
+    [E_local], offsets [E_local + 1], routes [T*top_k]) held by the plan in
+    ``workspace``; outputs left None are not written."""
+    torch = _torch()
+    d = desc
+    ws, wsp, wsn = _planned_workspace(d, workspace, "moe_mxfp4_plan_read")
+    _check(_lib.lib().moe_mxfp4_plan_read(
+        ctypes.byref(d), wsp, wsn,
+        _ptr(topk_ids, torch.int32, (d.T, d.top_k), "topk_ids", True),
+        _ptr(topk_weights, torch.float32, (d.T, d.top_k), "topk_weights", True),
+        _ptr(counts, torch.int32, (d.E_local,), "counts", True),
+        _ptr(offsets, torch.int32, (d.E_local + 1,), "offsets", True),
+        _ptr(routes, torch.int32, (d.T * d.top_k,), "routes", True),
+        _stream(stream)), "moe_mxfp4_plan_read")
 
 
 def moe_mxfp4_encode(values, packed, scales, rule="quark", stream=None):

@@ -43,6 +43,7 @@ EXPORTED = (
     "moe_mxfp4_plan",
     "moe_mxfp4_route",
     "moe_mxfp4_bucket",
+    "moe_mxfp4_plan_read",
     "moe_mxfp4_gate_up",
     "moe_mxfp4_down",
     "moe_mxfp4_decode_routes",
@@ -96,6 +97,7 @@ _SIGNATURES = {
     "moe_mxfp4_unpack": (_I32, [_DESC, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_mxfp4_route": (_I32, [_DESC, _P, _P, _P, _P]),
     "moe_mxfp4_bucket": (_I32, [_DESC, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_mxfp4_plan_read": (_I32, [_DESC, _P, _SZ, _P, _P, _P, _P, _P, _P]),
     "moe_mxfp4_dequant": (_I32, [_P, _P, _I64, _I64, _I32, _P, _P]),
     "moe_mxfp4_tile_weights": (_I32, [_P, _I64, _I64, _I32, _P]),
     "moe_mxfp4_encode": (_I32, [_P, _I32, _I64, _I64, _I32, _P, _P, _P]),

@@ -84,6 +84,19 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// A list entry with every field inside the call's bounds: expert < E_local,
+// positions p0 .. p0 + Te - 1 inside [0, R), tokens inside [0, T).  The plan
+// kernel writes entries that satisfy this already; the clamp keeps a stale
+// or foreign workspace from turning into out-of-range accesses.
+__device__ __forceinline__ WorkEntry clamp_entry(WorkEntry we, const ExpertArgs& A) {
+  we.e = min(max(we.e, 0), A.list_cap - 1);
+  we.p0 = min(max(we.p0, 0), A.R - 1);
+  we.Te = min(max(we.Te, 0), A.R - we.p0);
+#pragma unroll
+  for (int t = 0; t < kGemvMaxTokens; ++t) we.tok[t] = min(max(we.tok[t], 0), A.T - 1);
+  return we;
+}
+
 template <int kLanesPerRow>
 __device__ __forceinline__ float row_sum(float v) {
   v = row16_sum(v);
@@ -110,11 +123,12 @@ __global__ __launch_bounds__(256, 4) void gemv_kernel(ExpertArgs A) {
   // work units (list entry, row tile) of the plan's list, taken grid-stride:
   // the host's grid is a bound on the units, capped near the resident count,
   // so that a call whose list is short or empty launches few workgroups
-  const int n_units = A.plan->n_gemv * tiles;
+  if (A.plan->key != A.key) return;  // no plan for this call in the workspace
+  const int n_units = min(max(A.plan->n_gemv, 0), A.list_cap) * tiles;
   for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
     if (unit != static_cast<int>(blockIdx.x)) __syncthreads();  // LDS restaged for this unit
     const int item = unit / tiles;               // < n_gemv <= E_local
-    const WorkEntry we = A.list[item];
+    const WorkEntry we = clamp_entry(A.list[item], A);
     const int tile = unit - item * tiles;
     const int tid = threadIdx.x, g = tid / kLanesPerRow, q = tid % kLanesPerRow;
     const int red = A.red, RB = red >> 5, RV = red >> 3;
@@ -160,7 +174,7 @@ __global__ __launch_bounds__(256, 4) void gemv_kernel(ExpertArgs A) {
           int tok = we.tok[0];
 #pragma unroll
           for (int u = 1; u < kGemvMaxTokens; ++u) tok = tt == u ? we.tok[u] : tok;
-          row = tt < kGemvMaxTokens ? tok : A.routes[we.p0 + tt] / A.top_k;
+          row = tt < kGemvMaxTokens ? tok : min(max(A.routes[we.p0 + tt] / A.top_k, 0), A.T - 1);
         }
         src_row[t] = reinterpret_cast<const uint4*>(A.in + static_cast<size_t>(row) * red);
       }
@@ -319,8 +333,9 @@ __global__ __launch_bounds__(256, (kGroups == 1 && !kBf16W) ? 3 : 2) void mfma_k
   const int xcd = static_cast<int>(blockIdx.x) & 7, kx = static_cast<int>(blockIdx.x) >> 3;
   const int item = xcd + 8 * (kx / tiles);
   const int tile = kx - (kx / tiles) * tiles;
-  const int n_items = A.plan->n_mfma;
-  const WorkEntry we = A.list[min(item, A.list_cap - 1)];  // in bounds; used only when item < n_items
+  if (A.plan->key != A.key) return;  // no plan for this call in the workspace (whole workgroup)
+  const int n_items = min(max(A.plan->n_mfma, 0), A.list_cap);
+  const WorkEntry we = clamp_entry(A.list[min(item, A.list_cap - 1)], A);  // in bounds; used only when item < n_items
   if (item >= n_items) return;  // whole workgroup
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, q = lane >> 4;
@@ -620,7 +635,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs A) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = t * k + min(i, k - 1);
-      p[i] = i < k ? A.pos[r] : -1;
+      const int pr = A.pos[r];
+      p[i] = (i < k && pr >= 0 && pr < A.T * k) ? pr : -1;
       wt[i] = A.weights[r];
 #pragma unroll
       for (int c = 0; c < kCols; ++c)
@@ -634,7 +650,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs A) {
   }
   if (tid < 64) {
     // k <= 64: lane j holds route j of the token
-    const int p = tid < k ? A.pos[t * k + tid] : -1;
+    int p = tid < k ? A.pos[t * k + tid] : -1;
+    p = p < A.T * k ? p : -1;  // a position outside the routes (stale workspace) is skipped
     const uint64_t m = __ballot(p >= 0);
     if (p >= 0) {
       const int i = __popcll(m & ((1ull << tid) - 1ull));
@@ -785,7 +802,7 @@ __global__ __launch_bounds__(256) void route_rows_kernel(const float* __restrict
   if (r >= R || k4 >= K) return;
   const int p = pos[r];
   float4* dst = reinterpret_cast<float4*>(out + static_cast<size_t>(r) * K + k4);
-  if (p < 0) {
+  if (p < 0 || p >= R) {
     *dst = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   } else if (!in_place) {
     *dst = *reinterpret_cast<const float4*>(o + static_cast<size_t>(p) * K + k4);
@@ -865,6 +882,27 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
       o[2 * c + 1] = make_float4(v[2][0], v[2][1], v[3][0], v[3][1]);
     }
   }
+}
+
+// Copy of the plan's routing and bucketing (test hook).  Thread i < R
+// copies route i (ids, weights, routes padded with -1 past the local routes);
+// thread i <= E_l copies expert i's count and offset.
+__global__ __launch_bounds__(256) void plan_read_kernel(const Plan* plan, const int32_t* __restrict__ ids_ws,
+                                                        const float* __restrict__ weights_ws,
+                                                        const int32_t* __restrict__ counts_ws,
+                                                        const int32_t* __restrict__ offsets_ws,
+                                                        const int32_t* __restrict__ routes_ws, int R, int E_l,
+                                                        int32_t* ids, float* weights, int32_t* counts,
+                                                        int32_t* offsets, int32_t* routes) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int Rl = min(max(plan->R_local, 0), R);
+  if (i < R) {
+    if (ids != nullptr) ids[i] = ids_ws[i];
+    if (weights != nullptr) weights[i] = weights_ws[i];
+    if (routes != nullptr) routes[i] = i < Rl ? routes_ws[i] : -1;
+  }
+  if (i < E_l && counts != nullptr) counts[i] = counts_ws[i];
+  if (i <= E_l && offsets != nullptr) offsets[i] = offsets_ws[i];
 }
 
 }  // namespace moe

@@ -53,14 +53,19 @@ struct PassEntry {
 };
 static_assert(sizeof(PassEntry) == 64, "PassEntry is 64 bytes");
 
-// Header of the device plan, at the start of the workspace.
+// Header of the device plan, at the start of the workspace.  `key` is the
+// host's key of the descriptor the plan was made for (plan_key() in the
+// host code); the expert kernels leave a plan with another key alone, so a
+// workspace that holds no plan for this call (never planned, or planned for
+// another shape) gives no output instead of out-of-range indices.
 struct Plan {
   int32_t n_touched;   // local experts with at least one route
   int32_t R_local;     // local routes
   int32_t n_gemv;      // experts in the GEMV list
   int32_t n_mfma;      // experts in the MFMA list
   int32_t n_passes;    // entries of the pass list (decode regime)
-  int32_t pad[59];
+  uint32_t key;        // descriptor key of the call that wrote this plan
+  int32_t pad[58];
 };
 
 struct PlanArgs {
@@ -82,6 +87,7 @@ struct PlanArgs {
   PassEntry* passes;       // pass list, or nullptr
   int pass_shift;          // routes per pass = 1 << pass_shift (<= kStreamPassTokens) when passes != nullptr
   Plan* plan;
+  uint32_t key;            // written to plan->key
   int32_t* routes_out;     // bucket hook: copy of routes padded with -1, or nullptr
 };
 
@@ -112,6 +118,8 @@ struct ExpertArgs {
   const WorkEntry* list;   // the kernel's expert list
   int list_cap;            // entries the list has room for (E_local)
   const Plan* plan;
+  uint32_t key;            // the plan is used only when plan->key == key
+  int T, R;                // tokens, routes (T * top_k): bounds of every plan-derived index
   int red;                 // reduction length: K (gate/up) or I (down)
   int rows;                // output rows per expert: I row pairs (gate/up) or K (down)
   int tiled;               // packed weights in the tiled layout
@@ -125,7 +133,7 @@ struct ExpertArgs {
 
 struct CombineArgs {
   const float* o;          // per-route down projections [R, K] fp32, row = plan position or route
-  const int32_t* pos;
+  const int32_t* pos;      // plan position of each route, -1 when not local; values outside [0, T*top_k) are skipped
   const float* weights;
   uint16_t* out;
   int T, K, top_k;
@@ -142,6 +150,9 @@ struct StreamArgs {
   const uint16_t* bias;      // [E_l][rows_e] bf16, or nullptr
   const PassEntry* passes;
   const Plan* plan;
+  uint32_t key;              // the plan is used only when plan->key == key
+  int max_passes;            // host bound on the plan's pass count (entries the pass list holds)
+  int E_local, R;            // bounds of the pass entries' expert, position and route fields
   int red;                   // reduction length: K (gate/up) or I (down)
   int rows;                  // output rows per expert: I row pairs (gate/up) or K (down)
   int tok_from_pass;         // 1: activation row = token of the entry's route (gate/up); 0: row = plan position (down)
@@ -188,6 +199,13 @@ __global__ void combine_kernel(CombineArgs A);
 // zeros; with in_place == 0 the others are copied from o (plan order) to
 // their route's row.
 __global__ void route_rows_kernel(const float* o, const int32_t* pos, float* out, int R, int K, int in_place);
+// Copy of a plan's routing and bucketing (test hook): ids/weights [R], counts
+// [E_l], offsets [E_l + 1], routes [R] padded with -1 past the local routes;
+// null outputs are skipped.  One workgroup of 256 threads per 256 routes or experts.
+__global__ void plan_read_kernel(const Plan* plan, const int32_t* ids_ws, const float* weights_ws,
+                                 const int32_t* counts_ws, const int32_t* offsets_ws, const int32_t* routes_ws, int R,
+                                 int E_l, int32_t* ids, float* weights, int32_t* counts, int32_t* offsets,
+                                 int32_t* routes);
 // In-place row layout <-> tiled layout, one workgroup per 16-row group.
 __global__ void tile_kernel(uint8_t* packed, int64_t groups, int blocks, int inverse);
 // MXFP4 encoder, four lanes per 32-value block (bf16 or fp32 input); each

@@ -11,6 +11,8 @@
 #include <cstddef>
 #include <cstdint>
 #include <mutex>
+#include <tuple>
+#include <utility>
 
 #include "kernels.h"
 #include "moe_mxfp4.h"
@@ -86,7 +88,28 @@ int check_workspace(const moe_mxfp4_desc& d, const void* ws, size_t ws_bytes) {
   return MOE_OK;
 }
 
-int launch_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+// kernel<<<grid, block, lds, s>>>(args...) through hipLaunchKernel, which
+// returns the status of this launch only (an error left by other work on the
+// thread is neither reported nor cleared).
+template <typename... P, typename... A>
+hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s, A&&... args) {
+  std::tuple<P...> vals{std::forward<A>(args)...};
+  return std::apply(
+      [&](auto&... v) {
+        void* ptrs[] = {static_cast<void*>(&v)...};
+        return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, lds, s);
+      },
+      vals);
+}
+
+// Status of a sequence of enqueues: MOE_ERR_HIP at the first failed launch
+// (the launches before it stay enqueued).
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+#define MOE_TRY(expr)                      \
+  do {                                     \
+    const hipError_t moe_e_ = (expr);      \
+    if (moe_e_ != hipSuccess) return moe_e_; \
+  } while (0)
 
 template <typename T>
 T* at(void* ws, size_t off) {
@@ -170,6 +193,24 @@ int resident_workgroups(K kernel, size_t lds) {
   return n;
 }
 
+// Key of the plan a call makes: every descriptor field and regime choice
+// that shapes the plan (FNV-1a; never 0, the key of "no plan").  The expert
+// kernels compare it with the key the plan kernel stored in the workspace.
+uint32_t plan_key(const moe_mxfp4_desc& d, bool prefill) {
+  const int split = prefill ? 0 : stream_split(d);
+  const int32_t f[] = {d.T, d.K, d.I, d.E_global, d.E_local, d.expert_offset, d.top_k, split, prefill ? 1 : 0,
+                       mfma_enabled(d) ? 1 : 0, static_cast<int32_t>(stream_fits(d.K, split)),
+                       static_cast<int32_t>(stream_fits(d.I, split))};
+  uint32_t h = 2166136261u;
+  for (int32_t v : f) {
+    for (int b = 0; b < 4; ++b) {
+      h ^= (static_cast<uint32_t>(v) >> (8 * b)) & 0xFFu;
+      h *= 16777619u;
+    }
+  }
+  return h | 1u;
+}
+
 moe::PlanArgs plan_args(const moe_mxfp4_desc& d, void* ws) {
   const Layout L = make_layout(d);
   moe::PlanArgs P{};
@@ -191,16 +232,18 @@ moe::PlanArgs plan_args(const moe_mxfp4_desc& d, void* ws) {
   P.gemv_list = at<moe::WorkEntry>(ws, L.gemv_list);
   P.mfma_list = at<moe::WorkEntry>(ws, L.mfma_list);
   P.plan = at<Plan>(ws, L.plan);
+  P.key = plan_key(d, false);
   return P;
 }
 
 // Routing and bucketing into the workspace.  Small calls route inside the
 // plan kernel; larger ones route with one wave per token first.  The prefill
 // path puts every touched expert in the MFMA list and needs no pass list.
-void enqueue_plan(const moe_mxfp4_desc& d, const float* logits, const int32_t* ids, const float* wts, void* ws,
-                  hipStream_t s, bool prefill = false) {
+hipError_t enqueue_plan(const moe_mxfp4_desc& d, const float* logits, const int32_t* ids, const float* wts, void* ws,
+                        hipStream_t s, bool prefill = false) {
   moe::PlanArgs P = plan_args(d, ws);
   const int split = prefill ? 0 : stream_split(d);
+  P.key = plan_key(d, prefill);
   if (prefill) {
     P.mfma_enabled = 1;
     P.gemv_max = 0;
@@ -214,24 +257,25 @@ void enqueue_plan(const moe_mxfp4_desc& d, const float* logits, const int32_t* i
   if (logits != nullptr && d.T <= moe::kFusedRouteTokens) {
     P.logits = logits;
   } else if (logits != nullptr) {
-    hipLaunchKernelGGL(moe::route_topk_kernel, dim3((d.T + 3) / 4), dim3(256), 0, s, logits, d.T, d.E_global,
-                       d.top_k, d.scoring, P.ids_ws, P.weights_ws);
+    MOE_TRY(launch(moe::route_topk_kernel, dim3((d.T + 3) / 4), dim3(256), 0, s, logits, d.T, d.E_global, d.top_k,
+                   d.scoring, P.ids_ws, P.weights_ws));
     P.ids_in = P.ids_ws;
   } else {
     P.ids_in = ids;
     P.w_in = wts;
   }
-  hipLaunchKernelGGL(moe::plan_kernel, dim3(1), dim3(1024), 0, s, P);
+  return launch(moe::plan_kernel, dim3(1), dim3(1024), 0, s, P);
 }
 
-void enqueue_bucket_hook(const moe_mxfp4_desc& d, const int32_t* ids, void* ws, hipStream_t s, int32_t* counts,
-                         int32_t* offsets, int32_t* routes_out) {
+hipError_t enqueue_bucket_hook(const moe_mxfp4_desc& d, const int32_t* ids, void* ws, hipStream_t s, int32_t* counts,
+                               int32_t* offsets, int32_t* routes_out) {
   moe::PlanArgs P = plan_args(d, ws);
   P.ids_in = ids;
   P.counts = counts;
   P.offsets = offsets;
   P.routes_out = routes_out;
-  hipLaunchKernelGGL(moe::plan_kernel, dim3(1), dim3(1024), 0, s, P);
+  P.key = 0;  // counts and offsets go to the caller: the workspace holds no usable plan
+  return launch(moe::plan_kernel, dim3(1), dim3(1024), 0, s, P);
 }
 
 // Both regimes of one projection.  Grids are host-side upper bounds: at most
@@ -241,8 +285,8 @@ void enqueue_bucket_hook(const moe_mxfp4_desc& d, const int32_t* ids, void* ws, 
 // token pairs if repeated ids give an expert more routes); otherwise experts
 // with more than G routes are in the MFMA list, whose token groups per pass
 // follow T.
-void enqueue_expert_pair(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs A, const Layout& L, void* ws,
-                         hipStream_t s) {
+hipError_t enqueue_expert_pair(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs A, const Layout& L, void* ws,
+                               hipStream_t s) {
   const int64_t touched = tokens_bound(d);
   const int rows = A.rows, red = A.red;
   const int lanes = red > 4096 ? 32 : 16;
@@ -250,6 +294,7 @@ void enqueue_expert_pair(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs 
   {
     moe::ExpertArgs G = A;
     G.list = at<moe::WorkEntry>(ws, L.gemv_list);
+    G.list_cap = d.E_local;
     const size_t lds = static_cast<size_t>(moe::kGemvMaxTokens) * red * 2 +
                        static_cast<size_t>(gate_up ? 2 : 1) * rows_per_wg * (red / 32);
     // the kernel takes its (entry, row tile) units grid-stride: the grid is
@@ -262,11 +307,11 @@ void enqueue_expert_pair(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs 
     if (resident > 0) grid = std::min<int64_t>(grid, resident);
     const dim3 g(static_cast<unsigned>(grid));
     if (gate_up) {
-      if (lanes == 16) hipLaunchKernelGGL((moe::gemv_kernel<true, 16>), g, dim3(256), lds, s, G);
-      else hipLaunchKernelGGL((moe::gemv_kernel<true, 32>), g, dim3(256), lds, s, G);
+      if (lanes == 16) MOE_TRY(launch(moe::gemv_kernel<true, 16>, g, dim3(256), lds, s, G));
+      else MOE_TRY(launch(moe::gemv_kernel<true, 32>, g, dim3(256), lds, s, G));
     } else {
-      if (lanes == 16) hipLaunchKernelGGL((moe::gemv_kernel<false, 16>), g, dim3(256), lds, s, G);
-      else hipLaunchKernelGGL((moe::gemv_kernel<false, 32>), g, dim3(256), lds, s, G);
+      if (lanes == 16) MOE_TRY(launch(moe::gemv_kernel<false, 16>, g, dim3(256), lds, s, G));
+      else MOE_TRY(launch(moe::gemv_kernel<false, 32>, g, dim3(256), lds, s, G));
     }
   }
   const int64_t R = static_cast<int64_t>(d.T) * d.top_k;
@@ -287,10 +332,9 @@ void enqueue_expert_pair(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs 
     const int64_t slots = (mfma_experts + 7) / 8 * 8;
     if (gate_up) {
       const dim3 g(static_cast<unsigned>(slots * ((rows + moe::kMfmaRows - 1) / moe::kMfmaRows)));
-      if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<true, 1, false, false>), g, dim3(256), lds, s, M);
-      else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<true, 2, false, false>), g, dim3(256), lds, s, M);
-      else hipLaunchKernelGGL((moe::mfma_kernel<true, 4, false, false>), g, dim3(256), lds, s, M);
-      return;
+      if (groups == 1) return launch(moe::mfma_kernel<true, 1, false, false>, g, dim3(256), lds, s, M);
+      if (groups == 2) return launch(moe::mfma_kernel<true, 2, false, false>, g, dim3(256), lds, s, M);
+      return launch(moe::mfma_kernel<true, 4, false, false>, g, dim3(256), lds, s, M);
     }
     bool pair = rows % 32 == 0 && d.down_pairing != MOE_PAIRING_OFF;
     const int64_t grid2 = slots * ((rows + 2 * moe::kMfmaRows - 1) / (2 * moe::kMfmaRows));
@@ -302,16 +346,16 @@ void enqueue_expert_pair(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs 
     }
     if (pair) {
       const dim3 g(static_cast<unsigned>(grid2));
-      if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<false, 1, false, true>), g, dim3(256), lds, s, M);
-      else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<false, 2, false, true>), g, dim3(256), lds, s, M);
-      else hipLaunchKernelGGL((moe::mfma_kernel<false, 4, false, true>), g, dim3(256), lds, s, M);
-    } else {
-      const dim3 g(static_cast<unsigned>(slots * ((rows + moe::kMfmaRows - 1) / moe::kMfmaRows)));
-      if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<false, 1, false, false>), g, dim3(256), lds1, s, M);
-      else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<false, 2, false, false>), g, dim3(256), lds1, s, M);
-      else hipLaunchKernelGGL((moe::mfma_kernel<false, 4, false, false>), g, dim3(256), lds1, s, M);
+      if (groups == 1) return launch(moe::mfma_kernel<false, 1, false, true>, g, dim3(256), lds, s, M);
+      if (groups == 2) return launch(moe::mfma_kernel<false, 2, false, true>, g, dim3(256), lds, s, M);
+      return launch(moe::mfma_kernel<false, 4, false, true>, g, dim3(256), lds, s, M);
     }
+    const dim3 g(static_cast<unsigned>(slots * ((rows + moe::kMfmaRows - 1) / moe::kMfmaRows)));
+    if (groups == 1) return launch(moe::mfma_kernel<false, 1, false, false>, g, dim3(256), lds1, s, M);
+    if (groups == 2) return launch(moe::mfma_kernel<false, 2, false, false>, g, dim3(256), lds1, s, M);
+    return launch(moe::mfma_kernel<false, 4, false, false>, g, dim3(256), lds1, s, M);
   }
+  return hipSuccess;
 }
 
 // Prefill: the touched experts' weights, unpacked to bf16 in the workspace
@@ -327,20 +371,21 @@ PrefillLayout prefill_layout(const moe_mxfp4_desc& d) {
   return P;
 }
 
-void enqueue_unpack(const moe_mxfp4_desc& d, const uint8_t* w13p, const uint8_t* w13s, const uint8_t* w2p,
-                    const uint8_t* w2s, const int32_t* counts, uint16_t* w13_out, uint16_t* w2_out, hipStream_t s) {
+hipError_t enqueue_unpack(const moe_mxfp4_desc& d, const uint8_t* w13p, const uint8_t* w13s, const uint8_t* w2p,
+                          const uint8_t* w2s, const int32_t* counts, uint16_t* w13_out, uint16_t* w2_out,
+                          hipStream_t s) {
   const int tiled = d.weight_layout == MOE_LAYOUT_TILE16;
   const int64_t b13 = static_cast<int64_t>(2) * d.I * (d.K / 32), b2 = static_cast<int64_t>(d.K) * (d.I / 32);
-  hipLaunchKernelGGL(moe::unpack_kernel, dim3(static_cast<unsigned>((b13 + 255) / 256), d.E_local), dim3(256), 0, s,
-                     w13p, w13s, 2 * d.I, d.K, tiled, counts, w13_out);
-  hipLaunchKernelGGL(moe::unpack_kernel, dim3(static_cast<unsigned>((b2 + 255) / 256), d.E_local), dim3(256), 0, s,
-                     w2p, w2s, d.K, d.I, tiled, counts, w2_out);
+  MOE_TRY(launch(moe::unpack_kernel, dim3(static_cast<unsigned>((b13 + 255) / 256), d.E_local), dim3(256), 0, s, w13p,
+                 w13s, 2 * d.I, d.K, tiled, counts, w13_out));
+  return launch(moe::unpack_kernel, dim3(static_cast<unsigned>((b2 + 255) / 256), d.E_local), dim3(256), 0, s, w2p,
+                w2s, d.K, d.I, tiled, counts, w2_out);
 }
 
 // The MFMA kernel on the unpacked weights for every touched expert (the plan
 // of the prefill path lists them all).
-void enqueue_mfma_bf16(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs M, const Layout& L, void* ws,
-                       hipStream_t s) {
+hipError_t enqueue_mfma_bf16(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs M, const Layout& L, void* ws,
+                             hipStream_t s) {
   const int64_t R = static_cast<int64_t>(d.T) * d.top_k;
   const int64_t experts = std::min<int64_t>(d.E_local, R);
   M.list = at<moe::WorkEntry>(ws, L.mfma_list);
@@ -351,14 +396,13 @@ void enqueue_mfma_bf16(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs M,
                      static_cast<size_t>(gate_up ? 2 : 1) * moe::kMfmaRows * (M.red / 32);
   const dim3 g(static_cast<unsigned>(grid));
   if (gate_up) {
-    if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<true, 1, true, false>), g, dim3(256), lds, s, M);
-    else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<true, 2, true, false>), g, dim3(256), lds, s, M);
-    else hipLaunchKernelGGL((moe::mfma_kernel<true, 4, true, false>), g, dim3(256), lds, s, M);
-  } else {
-    if (groups == 1) hipLaunchKernelGGL((moe::mfma_kernel<false, 1, true, false>), g, dim3(256), lds, s, M);
-    else if (groups == 2) hipLaunchKernelGGL((moe::mfma_kernel<false, 2, true, false>), g, dim3(256), lds, s, M);
-    else hipLaunchKernelGGL((moe::mfma_kernel<false, 4, true, false>), g, dim3(256), lds, s, M);
+    if (groups == 1) return launch(moe::mfma_kernel<true, 1, true, false>, g, dim3(256), lds, s, M);
+    if (groups == 2) return launch(moe::mfma_kernel<true, 2, true, false>, g, dim3(256), lds, s, M);
+    return launch(moe::mfma_kernel<true, 4, true, false>, g, dim3(256), lds, s, M);
   }
+  if (groups == 1) return launch(moe::mfma_kernel<false, 1, true, false>, g, dim3(256), lds, s, M);
+  if (groups == 2) return launch(moe::mfma_kernel<false, 2, true, false>, g, dim3(256), lds, s, M);
+  return launch(moe::mfma_kernel<false, 4, true, false>, g, dim3(256), lds, s, M);
 }
 
 // One projection in the decode regime.  Items: n_passes x tiles of
@@ -370,6 +414,7 @@ void enqueue_mfma_bf16(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs M,
 struct StreamGrid {
   size_t lds;
   int64_t bound;  // items
+  int64_t passes; // host bound on the plan's pass count
   int resident;
 };
 
@@ -381,18 +426,19 @@ StreamGrid stream_grid(const moe_mxfp4_desc& d, const moe::StreamArgs& S) {
   const int64_t tp = moe::kStreamPassTokens / kSplit;
   const int64_t passes = std::min<int64_t>(R, (R + tokens_bound(d) * (tp - 1)) / tp);
   const int item_rows = (kPair ? 128 : 64) / kSplit;
+  G.passes = passes;
   G.bound = passes * ((S.rows + item_rows - 1) / item_rows);
   G.resident = resident_workgroups(moe::stream_kernel<kGateUp, kSplit, kPair>, G.lds);
   return G;
 }
 
 template <bool kGateUp, int kSplit, bool kPair>
-void launch_stream(const StreamGrid& G, const moe::StreamArgs& S, hipStream_t s) {
+hipError_t launch_stream(const StreamGrid& G, moe::StreamArgs S, hipStream_t s) {
   int64_t grid = std::max<int64_t>(G.resident > 0 ? G.resident : 1024,
                                    (G.bound + moe::kStreamMaxItems - 1) / moe::kStreamMaxItems);
   grid = std::max<int64_t>(1, std::min<int64_t>(grid, G.bound));
-  hipLaunchKernelGGL((moe::stream_kernel<kGateUp, kSplit, kPair>), dim3(static_cast<unsigned>(grid)), dim3(256), G.lds,
-                     s, S);
+  S.max_passes = static_cast<int>(G.passes);
+  return launch(moe::stream_kernel<kGateUp, kSplit, kPair>, dim3(static_cast<unsigned>(grid)), dim3(256), G.lds, s, S);
 }
 
 // The down projection runs in pairs of 16-row sets per wave (two weight loads
@@ -401,28 +447,28 @@ void launch_stream(const StreamGrid& G, const moe::StreamArgs& S, hipStream_t s)
 // slot; otherwise (few touched experts) the unpaired items keep more of the
 // chip streaming.
 template <bool kGateUp, int kSplit>
-void launch_stream_proj(const moe_mxfp4_desc& d, const moe::StreamArgs& S, hipStream_t s) {
+hipError_t launch_stream_proj(const moe_mxfp4_desc& d, const moe::StreamArgs& S, hipStream_t s) {
   if (!kGateUp && S.rows % 32 == 0 && d.down_pairing != MOE_PAIRING_OFF) {
     const StreamGrid G = stream_grid<false, kSplit, true>(d, S);
-    if (d.down_pairing == MOE_PAIRING_ON || G.bound >= G.resident) {
-      launch_stream<false, kSplit, true>(G, S, s);
-      return;
-    }
+    if (d.down_pairing == MOE_PAIRING_ON || G.bound >= G.resident) return launch_stream<false, kSplit, true>(G, S, s);
   }
-  launch_stream<kGateUp, kSplit, false>(stream_grid<kGateUp, kSplit, false>(d, S), S, s);
+  return launch_stream<kGateUp, kSplit, false>(stream_grid<kGateUp, kSplit, false>(d, S), S, s);
 }
 
 template <bool kGateUp>
-void enqueue_stream(const moe_mxfp4_desc& d, int split, const moe::StreamArgs& S, hipStream_t s) {
-  if (split == 4) launch_stream_proj<kGateUp, 4>(d, S, s);
-  else if (split == 2) launch_stream_proj<kGateUp, 2>(d, S, s);
-  else launch_stream_proj<kGateUp, 1>(d, S, s);
+hipError_t enqueue_stream(const moe_mxfp4_desc& d, int split, const moe::StreamArgs& S, hipStream_t s) {
+  if (split == 4) return launch_stream_proj<kGateUp, 4>(d, S, s);
+  if (split == 2) return launch_stream_proj<kGateUp, 2>(d, S, s);
+  return launch_stream_proj<kGateUp, 1>(d, S, s);
 }
 
 moe::StreamArgs stream_args(const moe_mxfp4_desc& d, const Layout& L, void* ws) {
   moe::StreamArgs S{};
   S.passes = at<moe::PassEntry>(ws, L.passes);
   S.plan = at<Plan>(ws, L.plan);
+  S.key = plan_key(d, false);
+  S.E_local = d.E_local;
+  S.R = d.T * d.top_k;
   S.act_kind = d.activation;
   S.alpha = d.swiglu_alpha;
   S.limit = d.swiglu_limit;
@@ -431,8 +477,16 @@ moe::StreamArgs stream_args(const moe_mxfp4_desc& d, const Layout& L, void* ws) 
   return S;
 }
 
-void enqueue_w13(const moe_mxfp4_desc& d, const uint16_t* x, const uint8_t* w13p, const uint8_t* w13s,
-                 const uint16_t* b13, uint16_t* a, void* ws, hipStream_t s) {
+// Bounds and plan key of the list kernels' arguments.
+void set_list_bounds(const moe_mxfp4_desc& d, moe::ExpertArgs& A, bool prefill) {
+  A.key = plan_key(d, prefill);
+  A.T = d.T;
+  A.R = d.T * d.top_k;
+  A.list_cap = d.E_local;
+}
+
+hipError_t enqueue_w13(const moe_mxfp4_desc& d, const uint16_t* x, const uint8_t* w13p, const uint8_t* w13s,
+                       const uint16_t* b13, uint16_t* a, void* ws, hipStream_t s) {
   const Layout L = make_layout(d);
   moe::ExpertArgs A{};
   A.in = x;
@@ -451,6 +505,7 @@ void enqueue_w13(const moe_mxfp4_desc& d, const uint16_t* x, const uint8_t* w13p
   A.act_kind = d.activation;
   A.alpha = d.swiglu_alpha;
   A.limit = d.swiglu_limit;
+  set_list_bounds(d, A, false);
   const int split = stream_split(d);
   if (stream_fits(d.K, split)) {
     moe::StreamArgs S = stream_args(d, L, ws);
@@ -464,26 +519,23 @@ void enqueue_w13(const moe_mxfp4_desc& d, const uint16_t* x, const uint8_t* w13p
     S.tok_from_pass = 1;
     S.il = A.il;
     S.a_out = A.a_out;
-    enqueue_stream<true>(d, split, S, s);
-    return;
+    return enqueue_stream<true>(d, split, S, s);
   }
-  enqueue_expert_pair(d, true, A, L, ws, s);
+  return enqueue_expert_pair(d, true, A, L, ws, s);
 }
 
 // Token sums: 1024 columns of a token per workgroup for small calls (several
 // workgroups share a token), 4096 for large ones (fewer, longer workgroups).
-void launch_combine(const moe_mxfp4_desc& d, const moe::CombineArgs& C, hipStream_t s) {
-  if (d.T <= moe::kStreamMaxTokens) {
-    hipLaunchKernelGGL(moe::combine_kernel<1>, dim3(d.T, (d.K + 1023) / 1024), dim3(256), 0, s, C);
-  } else {
-    hipLaunchKernelGGL(moe::combine_kernel<4>, dim3(d.T, (d.K + 4095) / 4096), dim3(256), 0, s, C);
-  }
+hipError_t launch_combine(const moe_mxfp4_desc& d, const moe::CombineArgs& C, hipStream_t s) {
+  if (d.T <= moe::kStreamMaxTokens)
+    return launch(moe::combine_kernel<1>, dim3(d.T, (d.K + 1023) / 1024), dim3(256), 0, s, C);
+  return launch(moe::combine_kernel<4>, dim3(d.T, (d.K + 4095) / 4096), dim3(256), 0, s, C);
 }
 
 // The down projection, then either the per-token combine into out (bf16
 // [T, K]) or, with out_routes, the per-route rows (fp32 [T*top_k, K]).
-void enqueue_w2(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_t* w2p, const uint8_t* w2s,
-                const uint16_t* b2, uint16_t* out, float* out_routes, void* ws, hipStream_t s) {
+hipError_t enqueue_w2(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_t* w2p, const uint8_t* w2s,
+                      const uint16_t* b2, uint16_t* out, float* out_routes, void* ws, hipStream_t s) {
   const Layout L = make_layout(d);
   moe::ExpertArgs A{};
   A.in = a != nullptr ? a : at<uint16_t>(ws, L.a);
@@ -498,6 +550,7 @@ void enqueue_w2(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_t* w2p, 
   A.rows = d.K;
   A.tiled = d.weight_layout == MOE_LAYOUT_TILE16;
   A.o_out = at<float>(ws, L.o);
+  set_list_bounds(d, A, false);
   moe::CombineArgs C;
   C.o = at<float>(ws, L.o);
   C.pos = at<int32_t>(ws, L.pos);
@@ -523,16 +576,14 @@ void enqueue_w2(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_t* w2p, 
     S.tok_from_pass = 0;
     S.o_by_route = 1;
     S.o_out = A.o_out;
-    enqueue_stream<false>(d, split, S, s);
+    MOE_TRY(enqueue_stream<false>(d, split, S, s));
   } else {
-    enqueue_expert_pair(d, false, A, L, ws, s);
+    MOE_TRY(enqueue_expert_pair(d, false, A, L, ws, s));
   }
-  if (out_routes != nullptr) {
-    hipLaunchKernelGGL(moe::route_rows_kernel, dim3((d.K / 4 + 255) / 256, R), dim3(256), 0, s, C.o, C.pos,
-                       out_routes, R, d.K, C.by_route);
-  } else {
-    launch_combine(d, C, s);
-  }
+  if (out_routes != nullptr)
+    return launch(moe::route_rows_kernel, dim3((d.K / 4 + 255) / 256, R), dim3(256), 0, s, static_cast<const float*>(C.o),
+                  static_cast<const int32_t*>(C.pos), out_routes, R, d.K, C.by_route);
+  return launch_combine(d, C, s);
 }
 
 int check_routing(const moe_mxfp4_desc& d, const float* logits, const int32_t* ids, const float* wts) {
@@ -572,10 +623,10 @@ int moe_mxfp4_decode(const moe_mxfp4_desc* desc, const uint16_t* x, const float*
     return MOE_ERR_ALIGN;
   if ((st = check_workspace(d, workspace, workspace_bytes)) != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  enqueue_plan(d, router_logits, topk_ids, topk_weights, workspace, s);
-  enqueue_w13(d, x, w13_packed, w13_scales, w13_bias, nullptr, workspace, s);
-  enqueue_w2(d, nullptr, w2_packed, w2_scales, w2_bias, out, nullptr, workspace, s);
-  return launch_status();
+  hipError_t e = enqueue_plan(d, router_logits, topk_ids, topk_weights, workspace, s);
+  if (e == hipSuccess) e = enqueue_w13(d, x, w13_packed, w13_scales, w13_bias, nullptr, workspace, s);
+  if (e == hipSuccess) e = enqueue_w2(d, nullptr, w2_packed, w2_scales, w2_bias, out, nullptr, workspace, s);
+  return hip_status(e);
 }
 
 int moe_mxfp4_decode_routes(const moe_mxfp4_desc* desc, const uint16_t* x, const float* router_logits,
@@ -594,10 +645,10 @@ int moe_mxfp4_decode_routes(const moe_mxfp4_desc* desc, const uint16_t* x, const
     return MOE_ERR_ALIGN;
   if ((st = check_workspace(d, workspace, workspace_bytes)) != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  enqueue_plan(d, router_logits, topk_ids, topk_weights, workspace, s);
-  enqueue_w13(d, x, w13_packed, w13_scales, w13_bias, nullptr, workspace, s);
-  enqueue_w2(d, nullptr, w2_packed, w2_scales, w2_bias, nullptr, out_routes, workspace, s);
-  return launch_status();
+  hipError_t e = enqueue_plan(d, router_logits, topk_ids, topk_weights, workspace, s);
+  if (e == hipSuccess) e = enqueue_w13(d, x, w13_packed, w13_scales, w13_bias, nullptr, workspace, s);
+  if (e == hipSuccess) e = enqueue_w2(d, nullptr, w2_packed, w2_scales, w2_bias, nullptr, out_routes, workspace, s);
+  return hip_status(e);
 }
 
 int moe_mxfp4_prefill_workspace_bytes(const moe_mxfp4_desc* desc, size_t* bytes) {
@@ -630,8 +681,9 @@ int moe_mxfp4_prefill(const moe_mxfp4_desc* desc, const uint16_t* x, const float
   const Layout L = make_layout(d);
   uint16_t* w13u = at<uint16_t>(workspace, PL.w13);
   uint16_t* w2u = at<uint16_t>(workspace, PL.w2);
-  enqueue_plan(d, router_logits, topk_ids, topk_weights, workspace, s, true);
-  enqueue_unpack(d, w13_packed, w13_scales, w2_packed, w2_scales, at<int32_t>(workspace, L.counts), w13u, w2u, s);
+  hipError_t e = enqueue_plan(d, router_logits, topk_ids, topk_weights, workspace, s, true);
+  if (e == hipSuccess)
+    e = enqueue_unpack(d, w13_packed, w13_scales, w2_packed, w2_scales, at<int32_t>(workspace, L.counts), w13u, w2u, s);
   moe::ExpertArgs A{};
   A.in = x;
   A.in_bytes = static_cast<uint32_t>(static_cast<size_t>(d.T) * d.K * 2);
@@ -648,7 +700,8 @@ int moe_mxfp4_prefill(const moe_mxfp4_desc* desc, const uint16_t* x, const float
   A.act_kind = d.activation;
   A.alpha = d.swiglu_alpha;
   A.limit = d.swiglu_limit;
-  enqueue_mfma_bf16(d, true, A, L, workspace, s);
+  set_list_bounds(d, A, true);
+  if (e == hipSuccess) e = enqueue_mfma_bf16(d, true, A, L, workspace, s);
   moe::ExpertArgs B{};
   B.in = A.a_out;
   B.in_bytes = static_cast<uint32_t>(static_cast<size_t>(d.T) * d.top_k * d.I * 2);
@@ -660,7 +713,8 @@ int moe_mxfp4_prefill(const moe_mxfp4_desc* desc, const uint16_t* x, const float
   B.rows = d.K;
   B.wbf = w2u;
   B.o_out = at<float>(workspace, L.o);
-  enqueue_mfma_bf16(d, false, B, L, workspace, s);
+  set_list_bounds(d, B, true);
+  if (e == hipSuccess) e = enqueue_mfma_bf16(d, false, B, L, workspace, s);
   moe::CombineArgs C;
   C.o = B.o_out;
   C.pos = at<int32_t>(workspace, L.pos);
@@ -670,8 +724,8 @@ int moe_mxfp4_prefill(const moe_mxfp4_desc* desc, const uint16_t* x, const float
   C.K = d.K;
   C.top_k = d.top_k;
   C.by_route = 0;
-  launch_combine(d, C, s);
-  return launch_status();
+  if (e == hipSuccess) e = launch_combine(d, C, s);
+  return hip_status(e);
 }
 
 int moe_mxfp4_unpack(const moe_mxfp4_desc* desc, const uint8_t* w13_packed, const uint8_t* w13_scales,
@@ -684,9 +738,9 @@ int moe_mxfp4_unpack(const moe_mxfp4_desc* desc, const uint8_t* w13_packed, cons
   if (!aligned16(w13_packed) || !aligned16(w2_packed) || !aligned16(w13_out) || !aligned16(w2_out))
     return MOE_ERR_ALIGN;
   if ((st = check_workspace(*desc, workspace, workspace_bytes)) != MOE_OK) return st;
-  enqueue_unpack(*desc, w13_packed, w13_scales, w2_packed, w2_scales,
-                 at<int32_t>(workspace, make_layout(*desc).counts), w13_out, w2_out, static_cast<hipStream_t>(stream));
-  return launch_status();
+  return hip_status(enqueue_unpack(*desc, w13_packed, w13_scales, w2_packed, w2_scales,
+                                   at<int32_t>(workspace, make_layout(*desc).counts), w13_out, w2_out,
+                                   static_cast<hipStream_t>(stream)));
 }
 
 int moe_mxfp4_plan(const moe_mxfp4_desc* desc, const float* router_logits, const int32_t* topk_ids,
@@ -696,8 +750,8 @@ int moe_mxfp4_plan(const moe_mxfp4_desc* desc, const float* router_logits, const
   if ((st = check_routing(*desc, router_logits, topk_ids, topk_weights)) != MOE_OK) return st;
   if (desc->T == 0) return MOE_OK;
   if ((st = check_workspace(*desc, workspace, workspace_bytes)) != MOE_OK) return st;
-  enqueue_plan(*desc, router_logits, topk_ids, topk_weights, workspace, static_cast<hipStream_t>(stream));
-  return launch_status();
+  return hip_status(
+      enqueue_plan(*desc, router_logits, topk_ids, topk_weights, workspace, static_cast<hipStream_t>(stream)));
 }
 
 int moe_mxfp4_gate_up(const moe_mxfp4_desc* desc, const uint16_t* x, const uint8_t* w13_packed,
@@ -710,8 +764,8 @@ int moe_mxfp4_gate_up(const moe_mxfp4_desc* desc, const uint16_t* x, const uint8
   if (!aligned16(x) || !aligned16(w13_packed) || !aligned16(w13_scales) || !aligned16(w13_bias) || !aligned16(a))
     return MOE_ERR_ALIGN;
   if ((st = check_workspace(*desc, workspace, workspace_bytes)) != MOE_OK) return st;
-  enqueue_w13(*desc, x, w13_packed, w13_scales, w13_bias, a, workspace, static_cast<hipStream_t>(stream));
-  return launch_status();
+  return hip_status(
+      enqueue_w13(*desc, x, w13_packed, w13_scales, w13_bias, a, workspace, static_cast<hipStream_t>(stream)));
 }
 
 int moe_mxfp4_down(const moe_mxfp4_desc* desc, const uint16_t* a, const uint8_t* w2_packed,
@@ -724,8 +778,8 @@ int moe_mxfp4_down(const moe_mxfp4_desc* desc, const uint16_t* a, const uint8_t*
   if (!aligned16(a) || !aligned16(w2_packed) || !aligned16(w2_scales) || !aligned16(w2_bias) || !aligned16(out))
     return MOE_ERR_ALIGN;
   if ((st = check_workspace(*desc, workspace, workspace_bytes)) != MOE_OK) return st;
-  enqueue_w2(*desc, a, w2_packed, w2_scales, w2_bias, out, nullptr, workspace, static_cast<hipStream_t>(stream));
-  return launch_status();
+  return hip_status(
+      enqueue_w2(*desc, a, w2_packed, w2_scales, w2_bias, out, nullptr, workspace, static_cast<hipStream_t>(stream)));
 }
 
 int moe_mxfp4_down_routes(const moe_mxfp4_desc* desc, const uint16_t* a, const uint8_t* w2_packed,
@@ -738,9 +792,8 @@ int moe_mxfp4_down_routes(const moe_mxfp4_desc* desc, const uint16_t* a, const u
   if (!aligned16(a) || !aligned16(w2_packed) || !aligned16(w2_scales) || !aligned16(w2_bias) || !aligned16(out_routes))
     return MOE_ERR_ALIGN;
   if ((st = check_workspace(*desc, workspace, workspace_bytes)) != MOE_OK) return st;
-  enqueue_w2(*desc, a, w2_packed, w2_scales, w2_bias, nullptr, out_routes, workspace,
-             static_cast<hipStream_t>(stream));
-  return launch_status();
+  return hip_status(enqueue_w2(*desc, a, w2_packed, w2_scales, w2_bias, nullptr, out_routes, workspace,
+                              static_cast<hipStream_t>(stream)));
 }
 
 int moe_mxfp4_route(const moe_mxfp4_desc* desc, const float* router_logits, int32_t* topk_ids,
@@ -750,10 +803,9 @@ int moe_mxfp4_route(const moe_mxfp4_desc* desc, const float* router_logits, int3
   if (desc->E_global > moe::kMaxGlobalExpertsRouted) return MOE_ERR_SHAPE;
   if (desc->T == 0) return MOE_OK;
   if (!router_logits || !topk_ids || !topk_weights) return MOE_ERR_NULL;
-  hipLaunchKernelGGL(moe::route_topk_kernel, dim3((desc->T + 3) / 4), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), router_logits, desc->T, desc->E_global, desc->top_k,
-                     desc->scoring, topk_ids, topk_weights);
-  return launch_status();
+  return hip_status(launch(moe::route_topk_kernel, dim3((desc->T + 3) / 4), dim3(256), 0,
+                           static_cast<hipStream_t>(stream), router_logits, desc->T, desc->E_global, desc->top_k,
+                           desc->scoring, topk_ids, topk_weights));
 }
 
 int moe_mxfp4_bucket(const moe_mxfp4_desc* desc, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
@@ -763,8 +815,26 @@ int moe_mxfp4_bucket(const moe_mxfp4_desc* desc, const int32_t* topk_ids, int32_
   if (desc->T == 0) return MOE_OK;
   if (!topk_ids || !counts || !offsets || !routes) return MOE_ERR_NULL;
   if ((st = check_workspace(*desc, workspace, workspace_bytes)) != MOE_OK) return st;
-  enqueue_bucket_hook(*desc, topk_ids, workspace, static_cast<hipStream_t>(stream), counts, offsets, routes);
-  return launch_status();
+  return hip_status(
+      enqueue_bucket_hook(*desc, topk_ids, workspace, static_cast<hipStream_t>(stream), counts, offsets, routes));
+}
+
+int moe_mxfp4_plan_read(const moe_mxfp4_desc* desc, const void* workspace, size_t workspace_bytes, int32_t* topk_ids,
+                        float* topk_weights, int32_t* counts, int32_t* offsets, int32_t* routes, void* stream) {
+  int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (desc->T == 0) return MOE_OK;
+  if ((st = check_workspace(*desc, workspace, workspace_bytes)) != MOE_OK) return st;
+  const moe_mxfp4_desc& d = *desc;
+  const Layout L = make_layout(d);
+  void* ws = const_cast<void*>(workspace);
+  const int R = d.T * d.top_k;
+  const int n = std::max(R, d.E_local + 1);
+  return hip_status(launch(moe::plan_read_kernel, dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
+                           at<const Plan>(ws, L.plan), at<const int32_t>(ws, L.ids), at<const float>(ws, L.weights),
+                           at<const int32_t>(ws, L.counts), at<const int32_t>(ws, L.offsets),
+                           at<const int32_t>(ws, L.routes), R, d.E_local, topk_ids, topk_weights, counts, offsets,
+                           routes));
 }
 
 int moe_mxfp4_dequant(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t cols, int32_t out_dtype,
@@ -777,10 +847,9 @@ int moe_mxfp4_dequant(const uint8_t* packed, const uint8_t* scales, int64_t rows
   if (!aligned16(packed) || !aligned16(out)) return MOE_ERR_ALIGN;
   const int64_t grid = (n_blocks + 255) / 256;
   if (grid > 0x7FFFFFFF) return MOE_ERR_SHAPE;
-  hipLaunchKernelGGL(moe::dequant_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), packed, scales, n_blocks, out_dtype == MOE_DTYPE_BF16 ? 1 : 0,
-                     out);
-  return launch_status();
+  return hip_status(launch(moe::dequant_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
+                           static_cast<hipStream_t>(stream), packed, scales, n_blocks,
+                           out_dtype == MOE_DTYPE_BF16 ? 1 : 0, out));
 }
 
 int moe_mxfp4_encode(const void* in, int32_t in_dtype, int64_t rows, int64_t cols, int32_t rule, uint8_t* packed,
@@ -797,12 +866,10 @@ int moe_mxfp4_encode(const void* in, int32_t in_dtype, int64_t rows, int64_t col
   const int quark = rule == MOE_ENCODE_QUARK ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (in_dtype == MOE_DTYPE_BF16)
-    hipLaunchKernelGGL(moe::encode_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, in, n_blocks, quark,
-                       packed, scales);
-  else
-    hipLaunchKernelGGL(moe::encode_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, in, n_blocks, quark,
-                       packed, scales);
-  return launch_status();
+    return hip_status(launch(moe::encode_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, in, n_blocks,
+                             quark, packed, scales));
+  return hip_status(launch(moe::encode_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, in, n_blocks,
+                           quark, packed, scales));
 }
 
 int moe_mxfp4_tile_weights(uint8_t* packed, int64_t rows, int64_t cols, int32_t inverse, void* stream) {
@@ -813,9 +880,8 @@ int moe_mxfp4_tile_weights(uint8_t* packed, int64_t rows, int64_t cols, int32_t 
   if (packed == nullptr) return MOE_ERR_NULL;
   if (!aligned16(packed)) return MOE_ERR_ALIGN;
   if (groups > 0x7FFFFFFF) return MOE_ERR_SHAPE;
-  hipLaunchKernelGGL(moe::tile_kernel, dim3(static_cast<unsigned>(groups)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), packed, groups, static_cast<int>(cols / 32), inverse);
-  return launch_status();
+  return hip_status(launch(moe::tile_kernel, dim3(static_cast<unsigned>(groups)), dim3(256), 0,
+                           static_cast<hipStream_t>(stream), packed, groups, static_cast<int>(cols / 32), inverse));
 }
 
 const char* moe_mxfp4_status_string(int status) {

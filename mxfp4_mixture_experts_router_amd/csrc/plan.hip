@@ -86,6 +86,10 @@ __device__ __forceinline__ int wave_exclusive_scan_dpp(int v, int& total) {
 // Top-k of one token by one wave, k rounds: the largest free logit (wave max),
 // then the lowest expert id holding it (ballot per slot; slot i holds ids
 // 64 i .. 64 i + 63, so the first slot with a match has the lowest id).
+// NaN logits rank below every number (fmaxf never returns a NaN next to a
+// number, and a NaN equals nothing): a round whose free logits are all NaN
+// takes the lowest free id.  Finite logits are the precondition of the layer;
+// this only keeps the ids distinct and in range when it is broken.
 template <int kPer>
 __device__ __forceinline__ void topk_of(const float (&v)[kPer], int E, int k, int lane, int& my_id, float& my_val) {
   uint32_t taken = 0;
@@ -99,12 +103,20 @@ __device__ __forceinline__ void topk_of(const float (&v)[kPer], int E, int k, in
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
       if (!((taken >> i) & 1u)) lm = fmaxf(lm, v[i]);
-    const float m = wave_max(lm);
+    float m = wave_max(lm);
     int win = -1;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const uint64_t b = __ballot(!((taken >> i) & 1u) && v[i] == m);
       if (win < 0 && b != 0) win = 64 * i + __ffsll(static_cast<unsigned long long>(b)) - 1;
+    }
+    if (win < 0) {  // every free logit is NaN: the lowest free id
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const uint64_t b = __ballot(!((taken >> i) & 1u));
+        if (win < 0 && b != 0) win = 64 * i + __ffsll(static_cast<unsigned long long>(b)) - 1;
+      }
+      m = __builtin_nanf("");
     }
     if ((win & 63) == lane) taken |= 1u << (win >> 6);
     if (lane == j) {
@@ -258,6 +270,7 @@ __device__ void bucket_one_wave(const PlanArgs& P, const int32_t* ids, int R, in
     P.offsets[E_l] = Rl;
     P.plan->n_touched = __popcll(fm);
     P.plan->R_local = Rl;
+    P.plan->key = P.key;
   }
 
   if (P.passes != nullptr) {
@@ -355,7 +368,11 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
     else if (P.E_global <= 512) route_tokens<8>(P, ids_s, wave, lane);
     else route_tokens<16>(P, ids_s, wave, lane);
   } else if (P.w_in != nullptr) {
-    for (int r = tid; r < R; r += blockDim.x) P.weights_ws[r] = P.w_in[r];
+    // ids mode: the plan keeps its own copy of the caller's routing
+    for (int r = tid; r < R; r += blockDim.x) {
+      P.weights_ws[r] = P.w_in[r];
+      P.ids_ws[r] = P.ids_in[r];
+    }
   }
   for (int i = tid; i < kPlanWaves * E_l; i += blockDim.x) hist[i] = 0;
   __syncthreads();
@@ -460,6 +477,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
       base_e[E_l] = total;
       P.plan->n_touched = n_touched;
       P.plan->R_local = total;
+      P.plan->key = P.key;
     }
     if (P.passes != nullptr) {
       const int sh = P.pass_shift, tp1 = (1 << sh) - 1;

@@ -122,7 +122,10 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
   const uint32_t expert_bytes = static_cast<uint32_t>(rows_e) * row_bytes;
   const uint32_t bstride = block_stride(A.tiled);
 
-  const int N = A.plan->n_passes * tiles;
+  // a workspace without this call's plan gives no output; pass entries are
+  // clamped to the host's bounds, so no plan value reaches outside a buffer
+  if (A.plan->key != A.key) return;
+  const int N = min(max(A.plan->n_passes, 0), A.max_passes) * tiles;
   const int P = gridDim.x;
   if (static_cast<int>(blockIdx.x) >= N) return;  // whole workgroup
   // items of this workgroup (the host's grid keeps this <= kStreamMaxItems; the
@@ -171,9 +174,9 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
   // enter item li: weights, staging row, strip DMA
   auto enter_load_item = [&]() {
     const PassEntry* pe = etab + li;
-    l_e = __builtin_amdgcn_readfirstlane(pe->e);
-    l_nt = __builtin_amdgcn_readfirstlane(pe->nt);
-    l_p = __builtin_amdgcn_readfirstlane(pe->p);
+    l_e = min(max(__builtin_amdgcn_readfirstlane(pe->e), 0), A.E_local - 1);
+    l_p = min(max(__builtin_amdgcn_readfirstlane(pe->p), 0), A.R - 1);
+    l_nt = min(max(__builtin_amdgcn_readfirstlane(pe->nt), 0), min(kTp, A.R - l_p));
     l_row0 = __builtin_amdgcn_readfirstlane(pe->pad0) * kItemRows;
     const int tt = stt < l_nt ? stt : 0;
     const int xrow = A.tok_from_pass ? static_cast<int>(pe->rte[tt]) / A.top_k : l_p + tt;
@@ -337,7 +340,7 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
           pk.y = static_cast<uint32_t>(h[2]) | (static_cast<uint32_t>(h[3]) << 16);
           *reinterpret_cast<uint2*>(A.a_out + p * rows + row0w + rl) = pk;
         } else {
-          const size_t orow = A.o_by_route ? static_cast<size_t>(etab[ci].rte[r]) : p;
+          const size_t orow = A.o_by_route ? static_cast<size_t>(min(static_cast<int>(etab[ci].rte[r]), A.R - 1)) : p;
           *reinterpret_cast<float4*>(A.o_out + orow * rows + row0w + rl) =
               make_float4(acc0[0] + b0[0], acc0[1] + b0[1], acc0[2] + b0[2], acc0[3] + b0[3]);
           if (kPair)

@@ -49,14 +49,20 @@ def _sigmoid(v: float) -> float:
 
 
 def topk_by_argmax(row, k):
-    """Repeated arg-max: the largest remaining logit, ties to the lower id."""
+    """Repeated arg-max: the largest remaining logit, ties to the lower id; a
+    NaN loses to every number and, among NaNs, the lower id comes first."""
+    def beats(v, b):
+        if math.isnan(v):
+            return False
+        return math.isnan(b) or v > b
+
     chosen = []
     for _ in range(k):
         best = None
         for e, v in enumerate(row):
             if e in chosen:
                 continue
-            if best is None or v > row[best]:
+            if best is None or beats(v, row[best]):
                 best = e
         chosen.append(best)
     return chosen

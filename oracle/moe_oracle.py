@@ -279,10 +279,13 @@ def route_topk(logits: np.ndarray, top_k: int, scoring: str, dtype=np.float32):
     Experts are ordered by (logit descending, id ascending) with a full sort
     and the first k are taken.  Softmax weights: exp(l_j - l_0) / sum over the
     k selected; sigmoid weights: sigmoid(l_j) / sum over the k selected.
+
+    Finite logits are the layer's precondition.  Reading for a NaN logit (the
+    pages are silent): it ranks below every number, -inf included, and NaNs
+    among themselves go to the lower id; the weights then follow the same
+    arithmetic (a selected NaN makes every weight of the token NaN).
     """
     logits = np.asarray(logits, dtype=np.float32)
-    if not np.all(np.isfinite(logits)):
-        raise ValueError("router logits must be finite")
     T, E = logits.shape
     if not 1 <= top_k <= E:
         raise ValueError("top_k out of range")
@@ -290,17 +293,20 @@ def route_topk(logits: np.ndarray, top_k: int, scoring: str, dtype=np.float32):
     weights = np.empty((T, top_k), dtype=dtype)
     expert = np.arange(E)
     for t in range(T):
-        order = np.lexsort((expert, -logits[t]))  # primary key: -logit; then id
+        nan = np.isnan(logits[t])
+        neg = np.where(nan, np.float32(0.0), -logits[t])
+        order = np.lexsort((expert, neg, nan))  # keys: NaN last, then -logit, then id
         sel = order[:top_k]
         ids[t] = sel
         l = logits[t, sel].astype(dtype)
-        if scoring == SOFTMAX:
-            p = np.exp(l - l[0])
-        elif scoring == SIGMOID:
-            p = np.asarray(1.0, dtype) / (np.asarray(1.0, dtype) + np.exp(-l))
-        else:
-            raise ValueError(f"unknown scoring {scoring!r}")
-        weights[t] = p / p.sum(dtype=dtype)
+        with np.errstate(invalid="ignore", over="ignore"):
+            if scoring == SOFTMAX:
+                p = np.exp(l - l[0])
+            elif scoring == SIGMOID:
+                p = np.asarray(1.0, dtype) / (np.asarray(1.0, dtype) + np.exp(-l))
+            else:
+                raise ValueError(f"unknown scoring {scoring!r}")
+            weights[t] = p / p.sum(dtype=dtype)
     return ids, weights
 
 

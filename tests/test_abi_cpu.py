@@ -238,6 +238,27 @@ def test_hook_error_paths():
     assert L.moe_mxfp4_dequant(A_MIS, A, 4, 64, 0, A, None) == E.MOE_ERR_ALIGN
     assert L.moe_mxfp4_dequant(None, A, 4, 64, 0, A, None) == E.MOE_ERR_NULL
     assert L.moe_mxfp4_dequant(A, A, 0, 64, 0, A, None) == E.MOE_OK
+    assert L.moe_mxfp4_plan_read(ctypes.byref(d), None, 1 << 40, A, A, A, A, A, None) == E.MOE_ERR_WORKSPACE
+    assert L.moe_mxfp4_plan_read(ctypes.byref(d), A_MIS, 1 << 40, A, A, A, A, A, None) == E.MOE_ERR_ALIGN
+    assert L.moe_mxfp4_plan_read(ctypes.byref(d), A, 16, A, A, A, A, A, None) == E.MOE_ERR_WORKSPACE
+    assert L.moe_mxfp4_plan_read(ctypes.byref(_desc(top_k=0)), A, 1 << 40, A, A, A, A, A, None) == E.MOE_ERR_SHAPE
+    assert L.moe_mxfp4_plan_read(ctypes.byref(_desc(T=0)), None, 0, None, None, None, None, None, None) == E.MOE_OK
+
+
+def test_binding_steps_need_a_planned_workspace():
+    # the steps that read a plan refuse to run on a workspace the binding would
+    # have to allocate (it would hold no plan); checked before any device work
+    torch = pytest.importorskip("torch")
+    import mxfp4_mixture_experts_router_amd as m
+    d = m.make_desc(T=4, K=256, I=256, E_global=8, E_local=8, top_k=2)
+    fake = torch.zeros(4)
+    for fn, args in ((m.moe_mxfp4_gate_up, (d, fake, fake, fake, None)),
+                     (m.moe_mxfp4_down, (d, fake, fake, fake, None)),
+                     (m.moe_mxfp4_down_routes, (d, fake, fake, fake, None)),
+                     (m.moe_mxfp4_unpack, (d, fake, fake, fake, fake, fake, fake, None)),
+                     (m.moe_mxfp4_plan_read, (d, None))):
+        with pytest.raises(ValueError, match="reads the plan"):
+            fn(*args)
 
 
 def test_binding_rejects_unexpected_dtypes():

@@ -452,3 +452,31 @@ def test_metric_pins_catch_planted_mistakes(monkeypatch):
         monkeypatch.setattr(oracle, "cosine", planted)
         with pytest.raises(AssertionError):
             test_cosine_closed_forms()
+
+
+def test_routing_nan_logits_rank_last():
+    # Reading (the pages are silent; finite logits are the precondition): a
+    # NaN logit ranks below every number, -inf included, ties to the lower id.
+    nan, inf = float("nan"), float("inf")
+    row = [nan, 1.0, nan, -inf, 0.5]
+    for k, want in ((2, [1, 4]), (3, [1, 4, 3]), (4, [1, 4, 3, 0]), (5, [1, 4, 3, 0, 2])):
+        ids, w = oracle.route_topk(np.array([row], np.float32), k, "softmax")
+        assert ids[0].tolist() == want
+        assert bf.topk_by_argmax(row, k) == want
+        # a selected NaN (or -inf next to finite values: exp(-inf) = 0) shapes the weights
+        if k == 2:
+            assert np.all(np.isfinite(w))
+        if k >= 4:
+            assert np.all(np.isnan(w))
+    # all NaN: ids 0..k-1, weights NaN
+    ids, w = oracle.route_topk(np.full((1, 6), np.nan, np.float32), 3, "sigmoid")
+    assert ids[0].tolist() == [0, 1, 2] and np.all(np.isnan(w))
+    # random rows with NaNs sprinkled in agree with the repeated arg-max
+    rng = np.random.default_rng(17)
+    for E, k in ((32, 4), (128, 4), (384, 8)):
+        logits = (np.round(rng.standard_normal((12, E)) * 4) / 4).astype(np.float32)
+        logits[rng.random((12, E)) < 0.2] = np.nan
+        logits[3] = np.nan
+        ids, _ = oracle.route_topk(logits, k, "softmax")
+        for t in range(12):
+            assert ids[t].tolist() == bf.topk_by_argmax([float(v) for v in logits[t]], k)
