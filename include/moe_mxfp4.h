@@ -187,6 +187,29 @@ int moe_mxfp4_decode(const moe_mxfp4_desc* desc,
                      void* stream);
 
 /*
+ * moe_mxfp4_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a fixed array of
+ * MOE_SCRATCH_BYTES in the library's device memory, one per GPU, held until
+ * the process ends; nothing is allocated or freed in the call.  Arguments,
+ * results and errors are those of moe_mxfp4_decode, plus MOE_ERR_WORKSPACE
+ * when moe_mxfp4_workspace_bytes() of the descriptor exceeds
+ * MOE_SCRATCH_BYTES (e.g. up to T * top_k = 256 routes at K = 7168,
+ * I = 2048), and MOE_ERR_HIP when the array's device address cannot be
+ * found.  Every call on one GPU uses that GPU's one array: calls that may
+ * overlap on a GPU (other streams or host threads) race and give wrong
+ * results; serialise them, or use moe_mxfp4_decode with distinct workspaces.
+ */
+#define MOE_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_mxfp4_decode_noalloc(const moe_mxfp4_desc* desc,
+                             const uint16_t* x,
+                             const float* router_logits,
+                             const int32_t* topk_ids, const float* topk_weights,
+                             const uint8_t* w13_packed, const uint8_t* w13_scales, const uint16_t* w13_bias,
+                             const uint8_t* w2_packed, const uint8_t* w2_scales, const uint16_t* w2_bias,
+                             uint16_t* out, void* stream);
+
+/*
  * The three steps of moe_mxfp4_decode, callable one by one on the same
  * workspace (decode = plan, then gate_up, then down, with identical launches).
  *

@@ -32,6 +32,7 @@ from ._lib import (  # noqa: F401
     MOE_PAIRING_AUTO,
     MOE_PAIRING_OFF,
     MOE_PAIRING_ON,
+    MOE_SCRATCH_BYTES,
     MOE_W13_GATE_UP,
     MOE_W13_INTERLEAVED,
     MOE_OK,
@@ -41,7 +42,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "MoeDesc", "MoeError", "make_desc", "moe_mxfp4_workspace_bytes", "moe_mxfp4_decode",
+    "MoeDesc", "MoeError", "make_desc", "moe_mxfp4_workspace_bytes", "moe_mxfp4_decode", "moe_mxfp4_decode_noalloc",
     "moe_mxfp4_plan", "moe_mxfp4_gate_up", "moe_mxfp4_down", "moe_mxfp4_route", "moe_mxfp4_bucket",
     "moe_mxfp4_plan_read", "moe_mxfp4_decode_routes", "moe_mxfp4_down_routes", "moe_mxfp4_prefill",
     "moe_mxfp4_prefill_workspace_bytes", "moe_mxfp4_unpack",
@@ -189,6 +190,31 @@ def moe_mxfp4_decode(desc: MoeDesc, x, w13_packed, w13_scales, w2_packed, w2_sca
         _ptr(out, torch.bfloat16, (d.T, d.K), "out"),
         wsp, wsn, _stream(stream)), "moe_mxfp4_decode")
     return ws
+
+
+def moe_mxfp4_decode_noalloc(desc: MoeDesc, x, w13_packed, w13_scales, w2_packed, w2_scales, out,
+                             router_logits=None, topk_ids=None, topk_weights=None, w13_bias=None, w2_bias=None,
+                             stream=None):
+    """One layer call on the library's own per-GPU workspace (no allocation
+    anywhere in the call); ``out`` (bf16 [T, K]) is overwritten.  Calls that
+    overlap on one GPU race."""
+    torch = _torch()
+    d = desc
+    s13p, s13s, s13b, s2p, s2s, s2b = _weights_shapes(d)
+    _check(_lib.lib().moe_mxfp4_decode_noalloc(
+        ctypes.byref(d),
+        _ptr(x, torch.bfloat16, (d.T, d.K), "x"),
+        _ptr(router_logits, torch.float32, (d.T, d.E_global), "router_logits", True),
+        _ptr(topk_ids, torch.int32, (d.T, d.top_k), "topk_ids", True),
+        _ptr(topk_weights, torch.float32, (d.T, d.top_k), "topk_weights", True),
+        _ptr(w13_packed, torch.uint8, s13p, "w13_packed"),
+        _ptr(w13_scales, torch.uint8, s13s, "w13_scales"),
+        _ptr(w13_bias, torch.bfloat16, s13b, "w13_bias", True),
+        _ptr(w2_packed, torch.uint8, s2p, "w2_packed"),
+        _ptr(w2_scales, torch.uint8, s2s, "w2_scales"),
+        _ptr(w2_bias, torch.bfloat16, s2b, "w2_bias", True),
+        _ptr(out, torch.bfloat16, (d.T, d.K), "out"),
+        _stream(stream)), "moe_mxfp4_decode_noalloc")
 
 
 def moe_mxfp4_plan(desc: MoeDesc, router_logits=None, topk_ids=None, topk_weights=None, workspace=None,

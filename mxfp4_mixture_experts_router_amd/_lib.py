@@ -36,10 +36,12 @@ MOE_PAIRING_ON = 1
 MOE_PAIRING_OFF = 2
 MOE_W13_GATE_UP = 0
 MOE_W13_INTERLEAVED = 1
+MOE_SCRATCH_BYTES = 64 << 20
 
 EXPORTED = (
     "moe_mxfp4_workspace_bytes",
     "moe_mxfp4_decode",
+    "moe_mxfp4_decode_noalloc",
     "moe_mxfp4_plan",
     "moe_mxfp4_route",
     "moe_mxfp4_bucket",
@@ -87,6 +89,7 @@ _DESC = ctypes.POINTER(MoeDesc)
 _SIGNATURES = {
     "moe_mxfp4_workspace_bytes": (_I32, [_DESC, ctypes.POINTER(_SZ)]),
     "moe_mxfp4_decode": (_I32, [_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_mxfp4_decode_noalloc": (_I32, [_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_mxfp4_plan": (_I32, [_DESC, _P, _P, _P, _P, _SZ, _P]),
     "moe_mxfp4_gate_up": (_I32, [_DESC, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_mxfp4_down": (_I32, [_DESC, _P, _P, _P, _P, _P, _P, _SZ, _P]),

@@ -586,6 +586,31 @@ hipError_t enqueue_w2(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_t*
   return launch_combine(d, C, s);
 }
 
+// The workspace of moe_mxfp4_decode_noalloc: one array per GPU in the code
+// object's device memory, held until the process ends.  Host code never uses
+// the array's name as an address (it names a host-side stand-in); the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current.  No part needs clearing between calls: each call's plan kernel
+// writes every field the later kernels read.
+static __device__ __align__(256) unsigned char scratch[MOE_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up on the first
+// call there (nullptr if the lookup fails).
+void* scratch_ptr() {
+  constexpr int kMaxDevices = 64;
+  static void* addr[kMaxDevices] = {};
+  static std::mutex lock;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  const std::lock_guard<std::mutex> guard(lock);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
 int check_routing(const moe_mxfp4_desc& d, const float* logits, const int32_t* ids, const float* wts) {
   const bool logits_mode = logits != nullptr;
   const bool ids_mode = ids != nullptr || wts != nullptr;
@@ -627,6 +652,26 @@ int moe_mxfp4_decode(const moe_mxfp4_desc* desc, const uint16_t* x, const float*
   if (e == hipSuccess) e = enqueue_w13(d, x, w13_packed, w13_scales, w13_bias, nullptr, workspace, s);
   if (e == hipSuccess) e = enqueue_w2(d, nullptr, w2_packed, w2_scales, w2_bias, out, nullptr, workspace, s);
   return hip_status(e);
+}
+
+int moe_mxfp4_decode_noalloc(const moe_mxfp4_desc* desc, const uint16_t* x, const float* router_logits,
+                             const int32_t* topk_ids, const float* topk_weights, const uint8_t* w13_packed,
+                             const uint8_t* w13_scales, const uint16_t* w13_bias, const uint8_t* w2_packed,
+                             const uint8_t* w2_scales, const uint16_t* w2_bias, uint16_t* out, void* stream) {
+  int st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const moe_mxfp4_desc& d = *desc;
+  if ((st = check_routing(d, router_logits, topk_ids, topk_weights)) != MOE_OK) return st;
+  if (d.T == 0) return MOE_OK;
+  if (!x || !w13_packed || !w13_scales || !w2_packed || !w2_scales || !out) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w13_packed) || !aligned16(w2_packed) || !aligned16(out) || !aligned16(w13_scales) ||
+      !aligned16(w2_scales) || !aligned16(w13_bias) || !aligned16(w2_bias))
+    return MOE_ERR_ALIGN;
+  if (make_layout(d).total > MOE_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = scratch_ptr();
+  if (ws == nullptr) return MOE_ERR_HIP;
+  return moe_mxfp4_decode(desc, x, router_logits, topk_ids, topk_weights, w13_packed, w13_scales, w13_bias,
+                          w2_packed, w2_scales, w2_bias, out, ws, MOE_SCRATCH_BYTES, stream);
 }
 
 int moe_mxfp4_decode_routes(const moe_mxfp4_desc* desc, const uint16_t* x, const float* router_logits,

@@ -245,6 +245,23 @@ def test_hook_error_paths():
     assert L.moe_mxfp4_plan_read(ctypes.byref(_desc(T=0)), None, 0, None, None, None, None, None, None) == E.MOE_OK
 
 
+def test_noalloc_refuses_calls_beyond_its_workspace_before_any_launch():
+    L = _lib.lib()
+    E = _lib
+    d = _desc(T=4096, K=7168, I=2048, E_global=384, E_local=48, top_k=8)
+    n = ctypes.c_size_t(0)
+    assert L.moe_mxfp4_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == E.MOE_OK
+    assert n.value > E.MOE_SCRATCH_BYTES
+    assert L.moe_mxfp4_decode_noalloc(ctypes.byref(d), A, A, None, None, A, A, None, A, A, None, A, None) == \
+        E.MOE_ERR_WORKSPACE
+    assert L.moe_mxfp4_decode_noalloc(ctypes.byref(d), A, None, None, None, A, A, None, A, A, None, A, None) == \
+        E.MOE_ERR_MODE
+    assert L.moe_mxfp4_decode_noalloc(ctypes.byref(d), A_MIS, A, None, None, A, A, None, A, A, None, A, None) == \
+        E.MOE_ERR_ALIGN
+    assert L.moe_mxfp4_decode_noalloc(ctypes.byref(_desc(T=0)), None, A, None, None, None, None, None, None, None,
+                                      None, None, None) == E.MOE_OK
+
+
 def test_binding_steps_need_a_planned_workspace():
     # the steps that read a plan refuse to run on a workspace the binding would
     # have to allocate (it would hold no plan); checked before any device work
