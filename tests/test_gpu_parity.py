@@ -356,6 +356,9 @@ BUCKET_CASES = [
     # 65 - 128 routes: the general path just above the one-wave limit
     (32, 32, 0, 4, 32, 0.0), (8, 8, 0, 2, 33, 0.0), (512, 512, 0, 8, 16, 0.1), (64, 16, 48, 4, 20, 0.2),
     (1, 1, 0, 1, 100, 0.0), (256, 32, 0, 8, 12, 0.0), (4, 4, 0, 1, 65, 0.0),
+    # 65 - 512 routes: one wave in 64-route chunks; 520: the general path again
+    (64, 64, 0, 8, 64, 0.0), (384, 48, 336, 8, 64, 0.1), (600, 512, 88, 4, 128, 0.05), (64, 64, 0, 8, 65, 0.0),
+    (256, 32, 0, 8, 40, 0.0), (2, 2, 0, 2, 200, 0.0),
 ]
 
 
