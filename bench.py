@@ -499,13 +499,13 @@ def measured_traffic(cfg, tokens, layout, w13_order="gate_up"):
     return int(np.mean([per_t[str(t)] for t in tokens]))
 
 
-def cpu_baseline(cfg, w0, torch, moe, layout, tokens=(1, 4)):
+def cpu_baseline(cfg, w0, torch, moe, layout, tokens=(1, 4, 8)):
     """The CPU oracle, as it stands, on a bounded sample of the headline
     workload: one call at each T in `tokens` (replica 0's weights), timed with
     BLAS on 1 thread and on every core of the process's affinity set.  The
     split into dequantisation (numpy, one thread either way) and the rest
     (matmuls, activation, combine) comes from timing the oracle's dequantise
-    of one call's touched experts on their own."""
+    of the sample's touched experts on their own."""
     import oracle
     from workloads import make_inputs
     from threadpoolctl import threadpool_limits
@@ -525,13 +525,13 @@ def cpu_baseline(cfg, w0, torch, moe, layout, tokens=(1, 4)):
     n_touched = sum(len(v) for v in touched.values())
     total_bytes = sum(len(touched[T]) * cfg.bytes_per_expert() + 4 * T * cfg.K + 4 * T * cfg.E_global
                       for T in tokens)
-    # dequantisation of the first call's touched experts, timed alone
+    # dequantisation of the sample's touched experts, timed alone
     t0 = time.perf_counter()
-    for e in touched[tokens[0]]:
-        oracle.dequantize(w0.w13_packed[e], w0.w13_scales[e])
-        oracle.dequantize(w0.w2_packed[e], w0.w2_scales[e])
-    deq_per_expert = (time.perf_counter() - t0) / max(1, len(touched[tokens[0]]))
-    deq_s = deq_per_expert * n_touched
+    for T in tokens:
+        for e in touched[T]:
+            oracle.dequantize(w0.w13_packed[e], w0.w13_scales[e])
+            oracle.dequantize(w0.w2_packed[e], w0.w2_scales[e])
+    deq_s = time.perf_counter() - t0
     checks = {}
     for T, inp in zip(tokens, calls):
         # the same call on the device (the benchmark's layout), compared with the oracle

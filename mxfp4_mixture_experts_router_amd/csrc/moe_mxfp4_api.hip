@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstddef>
 #include <cstdint>
 #include <mutex>
@@ -305,6 +306,18 @@ hipError_t enqueue_expert_pair(const moe_mxfp4_desc& d, bool gate_up, moe::Exper
                                                 : resident_workgroups(moe::gemv_kernel<false, 32>, lds));
     int64_t grid = std::max<int64_t>(1, touched * (rows / rows_per_wg));
     if (resident > 0) grid = std::min<int64_t>(grid, resident);
+    // With the MFMA regime on, the GEMV list holds the experts with 1..2
+    // routes; when uniform routing makes those rare (T * top_k / E_global
+    // routes per expert expected), a smaller grid keeps the launch of an
+    // empty or short list cheap (the loop is grid-stride: any grid covers
+    // any list, a long one only more slowly).
+    if (mfma_enabled(d)) {
+      const double lam = static_cast<double>(d.T) * d.top_k / d.E_global;
+      const double p12 = std::exp(-lam) * (lam + 0.5 * lam * lam);
+      const double expect = d.E_local * p12;
+      const int64_t want = static_cast<int64_t>(std::ceil(4.0 * expect + 2.0)) * (rows / rows_per_wg);
+      grid = std::max<int64_t>(1, std::min<int64_t>(grid, std::max<int64_t>(want, 64)));
+    }
     const dim3 g(static_cast<unsigned>(grid));
     if (gate_up) {
       if (lanes == 16) MOE_TRY(launch(moe::gemv_kernel<true, 16>, g, dim3(256), lds, s, G));

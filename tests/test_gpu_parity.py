@@ -855,14 +855,14 @@ def test_mfma_lists_every_column_group_count(case):
 
 def test_list_path_top1_just_above_one_wave_plan():
     # T = 100, top-1 over 4 experts: 100 routes (just above the plan kernel's
-    # one-wave bucketing) and more than 16 per expert, so the MFMA lists take
-    # them
+    # one-wave bucketing, in its 64-route chunked path) and more than 16 per
+    # expert, so the MFMA lists take them
     cfg = _cfg(K=512, I=512, E_global=4, E_local=4, top_k=1, bias=True)
     w = make_weights(cfg)
     inp = make_topk_inputs(cfg, 100, seed=23)
     ref = oracle.moe_forward_cfg(cfg, w, inp)
     y = bf16_to_np(run_decode(cfg, DeviceLayer(w), inp))
-    _assert_close(y, ref["y"], "two routes per lane, lists")
+    _assert_close(y, ref["y"], "top-1 list call just above the one-wave plan")
 
 
 @pytest.mark.parametrize("T", [3, 100])
@@ -898,8 +898,8 @@ def test_layer_no_local_route_writes_zeros_stream_path():
 
 @pytest.mark.parametrize("T", [3, 7, 24])
 def test_down_step_twice_on_one_plan(T):
-    # the combine fused into the down projection counts finished row tiles in
-    # the workspace; a second down call on the same plan must combine again
+    # the down step reads only the plan and the intermediate the workspace
+    # holds: a second down call on the same plan gives the same bits
     t = torch()
     cfg = _cfg(K=1056, I=1120, E_global=8, E_local=6, expert_offset=1, top_k=3, bias=True)
     w = make_weights(cfg)
