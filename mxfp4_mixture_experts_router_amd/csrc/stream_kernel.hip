@@ -122,15 +122,34 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
   const uint32_t expert_bytes = static_cast<uint32_t>(rows_e) * row_bytes;
   const uint32_t bstride = block_stride(A.tiled);
 
+  // The pass entries this workgroup may hold are requested before the plan
+  // header is read, bounded by the host's pass bound (so always inside the
+  // pass list; entries past the plan's count are dropped below): the two
+  // requests share one memory round trip.
+  const int P = gridDim.x;
+  const int bid = static_cast<int>(blockIdx.x);
+  const int n_bound = A.max_passes * tiles;
+  const int n_req = bid < n_bound ? min((n_bound - 1 - bid) / P + 1, kStreamMaxItems) : 0;
+  const int e_idx = bid + (tid >> 2) * P;  // item of this thread's entry part
+  const int e_pass = e_idx / tiles;
+  uint4 ent = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < 4 * n_req) ent = reinterpret_cast<const uint4*>(A.passes + e_pass)[tid & 3];
+  // (the header's address depends on the pass bound, 0 for any valid one, so
+  // that its request does not come before the bound's and the wait for the
+  // bound does not also wait for it; both values are taken before the checks
+  // so that neither request sinks below them)
+  const Plan* plan = A.plan + ((A.max_passes >> 31) & 1);
+  const uint32_t plan_key = plan->key;
+  const int plan_passes = plan->n_passes;
+  asm volatile("" ::"v"(ent.x), "v"(ent.y), "v"(ent.z), "v"(ent.w), "s"(plan_key), "s"(plan_passes));
   // a workspace without this call's plan gives no output; pass entries are
   // clamped to the host's bounds, so no plan value reaches outside a buffer
-  if (A.plan->key != A.key) return;
-  const int N = min(max(A.plan->n_passes, 0), A.max_passes) * tiles;
-  const int P = gridDim.x;
-  if (static_cast<int>(blockIdx.x) >= N) return;  // whole workgroup
+  if (plan_key != A.key) return;
+  const int N = min(max(plan_passes, 0), A.max_passes) * tiles;
+  if (bid >= N) return;  // whole workgroup
   // items of this workgroup (the host's grid keeps this <= kStreamMaxItems; the
   // min only guards the LDS table)
-  const int n_my = min((N - 1 - static_cast<int>(blockIdx.x)) / P + 1, kStreamMaxItems);
+  const int n_my = min((N - 1 - bid) / P + 1, kStreamMaxItems);
   const int total = n_my * NCp;
 
   // LDS: [2][kXBufBytes] staged activations | per (buffer, wave) scale strips
@@ -155,12 +174,8 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
   // pad0 field holds the tile.  The host sizes the grid so that n_my <= kStreamMaxItems.
   PassEntry* etab = reinterpret_cast<PassEntry*>(redbuf + (kSplit > 1 ? 4 * 64 * 8 : 0));
   if (tid < 4 * n_my) {
-    const int i = tid >> 2, part = tid & 3;
-    const int idx = static_cast<int>(blockIdx.x) + i * P;
-    const int sp = idx / tiles;
-    uint4 v = reinterpret_cast<const uint4*>(A.passes + sp)[part];
-    if (part == 0) v.w = static_cast<uint32_t>(idx - sp * tiles);
-    reinterpret_cast<uint4*>(etab + i)[part] = v;
+    if ((tid & 3) == 0) ent.w = static_cast<uint32_t>(e_idx - e_pass * tiles);
+    reinterpret_cast<uint4*>(etab + (tid >> 2))[tid & 3] = ent;
   }
   __syncthreads();
 
