@@ -80,6 +80,9 @@ def parse():
                         "against the decode path on the same calls (default: the wide-K slice at T=256, 2048)")
     p.add_argument("--down-pairing", default="auto", choices=("auto", "on", "off"),
                    help="row pairing of the down projection (a performance control; same results)")
+    p.add_argument("--mma", default="bf16", choices=("bf16", "scaled_fp4"),
+                   help="matrix instructions for experts with many routes (the MFMA list path): bf16 after an "
+                        "in-register FP4 decode, or scaled-FP4 MFMA on hi + lo E4M3 activations")
     p.add_argument("--per-route", action="store_true",
                    help="per-route output: fp32 [T*top_k, K] rows instead of the bf16 token sums")
     return p.parse_args()
@@ -163,7 +166,7 @@ def measure_config(torch, moe, cfg, tokens, args, reps, breakdown=True):
         d = moe.make_desc(T=T, K=K, I=I, E_global=cfg.E_global, E_local=cfg.E_local, top_k=cfg.top_k,
                           expert_offset=cfg.expert_offset, scoring=cfg.scoring, activation=cfg.activation,
                           swiglu_alpha=cfg.swiglu_alpha, swiglu_limit=cfg.swiglu_limit, weight_layout=args.layout,
-                          w13_order=args.w13_order, down_pairing=args.down_pairing)
+                          w13_order=args.w13_order, down_pairing=args.down_pairing, mma=args.mma)
         ws_bytes = moe.moe_mxfp4_workspace_bytes(d)
         inputs = [make_inputs(cfg, T, call=i) for i in range(L)]
         xs = [torch.from_numpy(inp.x.view(np.int16)).cuda().view(torch.bfloat16) for inp in inputs]

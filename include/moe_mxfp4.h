@@ -110,6 +110,22 @@ extern "C" {
 #define MOE_PAIRING_ON     1    /* whenever K % 32 == 0                               */
 #define MOE_PAIRING_OFF    2
 
+/* Matrix instructions for experts with many routes in one call (the MFMA
+ * list path; calls served by the decode-regime stream kernel and experts
+ * with one or two routes are not affected).
+ *   BF16:       each E2M1 weight block is decoded with its E8M0 scale to bf16
+ *               in registers and fed to v_mfma_f32_16x16x32_bf16 with the bf16
+ *               activations (exact products, fp32 sums).
+ *   SCALED_FP4: the packed E2M1 blocks and E8M0 scales go to
+ *               v_mfma_scale_f32_16x16x128_f8f6f4 as stored; the activations
+ *               are first split, row by row, into hi + lo E4M3 parts with one
+ *               E8M0 scale each (about the precision of bf16), and every
+ *               128-value chunk takes two scaled MFMAs.  Needs extra
+ *               workspace for the split rows (moe_mxfp4_workspace_bytes
+ *               includes it).                                              */
+#define MOE_MMA_BF16        0
+#define MOE_MMA_SCALED_FP4  1
+
 /* ---- layer descriptor --------------------------------------------------- */
 typedef struct moe_mxfp4_desc {
     int32_t T;              /* tokens in the call, >= 0 (T = 0 is a no-op); T * top_k
@@ -129,6 +145,9 @@ typedef struct moe_mxfp4_desc {
     int32_t weight_layout;  /* MOE_LAYOUT_* of w13_packed and w2_packed                   */
     int32_t down_pairing;   /* MOE_PAIRING_* (0 = automatic)                              */
     int32_t w13_order;      /* MOE_W13_* row order of the w13 tensors                      */
+    int32_t mma;            /* MOE_MMA_* for experts with many routes (0 = bf16); with
+                               SCALED_FP4 the split rows, T * 256 * ceil(K / 128) and
+                               T * top_k * 256 * ceil(I / 128) bytes, each below 2 GiB  */
 } moe_mxfp4_desc;
 
 /*

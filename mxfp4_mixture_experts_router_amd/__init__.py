@@ -35,6 +35,8 @@ from ._lib import (  # noqa: F401
     MOE_SCRATCH_BYTES,
     MOE_W13_GATE_UP,
     MOE_W13_INTERLEAVED,
+    MOE_MMA_BF16,
+    MOE_MMA_SCALED_FP4,
     MOE_OK,
     MOE_SCORING_SIGMOID,
     MOE_SCORING_SOFTMAX,
@@ -54,6 +56,7 @@ _ACT = {"silu_mul": MOE_ACT_SILU_MUL, "swiglu_oai": MOE_ACT_SWIGLU_OAI}
 _LAYOUT = {"rows": MOE_LAYOUT_ROWS, "tile16": MOE_LAYOUT_TILE16}
 _PAIRING = {"auto": MOE_PAIRING_AUTO, "on": MOE_PAIRING_ON, "off": MOE_PAIRING_OFF}
 _W13_ORDER = {"gate_up": MOE_W13_GATE_UP, "interleaved": MOE_W13_INTERLEAVED}
+_MMA = {"bf16": MOE_MMA_BF16, "scaled_fp4": MOE_MMA_SCALED_FP4}
 
 
 class MoeError(RuntimeError):
@@ -65,13 +68,14 @@ class MoeError(RuntimeError):
 def make_desc(T: int, K: int, I: int, E_global: int, E_local: int, top_k: int, expert_offset: int = 0,
               scoring="softmax", activation="silu_mul", swiglu_alpha: float = 1.702,
               swiglu_limit: float = 7.0, weight_layout="rows", down_pairing="auto",
-              w13_order="gate_up") -> MoeDesc:
+              w13_order="gate_up", mma="bf16") -> MoeDesc:
     sc = _SCORING[scoring] if isinstance(scoring, str) else int(scoring)
     ac = _ACT[activation] if isinstance(activation, str) else int(activation)
     wl = _LAYOUT[weight_layout] if isinstance(weight_layout, str) else int(weight_layout)
     dp = _PAIRING[down_pairing] if isinstance(down_pairing, str) else int(down_pairing)
     wo = _W13_ORDER[w13_order] if isinstance(w13_order, str) else int(w13_order)
-    return MoeDesc(T, K, I, E_global, E_local, expert_offset, top_k, sc, ac, swiglu_alpha, swiglu_limit, wl, dp, wo)
+    mm = _MMA[mma] if isinstance(mma, str) else int(mma)
+    return MoeDesc(T, K, I, E_global, E_local, expert_offset, top_k, sc, ac, swiglu_alpha, swiglu_limit, wl, dp, wo, mm)
 
 
 def moe_mxfp4_status_string(status: int) -> str:

@@ -36,6 +36,8 @@ MOE_PAIRING_ON = 1
 MOE_PAIRING_OFF = 2
 MOE_W13_GATE_UP = 0
 MOE_W13_INTERLEAVED = 1
+MOE_MMA_BF16 = 0
+MOE_MMA_SCALED_FP4 = 1
 MOE_SCRATCH_BYTES = 64 << 20
 
 EXPORTED = (
@@ -77,6 +79,7 @@ class MoeDesc(ctypes.Structure):
         ("weight_layout", ctypes.c_int32),
         ("down_pairing", ctypes.c_int32),
         ("w13_order", ctypes.c_int32),
+        ("mma", ctypes.c_int32),
     ]
 
 

@@ -23,7 +23,7 @@ LIB_NAME = "libmoe_mxfp4.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["plan.hip", "expert_kernels.hip", "stream_kernel.hip", "moe_mxfp4_api.hip"]
+SOURCES = ["plan.hip", "expert_kernels.hip", "scaled_kernels.hip", "stream_kernel.hip", "moe_mxfp4_api.hip"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 HIPCC_FLAGS = [
@@ -65,7 +65,7 @@ def build(verbose: bool = False) -> str:
         "flags": HIPCC_FLAGS,
         "sources": {s: _sha256(os.path.join(CSRC, s)) for s in SOURCES},
         "headers": {h: _sha256(os.path.join(d, h)) for d, h in
-                    ((INCLUDE, "moe_mxfp4.h"), (CSRC, "kernels.h"), (CSRC, "device_common.h"))},
+                    ((INCLUDE, "moe_mxfp4.h"), (CSRC, "kernels.h"), (CSRC, "device_common.h"), (CSRC, "list_common.h"))},
         "library_sha256": _sha256(LIB_PATH),
     }
     with open(os.path.join(PKG_DIR, "libmoe_mxfp4.manifest.json"), "w") as f:

@@ -125,6 +125,8 @@ struct ExpertArgs {
   int tiled;               // packed weights in the tiled layout
   int il;                  // gate/up: w13 rows interleaved (gate_row / up_row)
   const uint16_t* wbf;     // prefill: the weights unpacked to bf16 [E_l][rows_e][red] (MFMA kernel), else nullptr
+  const int32_t* in_scale; // scaled-FP4 MFMA kernel: per activation row, E8M0 of the hi (byte 0) and lo (byte 1) parts
+  uint32_t in_stride;      // scaled-FP4 MFMA kernel: bytes per split activation row (ceil(red / 128) * 256)
   uint16_t* a_out;         // gate/up output [R, I] bf16
   float* o_out;            // down output [R, K] fp32
   int act_kind;
@@ -179,6 +181,27 @@ __global__ void gemv_kernel(ExpertArgs A);
 // kBf16W reads the bf16-unpacked weights (prefill) instead of decoding MXFP4.
 template <bool kGateUp, int kGroups, bool kBf16W, bool kPair>
 __global__ void mfma_kernel(ExpertArgs A);
+
+// Scaled-FP4 form of the MFMA regime.  Activations are first split, row by
+// row, into two E4M3 parts with one E8M0 scale each (hi = the row rounded to
+// E4M3 under a scale set by its largest magnitude, lo = the remainder
+// rounded the same way), stored per 128-value chunk as [hi 128 B | lo 128 B]
+// (mx8_split_kernel).  mfma_fp4_kernel then feeds the packed E2M1 weight
+// blocks and their E8M0 scales to v_mfma_scale_f32_16x16x128_f8f6f4 without
+// decoding them, two MFMAs (hi, lo) per 16-row set, 16 tokens and 128 values.
+struct SplitArgs {
+  const uint16_t* in;      // bf16 rows [rows][L]
+  int rows;                // rows to split (the bound when rows_from_plan)
+  int L;                   // values per row, multiple of 32
+  int rows_from_plan;      // 1: split only plan->R_local rows (plan order, down input)
+  const Plan* plan;
+  uint32_t key;
+  uint8_t* out;            // [rows][ceil(L / 128)][hi 128 B | lo 128 B]
+  int32_t* scales;         // [rows]: E8M0 of hi | E8M0 of lo << 8
+};
+__global__ void mx8_split_kernel(SplitArgs A);
+template <bool kGateUp, int kGroups, bool kPair>
+__global__ void mfma_fp4_kernel(ExpertArgs A);
 // Prefill unpack: packed [E_l][rows][cols/2] (row or tiled layout) + scales
 // -> bf16 [E_l][rows][cols] in the row layout, for the experts with
 // counts[e] > 0 (all when counts is nullptr); grid (ceil(rows * cols/32 / 256), E_l).

@@ -24,10 +24,17 @@ using moe::Plan;
 
 
 bool stream_regime(const moe_mxfp4_desc& d);
+bool mfma_enabled(const moe_mxfp4_desc& d);
 
 struct Layout {
-  size_t plan, ids, weights, counts, offsets, gemv_list, mfma_list, passes, routes, pos, a, o, total;
+  size_t plan, ids, weights, counts, offsets, gemv_list, mfma_list, passes, routes, pos, a, o;
+  size_t xq, xq_scale, aq, aq_scale;  // split activations of the scaled-FP4 MFMA kernels (0 bytes otherwise)
+  size_t total;
 };
+
+// Bytes of one activation row split for the scaled-FP4 MFMA kernel: a
+// 256-byte chunk (hi 128 B, lo 128 B) per 128 values.
+size_t split_row_bytes(int L) { return static_cast<size_t>((L + 127) / 128) * 256; }
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -53,6 +60,11 @@ Layout make_layout(const moe_mxfp4_desc& d) {
   L.pos = take(R * 4);
   L.a = take(R * d.I * 2);
   L.o = take(R * d.K * 4);
+  const bool split = d.mma == MOE_MMA_SCALED_FP4 && mfma_enabled(d);
+  L.xq = take(split ? static_cast<size_t>(d.T) * split_row_bytes(d.K) : 0);
+  L.xq_scale = take(split ? static_cast<size_t>(d.T) * 4 : 0);
+  L.aq = take(split ? R * split_row_bytes(d.I) : 0);
+  L.aq_scale = take(split ? R * 4 : 0);
   L.total = off;
   return L;
 }
@@ -79,6 +91,12 @@ int check_desc(const moe_mxfp4_desc* d) {
   if (d->down_pairing != MOE_PAIRING_AUTO && d->down_pairing != MOE_PAIRING_ON && d->down_pairing != MOE_PAIRING_OFF)
     return MOE_ERR_MODE;
   if (d->w13_order != MOE_W13_GATE_UP && d->w13_order != MOE_W13_INTERLEAVED) return MOE_ERR_MODE;
+  if (d->mma != MOE_MMA_BF16 && d->mma != MOE_MMA_SCALED_FP4) return MOE_ERR_MODE;
+  // the split activation rows (whole 128-value chunks) obey the same bound
+  if (d->mma == MOE_MMA_SCALED_FP4) {
+    if (static_cast<int64_t>(d->T) * split_row_bytes(d->K) >= (int64_t{1} << 31)) return MOE_ERR_SHAPE;
+    if (static_cast<int64_t>(d->T) * d->top_k * split_row_bytes(d->I) >= (int64_t{1} << 31)) return MOE_ERR_SHAPE;
+  }
   return MOE_OK;
 }
 
@@ -279,6 +297,53 @@ hipError_t enqueue_bucket_hook(const moe_mxfp4_desc& d, const int32_t* ids, void
   return launch(moe::plan_kernel, dim3(1), dim3(1024), 0, s, P);
 }
 
+// The MFMA regime with scaled-FP4 instructions: the projection's input rows
+// (x by token, or the intermediate a by plan position) are split into E4M3
+// hi + lo parts in the workspace, then mfma_fp4_kernel runs on the same
+// work list, grid and row pairing as mfma_kernel would.
+hipError_t enqueue_mfma_fp4(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertArgs M, const Layout& L, void* ws,
+                            int groups, size_t lds, size_t lds1, int64_t slots, hipStream_t s) {
+  const int rows = M.rows;
+  moe::SplitArgs P{};
+  P.in = M.in;
+  P.L = M.red;
+  P.plan = M.plan;
+  P.key = M.key;
+  P.rows_from_plan = gate_up ? 0 : 1;
+  P.rows = gate_up ? d.T : d.T * d.top_k;
+  P.out = at<uint8_t>(ws, gate_up ? L.xq : L.aq);
+  P.scales = at<int32_t>(ws, gate_up ? L.xq_scale : L.aq_scale);
+  MOE_TRY(launch(moe::mx8_split_kernel, dim3(static_cast<unsigned>(P.rows)), dim3(256), 0, s, P));
+  M.in = reinterpret_cast<const uint16_t*>(P.out);
+  M.in_stride = static_cast<uint32_t>(split_row_bytes(M.red));
+  M.in_bytes = static_cast<uint32_t>(static_cast<size_t>(P.rows) * M.in_stride);
+  M.in_scale = P.scales;
+  if (gate_up) {
+    const dim3 g(static_cast<unsigned>(slots * ((rows + moe::kMfmaRows - 1) / moe::kMfmaRows)));
+    if (groups == 1) return launch(moe::mfma_fp4_kernel<true, 1, false>, g, dim3(256), lds, s, M);
+    if (groups == 2) return launch(moe::mfma_fp4_kernel<true, 2, false>, g, dim3(256), lds, s, M);
+    return launch(moe::mfma_fp4_kernel<true, 4, false>, g, dim3(256), lds, s, M);
+  }
+  bool pair = rows % 32 == 0 && d.down_pairing != MOE_PAIRING_OFF;
+  const int64_t grid2 = slots * ((rows + 2 * moe::kMfmaRows - 1) / (2 * moe::kMfmaRows));
+  if (pair && d.down_pairing == MOE_PAIRING_AUTO) {
+    const int resident = groups == 1   ? resident_workgroups(moe::mfma_fp4_kernel<false, 1, true>, lds)
+                         : groups == 2 ? resident_workgroups(moe::mfma_fp4_kernel<false, 2, true>, lds)
+                                       : resident_workgroups(moe::mfma_fp4_kernel<false, 4, true>, lds);
+    pair = grid2 >= resident;
+  }
+  if (pair) {
+    const dim3 g(static_cast<unsigned>(grid2));
+    if (groups == 1) return launch(moe::mfma_fp4_kernel<false, 1, true>, g, dim3(256), lds, s, M);
+    if (groups == 2) return launch(moe::mfma_fp4_kernel<false, 2, true>, g, dim3(256), lds, s, M);
+    return launch(moe::mfma_fp4_kernel<false, 4, true>, g, dim3(256), lds, s, M);
+  }
+  const dim3 g(static_cast<unsigned>(slots * ((rows + moe::kMfmaRows - 1) / moe::kMfmaRows)));
+  if (groups == 1) return launch(moe::mfma_fp4_kernel<false, 1, false>, g, dim3(256), lds1, s, M);
+  if (groups == 2) return launch(moe::mfma_fp4_kernel<false, 2, false>, g, dim3(256), lds1, s, M);
+  return launch(moe::mfma_fp4_kernel<false, 4, false>, g, dim3(256), lds1, s, M);
+}
+
 // Both regimes of one projection.  Grids are host-side upper bounds: at most
 // min(E_local, T*top_k) experts are touched, and at most T*top_k / (G+1) of
 // them have more than G = kGemvMaxTokens routes; workgroups past the lists exit.
@@ -343,6 +408,7 @@ hipError_t enqueue_expert_pair(const moe_mxfp4_desc& d, bool gate_up, moe::Exper
     const size_t lds1 = 2 * static_cast<size_t>(16 * groups) * moe::kXRowBytes +
                         static_cast<size_t>(moe::kMfmaRows) * (red / 32);
     const int64_t slots = (mfma_experts + 7) / 8 * 8;
+    if (d.mma == MOE_MMA_SCALED_FP4) return enqueue_mfma_fp4(d, gate_up, M, L, ws, groups, lds, lds1, slots, s);
     if (gate_up) {
       const dim3 g(static_cast<unsigned>(slots * ((rows + moe::kMfmaRows - 1) / moe::kMfmaRows)));
       if (groups == 1) return launch(moe::mfma_kernel<true, 1, false, false>, g, dim3(256), lds, s, M);

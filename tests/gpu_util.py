@@ -65,21 +65,21 @@ class DeviceLayer:
 
 
 def desc_for(cfg, T, E_local=None, expert_offset=None, weight_layout="rows", down_pairing="auto",
-             w13_order="gate_up"):
+             w13_order="gate_up", mma="bf16"):
     return moe.make_desc(T=T, K=cfg.K, I=cfg.I, E_global=cfg.E_global,
                          E_local=cfg.E_local if E_local is None else E_local, top_k=cfg.top_k,
                          expert_offset=cfg.expert_offset if expert_offset is None else expert_offset,
                          scoring=cfg.scoring, activation=cfg.activation,
                          swiglu_alpha=cfg.swiglu_alpha, swiglu_limit=cfg.swiglu_limit,
-                         weight_layout=weight_layout, down_pairing=down_pairing, w13_order=w13_order)
+                         weight_layout=weight_layout, down_pairing=down_pairing, w13_order=w13_order, mma=mma)
 
 
 def run_decode(cfg, layer, inp, expert_offset=None, workspace=None, stream=None, down_pairing="auto",
-               w13_order="gate_up"):
+               w13_order="gate_up", mma="bf16"):
     t = torch()
     T = inp.x.shape[0]
     d = desc_for(cfg, T, E_local=layer.E_local, expert_offset=expert_offset, weight_layout=layer.layout,
-                 down_pairing=down_pairing, w13_order=w13_order)
+                 down_pairing=down_pairing, w13_order=w13_order, mma=mma)
     x = dev_bf16(inp.x)
     out = t.full((T, cfg.K), float("nan"), dtype=t.bfloat16, device="cuda")
     kw = {}

@@ -43,7 +43,8 @@ def test_version_and_status_strings():
 
 def _desc(**kw):
     d = dict(T=4, K=256, I=256, E_global=8, E_local=8, expert_offset=0, top_k=2, scoring=0,
-             activation=0, swiglu_alpha=1.702, swiglu_limit=7.0, weight_layout=0, down_pairing=0, w13_order=0)
+             activation=0, swiglu_alpha=1.702, swiglu_limit=7.0, weight_layout=0, down_pairing=0, w13_order=0,
+             mma=0)
     d.update(kw)
     return _lib.MoeDesc(**d)
 
@@ -81,10 +82,35 @@ def test_workspace_query():
     (dict(activation=-1), _lib.MOE_ERR_MODE),
     (dict(w13_order=2), _lib.MOE_ERR_MODE),
     (dict(w13_order=-1), _lib.MOE_ERR_MODE),
+    (dict(mma=2), _lib.MOE_ERR_MODE),
+    (dict(mma=-1), _lib.MOE_ERR_MODE),
+    # split rows of the scaled-FP4 path: whole 256-byte chunks per 128 values,
+    # so I = 32 needs 8x the bf16 bytes (2^19 routes x 256 B = 128 MiB is fine,
+    # T * top_k = 2^23 routes x 256 B = 2 GiB is not)
+    (dict(mma=1, T=1 << 20, top_k=8, I=32, K=32), _lib.MOE_ERR_SHAPE),
 ])
 def test_bad_descriptors_are_refused(bad, code):
     st, _ = _ws_bytes(_desc(**bad))
     assert st == code
+
+
+def test_scaled_fp4_workspace_holds_the_split_rows():
+    # the split activations (x by token, the intermediate by route) exist only
+    # when the MFMA lists can run (T > 2): 256 bytes per 128 values, plus one
+    # scale word per row, each region 256-byte aligned
+    def split(T, K=256, I=256, top_k=2):
+        def up(n):
+            return (n + 255) // 256 * 256
+        return (up(T * ((K + 127) // 128) * 256) + up(T * 4) +
+                up(T * top_k * ((I + 127) // 128) * 256) + up(T * top_k * 4))
+    for T in (1, 2):
+        assert _ws_bytes(_desc(T=T, mma=1)) == _ws_bytes(_desc(T=T, mma=0))
+    for T, K, I in ((3, 256, 256), (40, 96, 224), (100, 7168, 2048)):
+        st0, n0 = _ws_bytes(_desc(T=T, K=K, I=I, mma=0))
+        st1, n1 = _ws_bytes(_desc(T=T, K=K, I=I, mma=1))
+        assert st0 == st1 == _lib.MOE_OK
+        assert n1 - n0 == split(T, K, I), (T, K, I)
+    assert _ws_bytes(_desc(mma=1, T=1 << 16, top_k=8, I=32, K=32))[0] == _lib.MOE_OK
 
 
 def test_largest_activation_buffers_are_accepted():
