@@ -65,7 +65,8 @@ struct Plan {
   int32_t n_mfma;      // experts in the MFMA list
   int32_t n_passes;    // entries of the pass list (decode regime)
   uint32_t key;        // descriptor key of the call that wrote this plan
-  int32_t pad[58];
+  int32_t n_passes2;   // entries of the second pass list (another pass size), or 0
+  int32_t pad[57];
 };
 
 struct PlanArgs {
@@ -86,6 +87,8 @@ struct PlanArgs {
   WorkEntry* mfma_list;    // [E_l]
   PassEntry* passes;       // pass list, or nullptr
   int pass_shift;          // routes per pass = 1 << pass_shift (<= kStreamPassTokens) when passes != nullptr
+  PassEntry* passes2;      // a second pass list, cut at 1 << pass_shift2 routes, or nullptr
+  int pass_shift2;
   Plan* plan;
   uint32_t key;            // written to plan->key
   int32_t* routes_out;     // bucket hook: copy of routes padded with -1, or nullptr
@@ -154,6 +157,7 @@ struct StreamArgs {
   const Plan* plan;
   uint32_t key;              // the plan is used only when plan->key == key
   int max_passes;            // host bound on the plan's pass count (entries the pass list holds)
+  int second_list;           // 1: `passes` is the plan's second pass list (count n_passes2)
   int E_local, R;            // bounds of the pass entries' expert, position and route fields
   int red;                   // reduction length: K (gate/up) or I (down)
   int rows;                  // output rows per expert: I row pairs (gate/up) or K (down)

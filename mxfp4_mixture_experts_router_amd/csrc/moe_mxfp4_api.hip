@@ -25,9 +25,11 @@ using moe::Plan;
 
 bool stream_regime(const moe_mxfp4_desc& d);
 bool mfma_enabled(const moe_mxfp4_desc& d);
+int stream_split(const moe_mxfp4_desc& d);
+int down_split(const moe_mxfp4_desc& d);
 
 struct Layout {
-  size_t plan, ids, weights, counts, offsets, gemv_list, mfma_list, passes, routes, pos, a, o;
+  size_t plan, ids, weights, counts, offsets, gemv_list, mfma_list, passes, passes2, routes, pos, a, o;
   size_t xq, xq_scale, aq, aq_scale;  // split activations of the scaled-FP4 MFMA kernels (0 bytes otherwise)
   size_t total;
 };
@@ -56,6 +58,8 @@ Layout make_layout(const moe_mxfp4_desc& d) {
   L.mfma_list = take(static_cast<size_t>(d.E_local) * sizeof(moe::WorkEntry));
   // decode regime: at most one pass per route
   L.passes = take(stream_regime(d) ? R * sizeof(moe::PassEntry) : 0);
+  // the down projection's own pass list, when its reduction split differs
+  L.passes2 = take(down_split(d) != stream_split(d) ? R * sizeof(moe::PassEntry) : 0);
   L.routes = take(R * 4);
   L.pos = take(R * 4);
   L.a = take(R * d.I * 2);
@@ -178,6 +182,20 @@ int stream_split(const moe_mxfp4_desc& d) {
   return split;
 }
 
+// The down projection's split.  Its items are (pass, rows) with the whole
+// reduction per workgroup when unsplit, so at decode (few routes per expert,
+// T <= 32) its 4-way split keeps more, shorter items in flight and ends the
+// launch with a shorter tail; passes then hold 4 routes, and an expert with
+// more local routes than that is read once per pass, which the few routes
+// per expert of these calls keep rare.  The plan then writes a second pass
+// list cut at 4 routes.
+int down_split(const moe_mxfp4_desc& d) {
+  const int split = stream_split(d);
+  if (split > 0 && split < 4 && d.T <= 32 && stream_fits(d.I, 4)) return 4;
+  return split;
+}
+int pass_shift_of(int split) { return split == 4 ? 2 : (split == 2 ? 3 : 4); }  // kStreamPassTokens / split routes
+
 size_t stream_lds_bytes(int red, bool gate_up, int split) {
   const size_t nw = gate_up ? 2 : 1;
   const size_t sw = (nw * 16 * (red / 32) + nw * 32 + 15) / 16 * 16;
@@ -217,9 +235,10 @@ int resident_workgroups(K kernel, size_t lds) {
 // kernels compare it with the key the plan kernel stored in the workspace.
 uint32_t plan_key(const moe_mxfp4_desc& d, bool prefill) {
   const int split = prefill ? 0 : stream_split(d);
-  const int32_t f[] = {d.T, d.K, d.I, d.E_global, d.E_local, d.expert_offset, d.top_k, split, prefill ? 1 : 0,
+  const int dsplit = prefill ? 0 : down_split(d);
+  const int32_t f[] = {d.T, d.K, d.I, d.E_global, d.E_local, d.expert_offset, d.top_k, split, dsplit, prefill ? 1 : 0,
                        mfma_enabled(d) ? 1 : 0, static_cast<int32_t>(stream_fits(d.K, split)),
-                       static_cast<int32_t>(stream_fits(d.I, split))};
+                       static_cast<int32_t>(stream_fits(d.I, dsplit))};
   uint32_t h = 2166136261u;
   for (int32_t v : f) {
     for (int b = 0; b < 4; ++b) {
@@ -267,12 +286,17 @@ hipError_t enqueue_plan(const moe_mxfp4_desc& d, const float* logits, const int3
     P.mfma_enabled = 1;
     P.gemv_max = 0;
   }
+  const int dsplit = prefill ? 0 : down_split(d);
   if (split > 0) {
     P.passes = at<moe::PassEntry>(ws, make_layout(d).passes);
-    P.pass_shift = split == 4 ? 2 : (split == 2 ? 3 : 4);  // kStreamPassTokens / split routes per pass
+    P.pass_shift = pass_shift_of(split);
+  }
+  if (dsplit != split) {
+    P.passes2 = at<moe::PassEntry>(ws, make_layout(d).passes2);
+    P.pass_shift2 = pass_shift_of(dsplit);
   }
   // the GEMV / MFMA lists are needed when a projection is not served by the stream kernel
-  P.lists = !(stream_fits(d.K, split) && stream_fits(d.I, split));
+  P.lists = !(stream_fits(d.K, split) && stream_fits(d.I, dsplit));
   if (logits != nullptr && d.T <= moe::kFusedRouteTokens) {
     P.logits = logits;
   } else if (logits != nullptr) {
@@ -639,7 +663,7 @@ hipError_t enqueue_w2(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_t*
   C.K = d.K;
   C.top_k = d.top_k;
   C.by_route = 0;
-  const int split = stream_split(d);
+  const int split = down_split(d);
   const int R = d.T * d.top_k;
   if (stream_fits(d.I, split)) {
     C.by_route = 1;
@@ -655,6 +679,10 @@ hipError_t enqueue_w2(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_t*
     S.tok_from_pass = 0;
     S.o_by_route = 1;
     S.o_out = A.o_out;
+    if (split != stream_split(d)) {
+      S.passes = at<moe::PassEntry>(ws, L.passes2);
+      S.second_list = 1;
+    }
     MOE_TRY(enqueue_stream<false>(d, split, S, s));
   } else {
     MOE_TRY(enqueue_expert_pair(d, false, A, L, ws, s));

@@ -205,6 +205,22 @@ __device__ __forceinline__ KeyCompare compare_keys(uint64_t loc, const uint64_t 
   return KeyCompare{less, eq};
 }
 
+// Route r, the j-th route of local expert e (plan position p), into its pass
+// entry of a list cut every 2^sh routes; the pass's first route writes the
+// entry's header.  `first` is the expert's first pass in the list.
+__device__ __forceinline__ void place_in_pass(PassEntry* list, int sh, int first, int e, int j, int p, int r,
+                                              const int* base_e) {
+  const int tp = 1 << sh;
+  const int pass = j >> sh, slot = j & (tp - 1);
+  PassEntry* pe = list + first + pass;
+  pe->rte[slot] = static_cast<uint16_t>(r);
+  if (slot == 0) {
+    pe->e = e;
+    pe->nt = min(tp, base_e[e + 1] - base_e[e] - pass * tp);
+    pe->p = p;
+  }
+}
+
 // Bucketing of R <= 64 routes by one wave: the counting sort of the general
 // path, written out with ballots.  Lane r holds route r; its plan position is
 // the number of local routes to lower experts plus its rank among the routes
@@ -273,11 +289,12 @@ __device__ void bucket_one_wave(const PlanArgs& P, const int32_t* ids, int R, in
     P.plan->key = P.key;
   }
 
-  if (P.passes != nullptr) {
-    const int sh = P.pass_shift, tp = 1 << sh;
+  // each pass list: an expert's routes in plan order, cut every 2^sh routes
+  auto write_passes = [&](PassEntry* list, int sh, int32_t* count) {
+    const int tp = 1 << sh;
     const uint64_t psm = __ballot(jin && (rank & (tp - 1)) == 0);
     if (jin) {
-      PassEntry* pe = P.passes + (__popcll(psm & le) - 1);
+      PassEntry* pe = list + (__popcll(psm & le) - 1);
       pe->rte[rank & (tp - 1)] = static_cast<uint16_t>(rj);
       if ((rank & (tp - 1)) == 0) {
         pe->e = ej;
@@ -285,8 +302,10 @@ __device__ void bucket_one_wave(const PlanArgs& P, const int32_t* ids, int R, in
         pe->p = j;
       }
     }
-    if (lane == 0) P.plan->n_passes = __popcll(psm);
-  }
+    if (lane == 0) *count = __popcll(psm);
+  };
+  if (P.passes != nullptr) write_passes(P.passes, P.pass_shift, &P.plan->n_passes);
+  if (P.passes2 != nullptr) write_passes(P.passes2, P.pass_shift2, &P.plan->n_passes2);
 
   if (P.lists) {
     const bool hm = first && P.mfma_enabled && cnt > P.gemv_max;
@@ -363,7 +382,7 @@ __device__ void build_lists(const PlanArgs& P, const int* base_e, const int32_t*
 constexpr int kChunkedRoutes = 512;
 
 __device__ void bucket_chunks(const PlanArgs& P, const int32_t* ids, int R, int lane, int* cnt, int* rank_s,
-                              int32_t* routes_s, int* base_e, int* pass_base) {
+                              int32_t* routes_s, int* base_e, int* pass_base, int* pass_base2) {
   const int E_l = P.E_local;
   const int bits = 32 - __clz(max(E_l - 1, 1));
   const uint64_t lt = (1ull << lane) - 1ull;
@@ -410,8 +429,9 @@ __device__ void bucket_chunks(const PlanArgs& P, const int32_t* ids, int R, int 
     P.plan->R_local = total;
     P.plan->key = P.key;
   }
-  if (P.passes != nullptr) {
-    const int sh = P.pass_shift, tp1 = (1 << sh) - 1;
+  // first pass of each expert in each pass list (exclusive scan of its pass counts)
+  auto pass_bases = [&](int sh, int* base, int32_t* count) {
+    const int tp1 = (1 << sh) - 1;
     int np = 0;
 #pragma unroll
     for (int i = 0; i < per; ++i) np += (cc[i] + tp1) >> sh;
@@ -420,11 +440,13 @@ __device__ void bucket_chunks(const PlanArgs& P, const int32_t* ids, int R, int 
 #pragma unroll
     for (int i = 0; i < per; ++i) {
       const int e = lane * per + i;
-      if (e < E_l) pass_base[e] = prun;
+      if (e < E_l) base[e] = prun;
       prun += (cc[i] + tp1) >> sh;
     }
-    if (lane == 0) P.plan->n_passes = np_total;
-  }
+    if (lane == 0) *count = np_total;
+  };
+  if (P.passes != nullptr) pass_bases(P.pass_shift, pass_base, &P.plan->n_passes);
+  if (P.passes2 != nullptr) pass_bases(P.pass_shift2, pass_base2, &P.plan->n_passes2);
   __builtin_amdgcn_wave_barrier();
   for (int c = 0; c < R; c += 64) {
     const int r = c + lane;
@@ -437,17 +459,8 @@ __device__ void bucket_chunks(const PlanArgs& P, const int32_t* ids, int R, int 
       P.routes[p] = r;
       routes_s[p] = r;
       P.pos[r] = p;
-      if (P.passes != nullptr) {
-        const int sh = P.pass_shift, tp = 1 << sh;
-        const int pass = j >> sh, slot = j & (tp - 1);
-        PassEntry* pe = P.passes + pass_base[e] + pass;
-        pe->rte[slot] = static_cast<uint16_t>(r);
-        if (slot == 0) {
-          pe->e = e;
-          pe->nt = min(tp, base_e[e + 1] - base_e[e] - pass * tp);
-          pe->p = p;
-        }
-      }
+      if (P.passes != nullptr) place_in_pass(P.passes, P.pass_shift, pass_base[e], e, j, p, r, base_e);
+      if (P.passes2 != nullptr) place_in_pass(P.passes2, P.pass_shift2, pass_base2[e], e, j, p, r, base_e);
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -500,6 +513,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
   __shared__ int base_e[kMaxLocalExperts + 1];
   __shared__ int ids_s[kFusedRouteTokens * kMaxTopK];
   __shared__ int pass_base[kMaxLocalExperts];
+  __shared__ int pass_base2[kMaxLocalExperts];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int R = P.T * P.top_k, E_l = P.E_local, offset = P.offset;
   const bool fused = P.logits != nullptr;
@@ -533,7 +547,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
     static_assert(3 * kChunkedRoutes <= kMaxLocalExperts * kPlanWaves, "LDS of the chunked path");
     if (wave == 0)
       bucket_chunks(P, fused ? ids_s : P.ids_in, R, lane, hist, hist + kMaxLocalExperts,
-                    hist + kMaxLocalExperts + kChunkedRoutes, base_e, pass_base);
+                    hist + kMaxLocalExperts + kChunkedRoutes, base_e, pass_base, pass_base2);
     return;
   }
 
@@ -632,8 +646,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
       P.plan->R_local = total;
       P.plan->key = P.key;
     }
-    if (P.passes != nullptr) {
-      const int sh = P.pass_shift, tp1 = (1 << sh) - 1;
+    auto pass_bases = [&](int sh, int* base, int32_t* count) {
+      const int tp1 = (1 << sh) - 1;
       int np = 0;
 #pragma unroll
       for (int i = 0; i < per; ++i) np += (c[i] + tp1) >> sh;
@@ -642,11 +656,13 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
 #pragma unroll
       for (int i = 0; i < per; ++i) {
         const int e = lane * per + i;
-        if (e < E_l) pass_base[e] = prun;
+        if (e < E_l) base[e] = prun;
         prun += (c[i] + tp1) >> sh;
       }
-      if (lane == 0) P.plan->n_passes = np_total;
-    }
+      if (lane == 0) *count = np_total;
+    };
+    if (P.passes != nullptr) pass_bases(P.pass_shift, pass_base, &P.plan->n_passes);
+    if (P.passes2 != nullptr) pass_bases(P.pass_shift2, pass_base2, &P.plan->n_passes2);
   }
   __syncthreads();
 
@@ -662,18 +678,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
       const int p = hist[e * kPlanWaves + wave] + __popcll(m & lt);
       P.routes[p] = r;
       P.pos[r] = p;
-      if (P.passes != nullptr) {
-        const int sh = P.pass_shift, tp = 1 << sh;
-        const int j = p - base_e[e];
-        const int pass = j >> sh, slot = j & (tp - 1);
-        PassEntry* pe = P.passes + pass_base[e] + pass;
-        pe->rte[slot] = static_cast<uint16_t>(r);
-        if (slot == 0) {
-          pe->e = e;
-          pe->nt = min(tp, base_e[e + 1] - base_e[e] - pass * tp);
-          pe->p = p;
-        }
-      }
+      if (P.passes != nullptr) place_in_pass(P.passes, P.pass_shift, pass_base[e], e, p - base_e[e], p, r, base_e);
+      if (P.passes2 != nullptr) place_in_pass(P.passes2, P.pass_shift2, pass_base2[e], e, p - base_e[e], p, r, base_e);
     }
     __builtin_amdgcn_wave_barrier();
     if (loc && (m & lt) == 0) hist[e * kPlanWaves + wave] += __popcll(m);  // next chunk of the segment

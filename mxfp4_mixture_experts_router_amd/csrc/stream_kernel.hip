@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
   // so that neither request sinks below them)
   const Plan* plan = A.plan + ((A.max_passes >> 31) & 1);
   const uint32_t plan_key = plan->key;
-  const int plan_passes = plan->n_passes;
+  const int plan_passes = A.second_list ? plan->n_passes2 : plan->n_passes;
   asm volatile("" ::"v"(ent.x), "v"(ent.y), "v"(ent.z), "v"(ent.w), "s"(plan_key), "s"(plan_passes));
   // a workspace without this call's plan gives no output; pass entries are
   // clamped to the host's bounds, so no plan value reaches outside a buffer

@@ -509,6 +509,14 @@ LAYER_CASES = [
                                    activation="swiglu_oai"), 200, 1.0),
     ("stream-regime-large-T-sigmoid", dict(K=1024, I=512, E_global=32, E_local=32, top_k=4, scoring="sigmoid"),
      128, 1.0),
+    # T <= 32 with the down projection split 4 ways (its own pass list, 4
+    # routes per pass) under a gate/up split of 1: 768 routes take the plan's
+    # general bucketing path, and every expert's 24 routes span 6 down passes
+    ("stream-down-split4-general-plan", dict(K=512, I=2048, E_global=32, E_local=32, top_k=24, bias=True), 32, 1.0),
+    # the same split pair with the one-wave (64 routes) and chunked (256 routes) plans
+    ("stream-down-split4-one-wave-plan", dict(K=1024, I=2048, E_global=16, E_local=16, top_k=4), 16, 1.0),
+    ("stream-down-split4-chunked-plan", dict(K=1024, I=2048, E_global=16, E_local=12, expert_offset=4, top_k=8,
+                                             scoring="sigmoid"), 32, 1.0),
 ]
 
 
