@@ -186,12 +186,16 @@ int stream_split(const moe_mxfp4_desc& d) {
 // reduction per workgroup when unsplit, so at decode (few routes per expert,
 // T <= 32) its 4-way split keeps more, shorter items in flight and ends the
 // launch with a shorter tail; passes then hold 4 routes, and an expert with
-// more local routes than that is read once per pass, which the few routes
-// per expert of these calls keep rare.  The plan then writes a second pass
-// list cut at 4 routes.
+// more local routes than that is read once per pass.  So it is taken only
+// when uniform routing expects at most 2 routes per expert (T * top_k <=
+// 2 * E_global): the gpt-oss-120b shape at T = 32 (1 route per expert)
+// gains ~1%, the gpt-oss-20b shape at T = 32 (4 per expert) lost 7% with
+// it.  The plan then writes a second pass list cut at 4 routes.
 int down_split(const moe_mxfp4_desc& d) {
   const int split = stream_split(d);
-  if (split > 0 && split < 4 && d.T <= 32 && stream_fits(d.I, 4)) return 4;
+  const int64_t R = static_cast<int64_t>(d.T) * d.top_k;
+  if (split > 0 && split < 4 && d.T <= 32 && R <= 2 * static_cast<int64_t>(d.E_global) && stream_fits(d.I, 4))
+    return 4;
   return split;
 }
 int pass_shift_of(int split) { return split == 4 ? 2 : (split == 2 ? 3 : 4); }  // kStreamPassTokens / split routes

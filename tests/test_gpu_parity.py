@@ -510,22 +510,26 @@ LAYER_CASES = [
     ("stream-regime-large-T-sigmoid", dict(K=1024, I=512, E_global=32, E_local=32, top_k=4, scoring="sigmoid"),
      128, 1.0),
     # T <= 32 with the down projection split 4 ways (its own pass list, 4
-    # routes per pass) under a gate/up split of 1: 768 routes take the plan's
-    # general bucketing path, and every expert's 24 routes span 6 down passes
-    ("stream-down-split4-general-plan", dict(K=512, I=2048, E_global=32, E_local=32, top_k=24, bias=True), 32, 1.0),
+    # routes per pass) under a gate/up split of 1, which needs T * top_k <=
+    # 2 * E_global; logits boosted on the slice make every route local, so
+    # each expert's routes span several down passes.  768 routes take the
+    # plan's general bucketing path (24 routes per expert, 6 down passes)
+    ("stream-down-split4-general-plan", dict(K=512, I=2048, E_global=384, E_local=32, top_k=24, bias=True), 32,
+     1.0, 30.0),
     # the same split pair with the one-wave (64 routes) and chunked (256 routes) plans
-    ("stream-down-split4-one-wave-plan", dict(K=1024, I=2048, E_global=16, E_local=16, top_k=4), 16, 1.0),
-    ("stream-down-split4-chunked-plan", dict(K=1024, I=2048, E_global=16, E_local=12, expert_offset=4, top_k=8,
-                                             scoring="sigmoid"), 32, 1.0),
+    ("stream-down-split4-one-wave-plan", dict(K=1024, I=2048, E_global=32, E_local=8, expert_offset=8, top_k=4),
+     16, 1.0, 30.0),
+    ("stream-down-split4-chunked-plan", dict(K=1024, I=2048, E_global=128, E_local=12, expert_offset=4, top_k=8,
+                                             scoring="sigmoid"), 32, 1.0, 30.0),
 ]
 
 
 @pytest.mark.parametrize("case", range(len(LAYER_CASES)))
 def test_layer_elementwise(case):
-    name, kw, T, xs = LAYER_CASES[case]
+    name, kw, T, xs, *boost = LAYER_CASES[case]
     cfg = _cfg(**kw)
     w = make_weights(cfg)
-    inp = make_inputs(cfg, T, t_index=case, x_scale=xs)
+    inp = make_inputs(cfg, T, t_index=case, x_scale=xs, all_local_boost=boost[0] if boost else 0.0)
     ref = oracle.moe_forward_cfg(cfg, w, inp)
     out = run_decode(cfg, DeviceLayer(w), inp)
     _assert_close(bf16_to_np(out), ref["y"], f"layer {name} T{T}")
