@@ -65,7 +65,8 @@ def build(verbose: bool = False) -> str:
         "flags": HIPCC_FLAGS,
         "sources": {s: _sha256(os.path.join(CSRC, s)) for s in SOURCES},
         "headers": {h: _sha256(os.path.join(d, h)) for d, h in
-                    ((INCLUDE, "moe_mxfp4.h"), (CSRC, "kernels.h"), (CSRC, "device_common.h"), (CSRC, "list_common.h"))},
+                    ((INCLUDE, "moe_mxfp4.h"), (CSRC, "kernels.h"), (CSRC, "device_common.h"), (CSRC, "list_common.h"),
+                     (CSRC, "route_plan.h"))},
         "library_sha256": _sha256(LIB_PATH),
     }
     with open(os.path.join(PKG_DIR, "libmoe_mxfp4.manifest.json"), "w") as f:

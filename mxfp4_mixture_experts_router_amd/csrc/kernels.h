@@ -42,6 +42,11 @@ static_assert(sizeof(WorkEntry) == 32, "WorkEntry is 32 bytes");
 // the plan kernel lists the passes of every touched expert in expert order.
 constexpr int kStreamMaxTokens = 64;
 constexpr int kStreamPassTokens = 16;
+// Calls of at most kSelfRoutes routes and kSelfTokens tokens whose two
+// projections both run in the stream regime skip the plan kernel: the gate/up
+// launch routes and buckets them itself (stream_kernel's kSelf form).
+constexpr int kSelfRoutes = 64;
+constexpr int kSelfTokens = 16;
 
 struct PassEntry {
   int32_t e;        // local expert
@@ -170,6 +175,7 @@ struct StreamArgs {
   float* o_out;              // down output [R, K] fp32
   int act_kind;
   float alpha, limit;
+  PlanArgs self;             // kSelf: the plan this launch makes (routing inputs, workspace outputs)
 };
 
 
@@ -213,8 +219,9 @@ __global__ void unpack_kernel(const uint8_t* packed, const uint8_t* scales, int 
                               const int32_t* counts, uint16_t* out);
 // Decode regime: kSplit waves share one 16-row sub-tile and split the
 // reduction (kSplit = 4, 2 or 1 for up to 4, 8 or 16 routes per pass); with
-// kPair (down projection, rows % 32 == 0) a wave's sub-tile is 32 rows.
-template <bool kGateUp, int kSplit, bool kPair>
+// kPair (down projection, rows % 32 == 0) a wave's sub-tile is 32 rows; with
+// kSelf (gate/up, at most kSelfRoutes routes) the launch makes the plan itself.
+template <bool kGateUp, int kSplit, bool kPair, bool kSelf = false>
 __global__ void stream_kernel(StreamArgs A);
 constexpr int kStreamRing = 4;   // steps (4 MX blocks per lane) in flight per wave
 constexpr int kStreamMaxItems = 32;  // items per workgroup (their entries live in LDS)

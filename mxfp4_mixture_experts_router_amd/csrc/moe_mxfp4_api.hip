@@ -281,8 +281,7 @@ moe::PlanArgs plan_args(const moe_mxfp4_desc& d, void* ws) {
 // Routing and bucketing into the workspace.  Small calls route inside the
 // plan kernel; larger ones route with one wave per token first.  The prefill
 // path puts every touched expert in the MFMA list and needs no pass list.
-hipError_t enqueue_plan(const moe_mxfp4_desc& d, const float* logits, const int32_t* ids, const float* wts, void* ws,
-                        hipStream_t s, bool prefill = false) {
+moe::PlanArgs full_plan_args(const moe_mxfp4_desc& d, void* ws, bool prefill) {
   moe::PlanArgs P = plan_args(d, ws);
   const int split = prefill ? 0 : stream_split(d);
   P.key = plan_key(d, prefill);
@@ -301,6 +300,12 @@ hipError_t enqueue_plan(const moe_mxfp4_desc& d, const float* logits, const int3
   }
   // the GEMV / MFMA lists are needed when a projection is not served by the stream kernel
   P.lists = !(stream_fits(d.K, split) && stream_fits(d.I, dsplit));
+  return P;
+}
+
+hipError_t enqueue_plan(const moe_mxfp4_desc& d, const float* logits, const int32_t* ids, const float* wts, void* ws,
+                        hipStream_t s, bool prefill = false) {
+  moe::PlanArgs P = full_plan_args(d, ws, prefill);
   if (logits != nullptr && d.T <= moe::kFusedRouteTokens) {
     P.logits = logits;
   } else if (logits != nullptr) {
@@ -525,7 +530,7 @@ struct StreamGrid {
   int resident;
 };
 
-template <bool kGateUp, int kSplit, bool kPair>
+template <bool kGateUp, int kSplit, bool kPair, bool kSelf = false>
 StreamGrid stream_grid(const moe_mxfp4_desc& d, const moe::StreamArgs& S) {
   StreamGrid G;
   G.lds = stream_lds_bytes(S.red, kGateUp || kPair, kSplit);
@@ -535,17 +540,18 @@ StreamGrid stream_grid(const moe_mxfp4_desc& d, const moe::StreamArgs& S) {
   const int item_rows = (kPair ? 128 : 64) / kSplit;
   G.passes = passes;
   G.bound = passes * ((S.rows + item_rows - 1) / item_rows);
-  G.resident = resident_workgroups(moe::stream_kernel<kGateUp, kSplit, kPair>, G.lds);
+  G.resident = resident_workgroups(moe::stream_kernel<kGateUp, kSplit, kPair, kSelf>, G.lds);
   return G;
 }
 
-template <bool kGateUp, int kSplit, bool kPair>
+template <bool kGateUp, int kSplit, bool kPair, bool kSelf = false>
 hipError_t launch_stream(const StreamGrid& G, moe::StreamArgs S, hipStream_t s) {
   int64_t grid = std::max<int64_t>(G.resident > 0 ? G.resident : 1024,
                                    (G.bound + moe::kStreamMaxItems - 1) / moe::kStreamMaxItems);
   grid = std::max<int64_t>(1, std::min<int64_t>(grid, G.bound));
   S.max_passes = static_cast<int>(G.passes);
-  return launch(moe::stream_kernel<kGateUp, kSplit, kPair>, dim3(static_cast<unsigned>(grid)), dim3(256), G.lds, s, S);
+  return launch(moe::stream_kernel<kGateUp, kSplit, kPair, kSelf>, dim3(static_cast<unsigned>(grid)), dim3(256), G.lds,
+                s, S);
 }
 
 // The down projection runs in pairs of 16-row sets per wave (two weight loads
@@ -567,6 +573,23 @@ hipError_t enqueue_stream(const moe_mxfp4_desc& d, int split, const moe::StreamA
   if (split == 4) return launch_stream_proj<kGateUp, 4>(d, S, s);
   if (split == 2) return launch_stream_proj<kGateUp, 2>(d, S, s);
   return launch_stream_proj<kGateUp, 1>(d, S, s);
+}
+
+// The gate/up launch that makes its own plan (S.self filled in).
+hipError_t enqueue_stream_self(const moe_mxfp4_desc& d, int split, const moe::StreamArgs& S, hipStream_t s) {
+  if (split == 4) return launch_stream<true, 4, false, true>(stream_grid<true, 4, false, true>(d, S), S, s);
+  if (split == 2) return launch_stream<true, 2, false, true>(stream_grid<true, 2, false, true>(d, S), S, s);
+  return launch_stream<true, 1, false, true>(stream_grid<true, 1, false, true>(d, S), S, s);
+}
+
+// Calls whose gate/up launch can make the plan itself: both projections in
+// the stream regime (no GEMV / MFMA lists), at most kSelfRoutes routes (one
+// wave buckets them) and kSelfTokens tokens (four per wave of a workgroup).
+bool self_plan_ok(const moe_mxfp4_desc& d) {
+  const int split = stream_split(d);
+  const int64_t R = static_cast<int64_t>(d.T) * d.top_k;
+  return split > 0 && stream_fits(d.K, split) && stream_fits(d.I, down_split(d)) && d.T <= moe::kSelfTokens &&
+         R <= moe::kSelfRoutes;
 }
 
 moe::StreamArgs stream_args(const moe_mxfp4_desc& d, const Layout& L, void* ws) {
@@ -592,8 +615,11 @@ void set_list_bounds(const moe_mxfp4_desc& d, moe::ExpertArgs& A, bool prefill) 
   A.list_cap = d.E_local;
 }
 
+// With `self` (a call that self_plan_ok() admits), the stream launch makes
+// the plan from those routing inputs instead of reading one.
 hipError_t enqueue_w13(const moe_mxfp4_desc& d, const uint16_t* x, const uint8_t* w13p, const uint8_t* w13s,
-                       const uint16_t* b13, uint16_t* a, void* ws, hipStream_t s) {
+                       const uint16_t* b13, uint16_t* a, void* ws, hipStream_t s,
+                       const moe::PlanArgs* self = nullptr) {
   const Layout L = make_layout(d);
   moe::ExpertArgs A{};
   A.in = x;
@@ -626,9 +652,34 @@ hipError_t enqueue_w13(const moe_mxfp4_desc& d, const uint16_t* x, const uint8_t
     S.tok_from_pass = 1;
     S.il = A.il;
     S.a_out = A.a_out;
+    if (self != nullptr) {
+      S.self = *self;
+      return enqueue_stream_self(d, split, S, s);
+    }
     return enqueue_stream<true>(d, split, S, s);
   }
   return enqueue_expert_pair(d, true, A, L, ws, s);
+}
+
+// Routing, bucketing and the gate/up projection of a decode call: one
+// launch that plans for itself where the call admits it, else the plan
+// kernel and then the gate/up launch.
+hipError_t enqueue_front(const moe_mxfp4_desc& d, const float* logits, const int32_t* ids, const float* wts,
+                         const uint16_t* x, const uint8_t* w13p, const uint8_t* w13s, const uint16_t* b13, void* ws,
+                         hipStream_t s) {
+  if (self_plan_ok(d)) {
+    moe::PlanArgs P = full_plan_args(d, ws, false);
+    if (logits != nullptr) {
+      P.logits = logits;
+    } else {
+      P.ids_in = ids;
+      P.w_in = wts;
+    }
+    return enqueue_w13(d, x, w13p, w13s, b13, nullptr, ws, s, &P);
+  }
+  hipError_t e = enqueue_plan(d, logits, ids, wts, ws, s);
+  if (e == hipSuccess) e = enqueue_w13(d, x, w13p, w13s, b13, nullptr, ws, s);
+  return e;
 }
 
 // Token sums: 1024 columns of a token per workgroup for small calls (several
@@ -759,8 +810,8 @@ int moe_mxfp4_decode(const moe_mxfp4_desc* desc, const uint16_t* x, const float*
     return MOE_ERR_ALIGN;
   if ((st = check_workspace(d, workspace, workspace_bytes)) != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = enqueue_plan(d, router_logits, topk_ids, topk_weights, workspace, s);
-  if (e == hipSuccess) e = enqueue_w13(d, x, w13_packed, w13_scales, w13_bias, nullptr, workspace, s);
+  hipError_t e = enqueue_front(d, router_logits, topk_ids, topk_weights, x, w13_packed, w13_scales, w13_bias,
+                               workspace, s);
   if (e == hipSuccess) e = enqueue_w2(d, nullptr, w2_packed, w2_scales, w2_bias, out, nullptr, workspace, s);
   return hip_status(e);
 }
@@ -801,8 +852,8 @@ int moe_mxfp4_decode_routes(const moe_mxfp4_desc* desc, const uint16_t* x, const
     return MOE_ERR_ALIGN;
   if ((st = check_workspace(d, workspace, workspace_bytes)) != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = enqueue_plan(d, router_logits, topk_ids, topk_weights, workspace, s);
-  if (e == hipSuccess) e = enqueue_w13(d, x, w13_packed, w13_scales, w13_bias, nullptr, workspace, s);
+  hipError_t e = enqueue_front(d, router_logits, topk_ids, topk_weights, x, w13_packed, w13_scales, w13_bias,
+                               workspace, s);
   if (e == hipSuccess) e = enqueue_w2(d, nullptr, w2_packed, w2_scales, w2_bias, nullptr, out_routes, workspace, s);
   return hip_status(e);
 }

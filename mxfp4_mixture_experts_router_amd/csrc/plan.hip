@@ -14,6 +14,7 @@
 // permutation is unique and reproducible.
 #include "device_common.h"
 #include "kernels.h"
+#include "route_plan.h"
 
 namespace moe {
 
@@ -32,179 +33,6 @@ __device__ __forceinline__ uint64_t same_expert_lanes(bool loc, int e, int bits)
   return m;
 }
 
-// Top-k of one token's logits by one wave: k rounds of a wave-wide arg-max
-// over the not-yet-taken experts (value descending, id ascending).  Lane j < k
-// returns the j-th winner.  Each lane holds kPer logits v[i] of experts
-// lane + 64 i (E <= 64 * kPer; entries past E are never taken).
-template <int kPer>
-__device__ __forceinline__ void load_logits(const float* __restrict__ row, int E, int lane, float (&v)[kPer]) {
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int idx = lane + 64 * i;
-    v[i] = idx < E ? row[idx] : 0.0f;
-  }
-}
-
-// Wave-wide max and sum without LDS: DPP inside rows of 16 lanes, then the
-// four row results read as scalars and combined in a fixed order.
-template <int kCtrl>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float rows_of_four(float v, int which) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), which));
-}
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp_f<0x124>(v));  // row_ror:4
-  v = fmaxf(v, dpp_f<0x128>(v));  // row_ror:8
-  return fmaxf(fmaxf(rows_of_four(v, 0), rows_of_four(v, 16)), fmaxf(rows_of_four(v, 32), rows_of_four(v, 48)));
-}
-__device__ __forceinline__ float wave_sum(float v) {
-  v += dpp_f<0xB1>(v);
-  v += dpp_f<0x4E>(v);
-  v += dpp_f<0x124>(v);
-  v += dpp_f<0x128>(v);
-  return (rows_of_four(v, 0) + rows_of_four(v, 16)) + (rows_of_four(v, 32) + rows_of_four(v, 48));
-}
-
-// Exclusive prefix sum over the 64 lanes (DPP row shifts, then the row
-// broadcasts of lanes 15 and 31); total = sum over all lanes.
-__device__ __forceinline__ int wave_exclusive_scan_dpp(int v, int& total) {
-  int x = v;
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
-  total = __builtin_amdgcn_readlane(x, 63);
-  return x - v;
-}
-
-// Top-k of one token by one wave, k rounds: the largest free logit (wave max),
-// then the lowest expert id holding it (ballot per slot; slot i holds ids
-// 64 i .. 64 i + 63, so the first slot with a match has the lowest id).
-// NaN logits rank below every number (fmaxf never returns a NaN next to a
-// number, and a NaN equals nothing): a round whose free logits are all NaN
-// takes the lowest free id.  Finite logits are the precondition of the layer;
-// this only keeps the ids distinct and in range when it is broken.
-template <int kPer>
-__device__ __forceinline__ void topk_of(const float (&v)[kPer], int E, int k, int lane, int& my_id, float& my_val) {
-  uint32_t taken = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i)
-    if (lane + 64 * i >= E) taken |= 1u << i;
-  my_id = 0;
-  my_val = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    float lm = -__builtin_inff();
-#pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      if (!((taken >> i) & 1u)) lm = fmaxf(lm, v[i]);
-    float m = wave_max(lm);
-    int win = -1;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const uint64_t b = __ballot(!((taken >> i) & 1u) && v[i] == m);
-      if (win < 0 && b != 0) win = 64 * i + __ffsll(static_cast<unsigned long long>(b)) - 1;
-    }
-    if (win < 0) {  // every free logit is NaN: the lowest free id
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const uint64_t b = __ballot(!((taken >> i) & 1u));
-        if (win < 0 && b != 0) win = 64 * i + __ffsll(static_cast<unsigned long long>(b)) - 1;
-      }
-      m = __builtin_nanf("");
-    }
-    if ((win & 63) == lane) taken |= 1u << (win >> 6);
-    if (lane == j) {
-      my_id = win;
-      my_val = m;
-    }
-  }
-}
-
-template <int kPer>
-__device__ __forceinline__ void wave_topk_n(const float* __restrict__ row, int E, int k, int lane, int& my_id,
-                                            float& my_val) {
-  float v[kPer];
-  load_logits<kPer>(row, E, lane, v);
-  topk_of<kPer>(v, E, k, lane, my_id, my_val);
-}
-
-__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int lane, int& my_id,
-                                          float& my_val) {
-  if (E <= 64) {
-    wave_topk_n<1>(row, E, k, lane, my_id, my_val);
-  } else if (E <= 128) {
-    wave_topk_n<2>(row, E, k, lane, my_id, my_val);
-  } else if (E <= 256) {
-    wave_topk_n<4>(row, E, k, lane, my_id, my_val);
-  } else if (E <= 512) {
-    wave_topk_n<8>(row, E, k, lane, my_id, my_val);
-  } else {
-    wave_topk_n<16>(row, E, k, lane, my_id, my_val);
-  }
-}
-
-__device__ __forceinline__ float wave_route_weight(float my_val, int k, int scoring, int lane) {
-  const float top0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_val), 0));
-  float p = 0.0f;
-  if (lane < k) p = (scoring == 0) ? expf(my_val - top0) : 1.0f / (1.0f + expf(-my_val));
-  return p / wave_sum(p);
-}
-
-template <int kPer>
-__device__ __forceinline__ void route_tokens(const PlanArgs& P, int* ids_s, int wave, int lane) {
-  constexpr int kMaxPerWave = kFusedRouteTokens / kPlanWaves;
-  float v[kMaxPerWave][kPer];
-#pragma unroll
-  for (int j = 0; j < kMaxPerWave; ++j) {
-    const int t = wave + kPlanWaves * j;
-    if (t < P.T) load_logits<kPer>(P.logits + static_cast<size_t>(t) * P.E_global, P.E_global, lane, v[j]);
-  }
-#pragma unroll
-  for (int j = 0; j < kMaxPerWave; ++j) {
-    const int t = wave + kPlanWaves * j;
-    if (t < P.T) {
-      int my_id;
-      float my_val;
-      topk_of<kPer>(v[j], P.E_global, P.top_k, lane, my_id, my_val);
-      const float w = wave_route_weight(my_val, P.top_k, P.scoring, lane);
-      if (lane < P.top_k) {
-        ids_s[t * P.top_k + lane] = my_id;
-        P.weights_ws[t * P.top_k + lane] = w;
-        P.ids_ws[t * P.top_k + lane] = my_id;
-      }
-    }
-  }
-}
-
-// Local routes of lanes in `loc` whose expert compares below / equal to this
-// lane's key: one ballot per expert-id bit, most significant first (bit b
-// splits the lanes still equal above b).
-struct KeyCompare {
-  uint64_t less, equal;
-};
-__device__ __forceinline__ KeyCompare compare_keys(uint64_t loc, const uint64_t (&bit_ballots)[10], int bits, int key) {
-  uint64_t less = 0, eq = loc;
-#pragma unroll
-  for (int b = 9; b >= 0; --b) {  // unrolled: the ballots stay in registers
-    if (b < bits) {
-      const uint64_t one = bit_ballots[b];
-      if ((key >> b) & 1) {
-        less |= eq & ~one;
-        eq &= one;
-      } else {
-        eq &= ~one;
-      }
-    }
-  }
-  return KeyCompare{less, eq};
-}
-
 // Route r, the j-th route of local expert e (plan position p), into its pass
 // entry of a list cut every 2^sh routes; the pass's first route writes the
 // entry's header.  `first` is the expert's first pass in the list.
@@ -221,121 +49,11 @@ __device__ __forceinline__ void place_in_pass(PassEntry* list, int sh, int first
   }
 }
 
-// Bucketing of R <= 64 routes by one wave: the counting sort of the general
-// path, written out with ballots.  Lane r holds route r; its plan position is
-// the number of local routes to lower experts plus its rank among the routes
-// to its own expert (stable).  The sorted order is staged in LDS (scratch,
-// 128 ints), from which lane j reads the route at position j to cut passes
-// and to list the touched experts.
-__device__ void bucket_one_wave(const PlanArgs& P, const int32_t* ids, int R, int lane, int* scratch) {
-  const int E_l = P.E_local;
-  const bool in = lane < R;
-  const int e = in ? ids[lane] - P.offset : -1;
-  const bool loc = in && static_cast<unsigned>(e) < static_cast<unsigned>(E_l);
-  const int bits = 32 - __clz(max(E_l - 1, 1));  // <= 9 (E_l <= 512)
-  const uint64_t lt = (1ull << lane) - 1ull, le = lt | (1ull << lane);
-  const uint64_t locm = __ballot(loc);
-  uint64_t bb[10];
-#pragma unroll
-  for (int b = 0; b < 10; ++b) bb[b] = b < bits ? __ballot(loc && ((e >> b) & 1)) : 0ull;
-  const KeyCompare c = compare_keys(locm, bb, bits, e);
-  const int p = __popcll(c.less) + __popcll(c.equal & lt);
-  const int Rl = __popcll(locm);
-  if (in) P.pos[lane] = loc ? p : -1;
-  if (loc) {
-    P.routes[p] = lane;
-    scratch[p] = lane;
-    scratch[64 + p] = e;
-  }
-  __builtin_amdgcn_wave_barrier();
-
-  // the sorted view: position j = lane
-  const int j = lane;
-  const bool jin = j < Rl;
-  const int rj = jin ? scratch[j] : 0;
-  const int ej = jin ? scratch[64 + j] : -1;
-  const int eprev = (jin && j > 0) ? scratch[64 + j - 1] : -1;
-  const bool first = jin && ej != eprev;
-  const uint64_t fm = __ballot(first);
-  const uint64_t upto = fm & le, after = fm & ~le;
-  const int start = upto ? 63 - __clzll(upto) : 0;         // first position of this expert
-  const int end = after ? __ffsll(static_cast<unsigned long long>(after)) - 1 : Rl;
-  const int rank = j - start, cnt = end - start;
-
-  // counts and offsets of every local expert: a touched one from its first
-  // position, an untouched one from the next touched expert
-  uint64_t lb[10];
-#pragma unroll
-  for (int b = 0; b < 10; ++b) lb[b] = b < bits ? __ballot(first && ((ej >> b) & 1)) : 0ull;
-  for (int e0 = 0; e0 < E_l; e0 += 64) {
-    const int ee = e0 + lane;
-    if (ee < E_l) {
-      const KeyCompare k = compare_keys(fm, lb, bits, ee);
-      const uint64_t ge = fm & ~k.less;  // leaders of experts >= ee (a suffix of the positions)
-      const int at = ge ? __ffsll(static_cast<unsigned long long>(ge)) - 1 : Rl;
-      int n = 0;
-      if (k.equal) {
-        const uint64_t nxt = fm & ~((k.equal << 1) - 1ull);
-        n = (nxt ? __ffsll(static_cast<unsigned long long>(nxt)) - 1 : Rl) - at;
-      }
-      P.counts[ee] = n;
-      P.offsets[ee] = at;
-    }
-  }
-  if (lane == 0) {
-    P.offsets[E_l] = Rl;
-    P.plan->n_touched = __popcll(fm);
-    P.plan->R_local = Rl;
-    P.plan->key = P.key;
-  }
-
-  // each pass list: an expert's routes in plan order, cut every 2^sh routes
-  auto write_passes = [&](PassEntry* list, int sh, int32_t* count) {
-    const int tp = 1 << sh;
-    const uint64_t psm = __ballot(jin && (rank & (tp - 1)) == 0);
-    if (jin) {
-      PassEntry* pe = list + (__popcll(psm & le) - 1);
-      pe->rte[rank & (tp - 1)] = static_cast<uint16_t>(rj);
-      if ((rank & (tp - 1)) == 0) {
-        pe->e = ej;
-        pe->nt = min(tp, cnt - rank);
-        pe->p = j;
-      }
-    }
-    if (lane == 0) *count = __popcll(psm);
-  };
-  if (P.passes != nullptr) write_passes(P.passes, P.pass_shift, &P.plan->n_passes);
-  if (P.passes2 != nullptr) write_passes(P.passes2, P.pass_shift2, &P.plan->n_passes2);
-
-  if (P.lists) {
-    const bool hm = first && P.mfma_enabled && cnt > P.gemv_max;
-    const bool hg = first && !hm;
-    const uint64_t mg = __ballot(hg), mm = __ballot(hm);
-    if (hg || hm) {
-      WorkEntry we;
-      we.e = ej;
-      we.p0 = j;
-      we.Te = cnt;
-#pragma unroll
-      for (int t = 0; t < kGemvMaxTokens; ++t) we.tok[t] = t < cnt ? scratch[j + t] / P.top_k : 0;
-#pragma unroll
-      for (int t = 0; t < 8 - 3 - kGemvMaxTokens; ++t) we.pad[t] = 0;
-      if (hg) P.gemv_list[__popcll(mg & lt)] = we;
-      else P.mfma_list[__popcll(mm & lt)] = we;
-    }
-    if (lane == 0) {
-      P.plan->n_gemv = __popcll(mg);
-      P.plan->n_mfma = __popcll(mm);
-    }
-  }
-  if (P.routes_out != nullptr && in) P.routes_out[lane] = jin ? rj : -1;
-}
-
 // Work lists of the touched experts in ascending order, split by regime (one
 // wave): experts with at most gemv_max routes (with the tokens of their first
 // routes) go to the GEMV list, the others to the MFMA list.  base_e holds the
 // exclusive offsets [E_l + 1]; routes_src the route of each plan position.
-__device__ void build_lists(const PlanArgs& P, const int* base_e, const int32_t* routes_src, int lane) {
+__device__ __forceinline__ void build_lists(const PlanArgs& P, const int* base_e, const int32_t* routes_src, int lane) {
   const int E_l = P.E_local;
   const uint64_t lt = (1ull << lane) - 1ull;
   int ng = 0, nm = 0;
@@ -381,7 +99,7 @@ __device__ void build_lists(const PlanArgs& P, const int* base_e, const int32_t*
 // caller), rank_s and routes_s [R], base_e [E_l + 1], pass_base [E_l].
 constexpr int kChunkedRoutes = 512;
 
-__device__ void bucket_chunks(const PlanArgs& P, const int32_t* ids, int R, int lane, int* cnt, int* rank_s,
+__device__ __forceinline__ void bucket_chunks(const PlanArgs& P, const int32_t* ids, int R, int lane, int* cnt, int* rank_s,
                               int32_t* routes_s, int* base_e, int* pass_base, int* pass_base2) {
   const int E_l = P.E_local;
   const int bits = 32 - __clz(max(E_l - 1, 1));
@@ -521,11 +239,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
   if (fused) {
     // a wave routes tokens wave, wave + 16, ... (at most kFusedRouteTokens / 16);
     // all of their logits are requested before the first top-k
-    if (P.E_global <= 64) route_tokens<1>(P, ids_s, wave, lane);
-    else if (P.E_global <= 128) route_tokens<2>(P, ids_s, wave, lane);
-    else if (P.E_global <= 256) route_tokens<4>(P, ids_s, wave, lane);
-    else if (P.E_global <= 512) route_tokens<8>(P, ids_s, wave, lane);
-    else route_tokens<16>(P, ids_s, wave, lane);
+    route_call<kPlanWaves, kFusedRouteTokens / kPlanWaves>(P, ids_s, wave, lane, true);
   } else if (P.w_in != nullptr) {
     // ids mode: the plan keeps its own copy of the caller's routing
     for (int r = tid; r < R; r += blockDim.x) {

@@ -1,0 +1,356 @@
+// Routing and the bucketing of small calls, by single waves: shared by the
+// plan kernel and by the gate/up stream kernel's self-planning form (calls
+// of at most 64 routes, where every gate/up workgroup routes and buckets the
+// call itself instead of reading a plan).  Both use these functions, so the
+// two make the same plan bit for bit.
+//
+// Routing: "MXFP4 MoE decode kernels", At a glance / Parity (gpt-oss top-4
+// softmax routing) and "GLM-5.3-Flash on Gaudi 2", Why (top-8 sigmoid
+// scoring).  Bucketing: "MXFP4 MoE decode kernels", Design, Routing inside
+// the kernel (counting sort by local expert, routes of other ranks skipped).
+#pragma once
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// Top-k of one token's logits by one wave: k rounds of a wave-wide arg-max
+// over the not-yet-taken experts (value descending, id ascending).  Lane j < k
+// returns the j-th winner.  Each lane holds kPer logits v[i] of experts
+// lane + 64 i (E <= 64 * kPer; entries past E are never taken).
+template <int kPer>
+__device__ __forceinline__ void load_logits(const float* __restrict__ row, int E, int lane, float (&v)[kPer]) {
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int idx = lane + 64 * i;
+    v[i] = idx < E ? row[idx] : 0.0f;
+  }
+}
+
+// Wave-wide sum without LDS: DPP inside rows of 16 lanes, then the four row
+// results read as scalars and added in a fixed order.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float rows_of_four(float v, int which) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), which));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x124>(v);
+  v += dpp_f<0x128>(v);
+  return (rows_of_four(v, 0) + rows_of_four(v, 16)) + (rows_of_four(v, 32) + rows_of_four(v, 48));
+}
+
+// Exclusive prefix sum over the 64 lanes (DPP row shifts, then the row
+// broadcasts of lanes 15 and 31); total = sum over all lanes.
+__device__ __forceinline__ int wave_exclusive_scan_dpp(int v, int& total) {
+  int x = v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  total = __builtin_amdgcn_readlane(x, 63);
+  return x - v;
+}
+
+// Order-preserving key of a logit: a larger logit has a larger key; -0 and
+// +0 share one key (they compare equal); every NaN takes key 1, below every
+// number (-inf is 0x007FFFFF); key 0 marks an entry that is taken or past E.
+__device__ __forceinline__ uint32_t logit_key(float v) {
+  uint32_t b = __float_as_uint(v);
+  if (b == 0x80000000u) b = 0u;
+  if (v != v) return 1u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_logit(uint32_t m) {
+  if (m == 1u) return __builtin_nanf("");
+  return __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
+}
+
+// Wave-wide maximum of a key: DPP inside rows of 16 lanes, then the four
+// row results as scalars.
+__device__ __forceinline__ uint32_t wave_max_key(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x124, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xF, 0xF, false)));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// Top-k of one token by one wave, k rounds on order-preserving keys: the
+// largest free key (wave max), then the lowest expert id holding it (one
+// ballot per slot; slot i holds ids 64 i .. 64 i + 63, so the first slot
+// with a match has the lowest id), whose key is then cleared.  Ranking:
+// logit descending, equal logits (-0 and +0 included) to the lower id, NaN
+// below every number and NaNs by id.  Finite logits are the precondition of
+// the layer; the NaN rule only keeps the ids distinct and in range when it
+// is broken.  top_k <= E, so every round finds a free entry (key >= 1).
+template <int kPer>
+__device__ __forceinline__ void topk_of(const float (&v)[kPer], int E, int k, int lane, int& my_id, float& my_val) {
+  uint32_t key[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) key[i] = lane + 64 * i < E ? logit_key(v[i]) : 0u;
+  my_id = 0;
+  my_val = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    uint32_t lm = key[0];
+#pragma unroll
+    for (int i = 1; i < kPer; ++i) lm = max(lm, key[i]);
+    const uint32_t m = wave_max_key(lm);
+    int win = -1;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const uint64_t b = __ballot(key[i] == m);
+      if (win < 0 && b != 0) win = 64 * i + __ffsll(static_cast<unsigned long long>(b)) - 1;
+    }
+    const uint32_t keep = (win & 63) == lane ? 0u : ~0u;  // this lane holds the winner: clear its slot
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) key[i] &= (win >> 6) == i ? keep : ~0u;
+    if (lane == j) {
+      my_id = win;
+      my_val = key_logit(m);
+    }
+  }
+}
+
+template <int kPer>
+__device__ __forceinline__ void wave_topk_n(const float* __restrict__ row, int E, int k, int lane, int& my_id,
+                                            float& my_val) {
+  float v[kPer];
+  load_logits<kPer>(row, E, lane, v);
+  topk_of<kPer>(v, E, k, lane, my_id, my_val);
+}
+
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int lane, int& my_id,
+                                          float& my_val) {
+  if (E <= 64) {
+    wave_topk_n<1>(row, E, k, lane, my_id, my_val);
+  } else if (E <= 128) {
+    wave_topk_n<2>(row, E, k, lane, my_id, my_val);
+  } else if (E <= 256) {
+    wave_topk_n<4>(row, E, k, lane, my_id, my_val);
+  } else if (E <= 512) {
+    wave_topk_n<8>(row, E, k, lane, my_id, my_val);
+  } else {
+    wave_topk_n<16>(row, E, k, lane, my_id, my_val);
+  }
+}
+
+__device__ __forceinline__ float wave_route_weight(float my_val, int k, int scoring, int lane) {
+  const float top0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_val), 0));
+  float p = 0.0f;
+  if (lane < k) p = (scoring == 0) ? expf(my_val - top0) : 1.0f / (1.0f + expf(-my_val));
+  return p / wave_sum(p);
+}
+
+// Routing of up to kWaves * kPerWave tokens by kWaves waves: wave w routes
+// tokens w, w + kWaves, ..., and requests all of their logits before the
+// first top-k.  The ids go to LDS (ids_s[t * top_k + j]); with write_ws
+// (uniform over the workgroup) the ids and weights also go to the workspace.
+template <int kPer, int kWaves, int kPerWave>
+__device__ __forceinline__ void route_tokens(const PlanArgs& P, int* ids_s, int wave, int lane, bool write_ws) {
+  float v[kPerWave][kPer];
+#pragma unroll
+  for (int j = 0; j < kPerWave; ++j) {
+    const int t = wave + kWaves * j;
+    if (t < P.T) load_logits<kPer>(P.logits + static_cast<size_t>(t) * P.E_global, P.E_global, lane, v[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < kPerWave; ++j) {
+    const int t = wave + kWaves * j;
+    if (t < P.T) {
+      int my_id;
+      float my_val;
+      topk_of<kPer>(v[j], P.E_global, P.top_k, lane, my_id, my_val);
+      if (lane < P.top_k) ids_s[t * P.top_k + lane] = my_id;
+      if (write_ws) {  // uniform: the weights are computed only where they are stored
+        const float w = wave_route_weight(my_val, P.top_k, P.scoring, lane);
+        if (lane < P.top_k) {
+          P.weights_ws[t * P.top_k + lane] = w;
+          P.ids_ws[t * P.top_k + lane] = my_id;
+        }
+      }
+    }
+  }
+}
+
+// route_tokens with the per-lane logit count chosen from E_global.
+template <int kWaves, int kPerWave>
+__device__ __forceinline__ void route_call(const PlanArgs& P, int* ids_s, int wave, int lane, bool write_ws) {
+  if (P.E_global <= 64) route_tokens<1, kWaves, kPerWave>(P, ids_s, wave, lane, write_ws);
+  else if (P.E_global <= 128) route_tokens<2, kWaves, kPerWave>(P, ids_s, wave, lane, write_ws);
+  else if (P.E_global <= 256) route_tokens<4, kWaves, kPerWave>(P, ids_s, wave, lane, write_ws);
+  else if (P.E_global <= 512) route_tokens<8, kWaves, kPerWave>(P, ids_s, wave, lane, write_ws);
+  else route_tokens<16, kWaves, kPerWave>(P, ids_s, wave, lane, write_ws);
+}
+
+// Local routes of lanes in `loc` whose expert compares below / equal to this
+// lane's key: one ballot per expert-id bit, most significant first (bit b
+// splits the lanes still equal above b).
+struct KeyCompare {
+  uint64_t less, equal;
+};
+__device__ __forceinline__ KeyCompare compare_keys(uint64_t loc, const uint64_t (&bit_ballots)[10], int bits, int key) {
+  uint64_t less = 0, eq = loc;
+#pragma unroll
+  for (int b = 9; b >= 0; --b) {  // unrolled: the ballots stay in registers
+    if (b < bits) {
+      const uint64_t one = bit_ballots[b];
+      if ((key >> b) & 1) {
+        less |= eq & ~one;
+        eq &= one;
+      } else {
+        eq &= ~one;
+      }
+    }
+  }
+  return KeyCompare{less, eq};
+}
+
+// Bucketing of R <= 64 routes by one wave: the counting sort of the general
+// path, written out with ballots.  Lane r holds route r; its plan position is
+// the number of local routes to lower experts plus its rank among the routes
+// to its own expert (stable).  The sorted order is staged in LDS (scratch,
+// 128 ints), from which lane j reads the route at position j.
+struct SmallBuckets {
+  int p;           // plan position of this lane's route (lanes < R), -1 when not local
+  int Rl;          // local routes
+  int bits;        // expert-id bits
+  bool jin;        // position j = lane holds a local route:
+  int rj, ej;      //   its route and local expert,
+  bool first;      //   whether it is its expert's first position,
+  int rank, cnt;   //   its rank among its expert's routes and their count
+  uint64_t fm;     // positions that start an expert
+};
+
+__device__ __forceinline__ SmallBuckets sort_small(const int32_t* ids, int R, int E_l, int offset, int lane,
+                                                   int* scratch) {
+  SmallBuckets b;
+  const bool in = lane < R;
+  const int e = in ? ids[lane] - offset : -1;
+  const bool loc = in && static_cast<unsigned>(e) < static_cast<unsigned>(E_l);
+  b.bits = 32 - __clz(max(E_l - 1, 1));  // <= 9 (E_l <= 512)
+  const uint64_t lt = (1ull << lane) - 1ull, le = lt | (1ull << lane);
+  const uint64_t locm = __ballot(loc);
+  uint64_t bb[10];
+#pragma unroll
+  for (int i = 0; i < 10; ++i) bb[i] = i < b.bits ? __ballot(loc && ((e >> i) & 1)) : 0ull;
+  const KeyCompare c = compare_keys(locm, bb, b.bits, e);
+  const int p = __popcll(c.less) + __popcll(c.equal & lt);
+  b.p = loc ? p : -1;
+  b.Rl = __popcll(locm);
+  if (loc) {
+    scratch[p] = lane;
+    scratch[64 + p] = e;
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // the sorted view: position j = lane
+  const int j = lane;
+  b.jin = j < b.Rl;
+  b.rj = b.jin ? scratch[j] : 0;
+  b.ej = b.jin ? scratch[64 + j] : -1;
+  const int eprev = (b.jin && j > 0) ? scratch[64 + j - 1] : -1;
+  b.first = b.jin && b.ej != eprev;
+  b.fm = __ballot(b.first);
+  const uint64_t upto = b.fm & le, after = b.fm & ~le;
+  const int start = upto ? 63 - __clzll(upto) : 0;  // first position of this expert
+  const int end = after ? __ffsll(static_cast<unsigned long long>(after)) - 1 : b.Rl;
+  b.rank = j - start;
+  b.cnt = end - start;
+  return b;
+}
+
+// A pass list of the sorted routes: each expert's routes in plan order, cut
+// every 2^sh routes, into `list` (global memory or LDS); *count = passes.
+__device__ __forceinline__ void small_pass_list(const SmallBuckets& b, PassEntry* list, int sh, int lane,
+                                                int32_t* count) {
+  const int tp = 1 << sh;
+  const uint64_t le = (2ull << lane) - 1ull;
+  const uint64_t psm = __ballot(b.jin && (b.rank & (tp - 1)) == 0);
+  if (b.jin) {
+    PassEntry* pe = list + (__popcll(psm & le) - 1);
+    pe->rte[b.rank & (tp - 1)] = static_cast<uint16_t>(b.rj);
+    if ((b.rank & (tp - 1)) == 0) {
+      pe->e = b.ej;
+      pe->nt = min(tp, b.cnt - b.rank);
+      pe->p = lane;
+    }
+  }
+  if (lane == 0) *count = __popcll(psm);
+}
+
+// The whole plan of R <= 64 routes by one wave, into the workspace:
+// positions, routes, counts and offsets of every local expert, the header,
+// the pass lists and (when a projection needs them) the GEMV / MFMA lists.
+__device__ __forceinline__ void bucket_one_wave(const PlanArgs& P, const int32_t* ids, int R, int lane,
+                                                int* scratch) {
+  const int E_l = P.E_local;
+  const SmallBuckets b = sort_small(ids, R, E_l, P.offset, lane, scratch);
+  const uint64_t lt = (1ull << lane) - 1ull;
+  if (lane < R) P.pos[lane] = b.p;
+  if (b.p >= 0) P.routes[b.p] = lane;
+  const int Rl = b.Rl, bits = b.bits;
+
+  // counts and offsets of every local expert: a touched one from its first
+  // position, an untouched one from the next touched expert
+  uint64_t lb[10];
+#pragma unroll
+  for (int i = 0; i < 10; ++i) lb[i] = i < bits ? __ballot(b.first && ((b.ej >> i) & 1)) : 0ull;
+  for (int e0 = 0; e0 < E_l; e0 += 64) {
+    const int ee = e0 + lane;
+    if (ee < E_l) {
+      const KeyCompare k = compare_keys(b.fm, lb, bits, ee);
+      const uint64_t ge = b.fm & ~k.less;  // leaders of experts >= ee (a suffix of the positions)
+      const int at = ge ? __ffsll(static_cast<unsigned long long>(ge)) - 1 : Rl;
+      int n = 0;
+      if (k.equal) {
+        const uint64_t nxt = b.fm & ~((k.equal << 1) - 1ull);
+        n = (nxt ? __ffsll(static_cast<unsigned long long>(nxt)) - 1 : Rl) - at;
+      }
+      P.counts[ee] = n;
+      P.offsets[ee] = at;
+    }
+  }
+  if (lane == 0) {
+    P.offsets[E_l] = Rl;
+    P.plan->n_touched = __popcll(b.fm);
+    P.plan->R_local = Rl;
+    P.plan->key = P.key;
+  }
+  if (P.passes != nullptr) small_pass_list(b, P.passes, P.pass_shift, lane, &P.plan->n_passes);
+  if (P.passes2 != nullptr) small_pass_list(b, P.passes2, P.pass_shift2, lane, &P.plan->n_passes2);
+
+  if (P.lists) {
+    const bool hm = b.first && P.mfma_enabled && b.cnt > P.gemv_max;
+    const bool hg = b.first && !hm;
+    const uint64_t mg = __ballot(hg), mm = __ballot(hm);
+    if (hg || hm) {
+      WorkEntry we;
+      we.e = b.ej;
+      we.p0 = lane;
+      we.Te = b.cnt;
+#pragma unroll
+      for (int t = 0; t < kGemvMaxTokens; ++t) we.tok[t] = t < b.cnt ? scratch[lane + t] / P.top_k : 0;
+#pragma unroll
+      for (int t = 0; t < 8 - 3 - kGemvMaxTokens; ++t) we.pad[t] = 0;
+      if (hg) P.gemv_list[__popcll(mg & lt)] = we;
+      else P.mfma_list[__popcll(mm & lt)] = we;
+    }
+    if (lane == 0) {
+      P.plan->n_gemv = __popcll(mg);
+      P.plan->n_mfma = __popcll(mm);
+    }
+  }
+  if (P.routes_out != nullptr && lane < R) P.routes_out[lane] = b.jin ? b.rj : -1;
+}
+
+}  // namespace moe

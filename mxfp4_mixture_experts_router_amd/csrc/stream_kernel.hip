@@ -28,7 +28,16 @@
 //    sub-tile are summed in LDS in slice order (fixed, so reproducible).
 // The epilogue applies bias and (gate/up) the activation of
 // device_common.h's activate(), rounding the activation to bf16.
+//
+// kSelf (gate/up of calls with at most kSelfRoutes routes, T <= kSelfTokens):
+// no plan kernel runs before this launch.  Every workgroup routes the call's
+// tokens and buckets its routes itself (route_plan.h: the plan kernel's own
+// functions, so the same plan), keeping the pass list in LDS, and workgroup 0
+// also writes the whole plan into the workspace for the down projection and
+// the combine.  That takes one dependent launch, and its memory round trips,
+// off a small call.
 #include "kernels.h"
+#include "route_plan.h"
 
 namespace moe {
 
@@ -87,9 +96,10 @@ __device__ __forceinline__ void set_priority(int remaining_items) {
 
 }  // namespace
 
-template <bool kGateUp, int kSplit, bool kPair>
+template <bool kGateUp, int kSplit, bool kPair, bool kSelf>
 __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
   static_assert(!(kGateUp && kPair), "pairing is for the down projection");
+  static_assert(kGateUp || !kSelf, "only the gate/up launch plans the call");
   constexpr int kR = kStreamRing;
   constexpr int kTp = 16 / kSplit;         // routes per pass
   constexpr int kSub = 4 / kSplit;         // wave sub-tiles per item
@@ -122,34 +132,75 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
   const uint32_t expert_bytes = static_cast<uint32_t>(rows_e) * row_bytes;
   const uint32_t bstride = block_stride(A.tiled);
 
-  // The pass entries this workgroup may hold are requested before the plan
-  // header is read, bounded by the host's pass bound (so always inside the
-  // pass list; entries past the plan's count are dropped below): the two
-  // requests share one memory round trip.
   const int P = gridDim.x;
   const int bid = static_cast<int>(blockIdx.x);
-  const int n_bound = A.max_passes * tiles;
-  const int n_req = bid < n_bound ? min((n_bound - 1 - bid) / P + 1, kStreamMaxItems) : 0;
-  const int e_idx = bid + (tid >> 2) * P;  // item of this thread's entry part
-  const int e_pass = e_idx / tiles;
+  int N, n_my, e_idx, e_pass;
   uint4 ent = make_uint4(0u, 0u, 0u, 0u);
-  if (tid < 4 * n_req) ent = reinterpret_cast<const uint4*>(A.passes + e_pass)[tid & 3];
-  // (the header's address depends on the pass bound, 0 for any valid one, so
-  // that its request does not come before the bound's and the wait for the
-  // bound does not also wait for it; both values are taken before the checks
-  // so that neither request sinks below them)
-  const Plan* plan = A.plan + ((A.max_passes >> 31) & 1);
-  const uint32_t plan_key = plan->key;
-  const int plan_passes = A.second_list ? plan->n_passes2 : plan->n_passes;
-  asm volatile("" ::"v"(ent.x), "v"(ent.y), "v"(ent.z), "v"(ent.w), "s"(plan_key), "s"(plan_passes));
-  // a workspace without this call's plan gives no output; pass entries are
-  // clamped to the host's bounds, so no plan value reaches outside a buffer
-  if (plan_key != A.key) return;
-  const int N = min(max(plan_passes, 0), A.max_passes) * tiles;
-  if (bid >= N) return;  // whole workgroup
-  // items of this workgroup (the host's grid keeps this <= kStreamMaxItems; the
-  // min only guards the LDS table)
-  const int n_my = min((N - 1 - bid) / P + 1, kStreamMaxItems);
+  if constexpr (kSelf) {
+    // the call's routing and pass list, in the staging buffers (unused until
+    // the first step is staged): ids [kSelfRoutes] | two sort scratches of
+    // 128 ints | pass count | pass list [kSelfRoutes] at byte 2048
+    const PlanArgs& Q = A.self;
+    int* ids_l = reinterpret_cast<int*>(lds);
+    int* sort0 = ids_l + kSelfRoutes;
+    int* sort1 = sort0 + 128;
+    int* np_l = sort1 + 128;
+    PassEntry* ptab = reinterpret_cast<PassEntry*>(lds + 2048);
+    const int R = Q.T * Q.top_k;
+    // the workgroups sharing a CU (bids 256 apart under the usual dispatch
+    // order) give their single-wave jobs (a lone token's routing, the sort)
+    // to different SIMDs: virtual wave vw = 0 is a different wave in each
+    const int vw = (wave - (bid >> 8)) & 3;
+    if (Q.logits != nullptr) {
+      route_call<4, kSelfTokens / 4>(Q, ids_l, vw, lane, bid == 0);
+    } else if (tid < R) {
+      ids_l[tid] = Q.ids_in[tid];
+      if (bid == 0 && Q.w_in != nullptr) {  // the plan keeps its own copy of the caller's routing
+        Q.weights_ws[tid] = Q.w_in[tid];
+        Q.ids_ws[tid] = Q.ids_in[tid];
+      }
+    }
+    __syncthreads();
+    if (vw == 0) {
+      const SmallBuckets b = sort_small(ids_l, R, Q.E_local, Q.offset, lane, sort0);
+      small_pass_list(b, ptab, Q.pass_shift, lane, np_l);
+    } else if (vw == 1 && bid == 0) {
+      bucket_one_wave(Q, ids_l, R, lane, sort1);
+    }
+    __syncthreads();
+    N = min(max(*np_l, 0), A.max_passes) * tiles;
+    if (bid >= N) return;  // whole workgroup
+    n_my = min((N - 1 - bid) / P + 1, kStreamMaxItems);
+    e_idx = bid + (tid >> 2) * P;
+    e_pass = e_idx / tiles;
+    if (tid < 4 * n_my) ent = reinterpret_cast<const uint4*>(ptab + e_pass)[tid & 3];
+  } else {
+    // The pass entries this workgroup may hold are requested before the plan
+    // header is read, bounded by the host's pass bound (so always inside the
+    // pass list; entries past the plan's count are dropped below): the two
+    // requests share one memory round trip.
+    const int n_bound = A.max_passes * tiles;
+    const int n_req = bid < n_bound ? min((n_bound - 1 - bid) / P + 1, kStreamMaxItems) : 0;
+    e_idx = bid + (tid >> 2) * P;  // item of this thread's entry part
+    e_pass = e_idx / tiles;
+    if (tid < 4 * n_req) ent = reinterpret_cast<const uint4*>(A.passes + e_pass)[tid & 3];
+    // (the header's address depends on the pass bound, 0 for any valid one, so
+    // that its request does not come before the bound's and the wait for the
+    // bound does not also wait for it; both values are taken before the checks
+    // so that neither request sinks below them)
+    const Plan* plan = A.plan + ((A.max_passes >> 31) & 1);
+    const uint32_t plan_key = plan->key;
+    const int plan_passes = A.second_list ? plan->n_passes2 : plan->n_passes;
+    asm volatile("" ::"v"(ent.x), "v"(ent.y), "v"(ent.z), "v"(ent.w), "s"(plan_key), "s"(plan_passes));
+    // a workspace without this call's plan gives no output; pass entries are
+    // clamped to the host's bounds, so no plan value reaches outside a buffer
+    if (plan_key != A.key) return;
+    N = min(max(plan_passes, 0), A.max_passes) * tiles;
+    if (bid >= N) return;  // whole workgroup
+    // items of this workgroup (the host's grid keeps this <= kStreamMaxItems; the
+    // min only guards the LDS table)
+    n_my = min((N - 1 - bid) / P + 1, kStreamMaxItems);
+  }
   const int total = n_my * NCp;
 
   // LDS: [2][kXBufBytes] staged activations | per (buffer, wave) scale strips
@@ -387,14 +438,17 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
     if (g0 + s < total) step(g0 + s, s);
 }
 
-template __global__ void stream_kernel<true, 1, false>(StreamArgs);
-template __global__ void stream_kernel<true, 2, false>(StreamArgs);
-template __global__ void stream_kernel<true, 4, false>(StreamArgs);
-template __global__ void stream_kernel<false, 1, false>(StreamArgs);
-template __global__ void stream_kernel<false, 2, false>(StreamArgs);
-template __global__ void stream_kernel<false, 4, false>(StreamArgs);
-template __global__ void stream_kernel<false, 1, true>(StreamArgs);
-template __global__ void stream_kernel<false, 2, true>(StreamArgs);
-template __global__ void stream_kernel<false, 4, true>(StreamArgs);
+template __global__ void stream_kernel<true, 1, false, false>(StreamArgs);
+template __global__ void stream_kernel<true, 2, false, false>(StreamArgs);
+template __global__ void stream_kernel<true, 4, false, false>(StreamArgs);
+template __global__ void stream_kernel<false, 1, false, false>(StreamArgs);
+template __global__ void stream_kernel<false, 2, false, false>(StreamArgs);
+template __global__ void stream_kernel<false, 4, false, false>(StreamArgs);
+template __global__ void stream_kernel<false, 1, true, false>(StreamArgs);
+template __global__ void stream_kernel<false, 2, true, false>(StreamArgs);
+template __global__ void stream_kernel<false, 4, true, false>(StreamArgs);
+template __global__ void stream_kernel<true, 1, false, true>(StreamArgs);
+template __global__ void stream_kernel<true, 2, false, true>(StreamArgs);
+template __global__ void stream_kernel<true, 4, false, true>(StreamArgs);
 
 }  // namespace moe

@@ -18,7 +18,8 @@ import pytest
 
 import mxfp4_mixture_experts_router_amd as moe
 import oracle
-from workloads import LayerConfig, LayerWeights, get_config, make_inputs, make_topk_inputs, make_weights
+from workloads import (LayerConfig, LayerInputs, LayerWeights, get_config, make_inputs, make_topk_inputs,
+                       make_weights)
 
 from gpu_util import (DeviceLayer, bf16_bits_np, bf16_to_np, desc_for, dev_bf16, dev_f32, dev_i32, dev_u8,
                       run_decode, torch)
@@ -473,6 +474,88 @@ def test_steps_compose_to_decode():
     moe.moe_mxfp4_down(d, layer.w2p, layer.w2s, out1, ws, w2_bias=layer.b2)
     out2 = run_decode(cfg, layer, inp)
     assert np.array_equal(bf16_bits_np(out1), bf16_bits_np(out2))
+
+
+# Calls of at most 64 routes and 16 tokens whose two projections both run in
+# the stream regime skip the plan kernel: the gate/up launch of
+# moe_mxfp4_decode routes and buckets the call in every workgroup and its
+# workgroup 0 writes the plan.  The layer output is bit-identical to the
+# three steps (plan kernel, gate/up, down) and the plan left in the
+# workspace is the plan kernel's, bit for bit.  _self_planned mirrors the
+# library's rule so that every case below is known to take that path.
+def _stream_fits(red, split):
+    return split > 0 and (((red // 32) + 3) // 4 + split - 1) // split >= 4
+
+
+def _self_planned(cfg, T):
+    R = T * cfg.top_k
+    if not (T <= 64 or (R < 65536 and R <= 16 * cfg.E_global)):
+        return False
+    split = 4 if T <= 4 else (2 if T <= 8 else 1)
+    while split > 1 and not (_stream_fits(cfg.K, split) and _stream_fits(cfg.I, split)):
+        split //= 2
+    dsplit = split
+    if 0 < split < 4 and T <= 32 and R <= 2 * cfg.E_global and _stream_fits(cfg.I, 4):
+        dsplit = 4
+    return _stream_fits(cfg.K, split) and _stream_fits(cfg.I, dsplit) and T <= 16 and R <= 64
+
+
+SELF_PLAN_CFGS = {
+    "top4": dict(K=2048, I=2048, E_global=128, E_local=16, expert_offset=40, top_k=4, activation="swiglu_oai",
+                 bias=True, scale_lo=115, scale_hi=127),
+    "top8-sigmoid": dict(K=2048, I=1024, E_global=256, E_local=32, expert_offset=96, top_k=8, scoring="sigmoid",
+                         scale_lo=115, scale_hi=127),
+    "all-experts": dict(K=1024, I=2048, E_global=24, E_local=24, top_k=4, bias=True),
+}
+SELF_PLAN_CASES = [("top4", 1, "random"), ("top4", 1, "all-local"), ("top4", 4, "random"), ("top4", 4, "all-local"),
+                   ("top4", 8, "all-local"), ("top4", 16, "random"), ("top4", 16, "all-local"),
+                   ("top4", 5, "ties"), ("top8-sigmoid", 2, "all-local"), ("top8-sigmoid", 8, "random"),
+                   ("top8-sigmoid", 8, "all-local"), ("all-experts", 16, "random"), ("all-experts", 3, "ids"),
+                   ("top4", 12, "ids")]
+
+
+@pytest.mark.parametrize("name,T,variant", SELF_PLAN_CASES)
+def test_self_planned_decode_matches_the_steps(name, T, variant):
+    t = torch()
+    cfg = _cfg(**SELF_PLAN_CFGS[name])
+    assert _self_planned(cfg, T), (name, T)
+    w = make_weights(cfg)
+    layer = DeviceLayer(w, layout="tile16")
+    if variant == "ids":
+        inp = make_topk_inputs(cfg, T, seed=T, pad_fraction=0.2)
+    elif variant == "ties":
+        inp = make_inputs(cfg, T, t_index=T)
+        rng = np.random.default_rng(T)
+        logits = (np.round(rng.standard_normal((T, cfg.E_global)) * 2) / 2).astype(np.float32)
+        logits[0] = 0.5
+        logits[1, cfg.expert_offset:cfg.expert_offset + 8] = 9.0
+        inp = LayerInputs(x=inp.x, logits=logits)
+    else:
+        inp = make_inputs(cfg, T, t_index=T, all_local_boost=30.0 if variant == "all-local" else 0.0)
+    d = desc_for(cfg, T, weight_layout="tile16")
+    nbytes = moe.moe_mxfp4_workspace_bytes(d)
+    ws1 = t.full((nbytes,), 0x5A, dtype=t.uint8, device="cuda")
+    out1 = run_decode(cfg, layer, inp, workspace=ws1)
+    if inp.logits is not None:
+        route = dict(router_logits=dev_f32(inp.logits))
+    else:
+        route = dict(topk_ids=dev_i32(inp.topk_ids), topk_weights=dev_f32(inp.topk_weights))
+    ws2 = t.full((nbytes,), 0xA5, dtype=t.uint8, device="cuda")
+    moe.moe_mxfp4_plan(d, workspace=ws2, **route)
+    moe.moe_mxfp4_gate_up(d, dev_bf16(inp.x), layer.w13p, layer.w13s, ws2, w13_bias=layer.b13)
+    out2 = t.empty((T, cfg.K), dtype=t.bfloat16, device="cuda")
+    moe.moe_mxfp4_down(d, layer.w2p, layer.w2s, out2, ws2, w2_bias=layer.b2)
+    t.cuda.synchronize()
+    what = f"{name} T={T} {variant}"
+    assert np.array_equal(bf16_bits_np(out1), bf16_bits_np(out2)), what
+    p1, p2 = _plan_read(cfg, T, d, ws1), _plan_read(cfg, T, d, ws2)
+    for k in ("ids", "counts", "offsets", "routes"):
+        assert np.array_equal(p1[k], p2[k]), (what, k)
+    assert np.array_equal(p1["w"].view(np.uint32), p2["w"].view(np.uint32)), what
+    if inp.logits is not None:
+        _check_plan(cfg, inp.logits, p1, what)
+    ref = oracle.moe_forward_cfg(cfg, w, inp)
+    _assert_close(bf16_to_np(out1), ref["y"], what)
 
 
 # --------------------------------------------------------------------------
