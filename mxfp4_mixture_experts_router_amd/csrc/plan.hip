@@ -24,11 +24,13 @@ namespace {
 // lane: the expert's bits compared lane against lane with one ballot per bit
 // (E_l <= 512: at most 9), no loop over the distinct experts.
 __device__ __forceinline__ uint64_t same_expert_lanes(bool loc, int e, int bits) {
-  uint64_t m = __ballot(loc);
+  const uint64_t locm = __ballot(loc);
+  const int ek = loc ? e : 0;
+  uint64_t m = locm;
+#pragma unroll
   for (int b = 0; b < bits; ++b) {
-    const bool bit = (e >> b) & 1;
-    const uint64_t one = __ballot(loc && bit);
-    m &= bit ? one : ~one;
+    const uint64_t one = __ballot((ek >> b) & 1) & locm;
+    m &= ((ek >> b) & 1) ? one : ~one;
   }
   return m;
 }
@@ -102,7 +104,7 @@ constexpr int kChunkedRoutes = 512;
 __device__ __forceinline__ void bucket_chunks(const PlanArgs& P, const int32_t* ids, int R, int lane, int* cnt, int* rank_s,
                               int32_t* routes_s, int* base_e, int* pass_base, int* pass_base2) {
   const int E_l = P.E_local;
-  const int bits = 32 - __clz(max(E_l - 1, 1));
+  constexpr int bits = kExpertIdBits;
   const uint64_t lt = (1ull << lane) - 1ull;
   for (int c = 0; c < R; c += 64) {
     const int r = c + lane;
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
   // the R routes in 16 contiguous segments, one per wave, 64 at a time
   const int seg = (R + kPlanWaves - 1) / kPlanWaves;
   const int s0 = min(R, wave * seg), s1 = min(R, s0 + seg);
-  const int bits = 32 - __clz(max(E_l - 1, 1));
+  constexpr int bits = kExpertIdBits;
   const uint64_t lt = (1ull << lane) - 1ull;
   // the ids of kIdBatch chunks are requested together, then the chunks are
   // processed in order (one memory latency per batch instead of per chunk);

@@ -192,6 +192,13 @@ __device__ __forceinline__ void route_call(const PlanArgs& P, int* ids_s, int wa
   else route_tokens<16, kWaves, kPerWave>(P, ids_s, wave, lane, write_ws);
 }
 
+// Bits of a local expert id (E_local <= 512).  The ballot-per-bit sorts
+// always walk all of them: the bits above an id's width are zero in every
+// lane and change no comparison, and a fixed count unrolls into straight-line
+// code (a runtime count put every ballot behind a branch of its own).
+constexpr int kExpertIdBits = 9;
+static_assert((1 << kExpertIdBits) >= kMaxLocalExperts, "expert ids fit kExpertIdBits");
+
 // Local routes of lanes in `loc` whose expert compares below / equal to this
 // lane's key: one ballot per expert-id bit, most significant first (bit b
 // splits the lanes still equal above b).
@@ -237,7 +244,7 @@ __device__ __forceinline__ SmallBuckets sort_small(const int32_t* ids, int R, in
   const bool in = lane < R;
   const int e = in ? ids[lane] - offset : -1;
   const bool loc = in && static_cast<unsigned>(e) < static_cast<unsigned>(E_l);
-  b.bits = 32 - __clz(max(E_l - 1, 1));  // <= 9 (E_l <= 512)
+  b.bits = kExpertIdBits;
   const uint64_t lt = (1ull << lane) - 1ull, le = lt | (1ull << lane);
   const uint64_t locm = __ballot(loc);
   uint64_t bb[10];
@@ -302,9 +309,10 @@ __device__ __forceinline__ void bucket_one_wave(const PlanArgs& P, const int32_t
 
   // counts and offsets of every local expert: a touched one from its first
   // position, an untouched one from the next touched expert
+  const int fk = b.first ? b.ej : 0;
   uint64_t lb[10];
 #pragma unroll
-  for (int i = 0; i < 10; ++i) lb[i] = i < bits ? __ballot(b.first && ((b.ej >> i) & 1)) : 0ull;
+  for (int i = 0; i < 10; ++i) lb[i] = i < bits ? __ballot((fk >> i) & 1) : 0ull;
   for (int e0 = 0; e0 < E_l; e0 += 64) {
     const int ee = e0 + lane;
     if (ee < E_l) {
