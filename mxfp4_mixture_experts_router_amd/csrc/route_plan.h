@@ -151,6 +151,113 @@ __device__ __forceinline__ float wave_route_weight(float my_val, int k, int scor
   return p / wave_sum(p);
 }
 
+// Maximum / minimum inside each row of 16 lanes, by DPP alone: every lane
+// of a row ends with its row's result.
+__device__ __forceinline__ uint32_t row_max_key(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x124, 0xF, 0xF, false)));
+  return max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xF, 0xF, false)));
+}
+__device__ __forceinline__ int row_min(int v) {
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false));
+  return min(v, __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));
+}
+
+// Top-k of four tokens at once, one per 16-lane row (k <= 16, E <= 16 kPer):
+// lane c of a row holds the keys of experts c + 16 i.  The ranking is
+// topk_of's (key descending, then the lowest id: the lowest slot i with a
+// match in a lane, then the row minimum over lanes).  Lane c < k of each row
+// returns its token's c-th winner; every lane gets its row's largest logit.
+template <int kPer>
+__device__ __forceinline__ void topk_rows(const float (&v)[kPer], int E, int k, int lane, int& my_id, float& my_val,
+                                          float& top0) {
+  const int c = lane & 15;
+  uint32_t key[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) key[i] = c + 16 * i < E ? logit_key(v[i]) : 0u;
+  my_id = 0;
+  my_val = 0.0f;
+  top0 = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    uint32_t lm = key[0];
+#pragma unroll
+    for (int i = 1; i < kPer; ++i) lm = max(lm, key[i]);
+    const uint32_t m = row_max_key(lm);
+    int cand = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = kPer - 1; i >= 0; --i) cand = key[i] == m ? c + 16 * i : cand;
+    const int win = row_min(cand);
+    const uint32_t keep = (win & 15) == c ? 0u : ~0u;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) key[i] &= (win >> 4) == i ? keep : ~0u;
+    const float val = key_logit(m);
+    if (j == 0) top0 = val;
+    if (c == j) {
+      my_id = win;
+      my_val = val;
+    }
+  }
+}
+
+// The routing weight of topk_rows' lane c < k.  Bit-identical to
+// wave_route_weight for a token held by a whole wave: that token's weights
+// are nonzero in lanes 0 .. k - 1 of row 0 only, so wave_sum's result is
+// lane 0's value after four in-row DPP adds, plus zeros; here the same adds
+// run inside each row and the row's first lane is read.
+__device__ __forceinline__ float row_route_weight(float my_val, float top0, int k, int scoring, int lane) {
+  float p = 0.0f;
+  if ((lane & 15) < k) p = (scoring == 0) ? expf(my_val - top0) : 1.0f / (1.0f + expf(-my_val));
+  float s = p;
+  s += dpp_f<0xB1>(s);
+  s += dpp_f<0x4E>(s);
+  s += dpp_f<0x124>(s);
+  s += dpp_f<0x128>(s);
+  const float r0 = rows_of_four(s, 0), r1 = rows_of_four(s, 16), r2 = rows_of_four(s, 32), r3 = rows_of_four(s, 48);
+  const int rho = lane >> 4;
+  const float r = rho == 0 ? r0 : (rho == 1 ? r1 : (rho == 2 ? r2 : r3));
+  return p / ((r + 0.0f) + (0.0f + 0.0f));
+}
+
+// Routing of up to 4 * kWaves * kBatches tokens, four per wave and batch:
+// wave w routes tokens 4 (w + kWaves b) + row, b < kBatches, and requests
+// all of their logits before the first top-k.  Same outputs as route_tokens.
+template <int kPer, int kWaves, int kBatches>
+__device__ __forceinline__ void route_tokens_rows(const PlanArgs& P, int* ids_s, int wave, int lane, bool write_ws) {
+  const int rho = lane >> 4, c = lane & 15;
+  float v[kBatches][kPer];
+#pragma unroll
+  for (int b = 0; b < kBatches; ++b) {
+    const int t = 4 * (wave + kWaves * b) + rho;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = c + 16 * i;
+      v[b][i] = (t < P.T && e < P.E_global) ? P.logits[static_cast<size_t>(t) * P.E_global + e] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < kBatches; ++b) {
+    const int t0 = 4 * (wave + kWaves * b);
+    if (t0 < P.T) {  // wave-uniform; rows past T route zeros and store nothing
+      int my_id;
+      float my_val, top0;
+      topk_rows<kPer>(v[b], P.E_global, P.top_k, lane, my_id, my_val, top0);
+      const int t = t0 + rho;
+      const bool st = t < P.T && c < P.top_k;
+      if (st) ids_s[t * P.top_k + c] = my_id;
+      if (write_ws) {  // uniform: the weights are computed only where they are stored
+        const float w = row_route_weight(my_val, top0, P.top_k, P.scoring, lane);
+        if (st) {
+          P.weights_ws[t * P.top_k + c] = w;
+          P.ids_ws[t * P.top_k + c] = my_id;
+        }
+      }
+    }
+  }
+}
+
 // Routing of up to kWaves * kPerWave tokens by kWaves waves: wave w routes
 // tokens w, w + kWaves, ..., and requests all of their logits before the
 // first top-k.  The ids go to LDS (ids_s[t * top_k + j]); with write_ws
@@ -183,8 +290,17 @@ __device__ __forceinline__ void route_tokens(const PlanArgs& P, int* ids_s, int 
 }
 
 // route_tokens with the per-lane logit count chosen from E_global.
+// Where a wave would route more than one token and a token's top-k fits a
+// 16-lane row (top_k <= 16, E_global <= 256), four tokens share each wave.
 template <int kWaves, int kPerWave>
 __device__ __forceinline__ void route_call(const PlanArgs& P, int* ids_s, int wave, int lane, bool write_ws) {
+  if (P.T > kWaves && P.top_k <= 16 && P.E_global <= 256) {
+    constexpr int kB = (kPerWave + 3) / 4;
+    if (P.E_global <= 64) route_tokens_rows<4, kWaves, kB>(P, ids_s, wave, lane, write_ws);
+    else if (P.E_global <= 128) route_tokens_rows<8, kWaves, kB>(P, ids_s, wave, lane, write_ws);
+    else route_tokens_rows<16, kWaves, kB>(P, ids_s, wave, lane, write_ws);
+    return;
+  }
   if (P.E_global <= 64) route_tokens<1, kWaves, kPerWave>(P, ids_s, wave, lane, write_ws);
   else if (P.E_global <= 128) route_tokens<2, kWaves, kPerWave>(P, ids_s, wave, lane, write_ws);
   else if (P.E_global <= 256) route_tokens<4, kWaves, kPerWave>(P, ids_s, wave, lane, write_ws);
