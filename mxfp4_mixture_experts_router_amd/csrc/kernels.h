@@ -44,9 +44,15 @@ constexpr int kStreamMaxTokens = 64;
 constexpr int kStreamPassTokens = 16;
 // Calls of at most kSelfRoutes routes and kSelfTokens tokens whose two
 // projections both run in the stream regime skip the plan kernel: the gate/up
-// launch routes and buckets them itself (stream_kernel's kSelf form).
-constexpr int kSelfRoutes = 64;
-constexpr int kSelfTokens = 16;
+// launch routes and buckets them itself (stream_kernel's kSelf form).  Above
+// 16 tokens that needs the four-tokens-per-wave router (top_k <= 16,
+// E_global <= 256).  LDS of the prologue: kSelfLdsBase bytes, then (above 64
+// routes) two sets of the chunked bucketing's arrays of self_bucket_ints()
+// ints each.
+constexpr int kSelfRoutes = 128;
+constexpr int kSelfTokens = 32;
+constexpr int kSelfLdsBase = 2048 + kSelfRoutes * 64;
+__host__ __device__ inline int self_bucket_ints(int E_local, int R) { return (4 * E_local + 2 * R + 1 + 3) & ~3; }
 
 struct PassEntry {
   int32_t e;        // local expert

@@ -27,6 +27,7 @@ bool stream_regime(const moe_mxfp4_desc& d);
 bool mfma_enabled(const moe_mxfp4_desc& d);
 int stream_split(const moe_mxfp4_desc& d);
 int down_split(const moe_mxfp4_desc& d);
+size_t self_lds_bytes(const moe_mxfp4_desc& d);
 
 struct Layout {
   size_t plan, ids, weights, counts, offsets, gemv_list, mfma_list, passes, passes2, routes, pos, a, o;
@@ -534,6 +535,7 @@ template <bool kGateUp, int kSplit, bool kPair, bool kSelf = false>
 StreamGrid stream_grid(const moe_mxfp4_desc& d, const moe::StreamArgs& S) {
   StreamGrid G;
   G.lds = stream_lds_bytes(S.red, kGateUp || kPair, kSplit);
+  if (kSelf) G.lds = std::max(G.lds, self_lds_bytes(d));
   const int64_t R = static_cast<int64_t>(d.T) * d.top_k;
   const int64_t tp = moe::kStreamPassTokens / kSplit;
   const int64_t passes = std::min<int64_t>(R, (R + tokens_bound(d) * (tp - 1)) / tp);
@@ -584,12 +586,19 @@ hipError_t enqueue_stream_self(const moe_mxfp4_desc& d, int split, const moe::St
 
 // Calls whose gate/up launch can make the plan itself: both projections in
 // the stream regime (no GEMV / MFMA lists), at most kSelfRoutes routes (one
-// wave buckets them) and kSelfTokens tokens (four per wave of a workgroup).
+// wave buckets them) and kSelfTokens tokens, more than 16 of them only where
+// four tokens share a wave's top-k (top_k <= 16, E_global <= 256).
 bool self_plan_ok(const moe_mxfp4_desc& d) {
   const int split = stream_split(d);
   const int64_t R = static_cast<int64_t>(d.T) * d.top_k;
   return split > 0 && stream_fits(d.K, split) && stream_fits(d.I, down_split(d)) && d.T <= moe::kSelfTokens &&
-         R <= moe::kSelfRoutes;
+         R <= moe::kSelfRoutes && (d.T <= 16 || (d.top_k <= 16 && d.E_global <= 256));
+}
+
+// LDS of the self-planning prologue (the kernel's layout).
+size_t self_lds_bytes(const moe_mxfp4_desc& d) {
+  const int R = d.T * d.top_k;
+  return moe::kSelfLdsBase + (R > 64 ? 2 * 4 * static_cast<size_t>(moe::self_bucket_ints(d.E_local, R)) : 0);
 }
 
 moe::StreamArgs stream_args(const moe_mxfp4_desc& d, const Layout& L, void* ws) {

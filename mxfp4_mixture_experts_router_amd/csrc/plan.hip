@@ -18,180 +18,6 @@
 
 namespace moe {
 
-namespace {
-
-// Lanes of the wave whose `loc` routes go to the same local expert as this
-// lane: the expert's bits compared lane against lane with one ballot per bit
-// (E_l <= 512: at most 9), no loop over the distinct experts.
-__device__ __forceinline__ uint64_t same_expert_lanes(bool loc, int e, int bits) {
-  const uint64_t locm = __ballot(loc);
-  const int ek = loc ? e : 0;
-  uint64_t m = locm;
-#pragma unroll
-  for (int b = 0; b < bits; ++b) {
-    const uint64_t one = __ballot((ek >> b) & 1) & locm;
-    m &= ((ek >> b) & 1) ? one : ~one;
-  }
-  return m;
-}
-
-// Route r, the j-th route of local expert e (plan position p), into its pass
-// entry of a list cut every 2^sh routes; the pass's first route writes the
-// entry's header.  `first` is the expert's first pass in the list.
-__device__ __forceinline__ void place_in_pass(PassEntry* list, int sh, int first, int e, int j, int p, int r,
-                                              const int* base_e) {
-  const int tp = 1 << sh;
-  const int pass = j >> sh, slot = j & (tp - 1);
-  PassEntry* pe = list + first + pass;
-  pe->rte[slot] = static_cast<uint16_t>(r);
-  if (slot == 0) {
-    pe->e = e;
-    pe->nt = min(tp, base_e[e + 1] - base_e[e] - pass * tp);
-    pe->p = p;
-  }
-}
-
-// Work lists of the touched experts in ascending order, split by regime (one
-// wave): experts with at most gemv_max routes (with the tokens of their first
-// routes) go to the GEMV list, the others to the MFMA list.  base_e holds the
-// exclusive offsets [E_l + 1]; routes_src the route of each plan position.
-__device__ __forceinline__ void build_lists(const PlanArgs& P, const int* base_e, const int32_t* routes_src, int lane) {
-  const int E_l = P.E_local;
-  const uint64_t lt = (1ull << lane) - 1ull;
-  int ng = 0, nm = 0;
-  for (int e0 = 0; e0 < E_l; e0 += 64) {
-    const int e = e0 + lane;
-    const int cnt = e < E_l ? base_e[e + 1] - base_e[e] : 0;
-    const bool hm = P.mfma_enabled && cnt > P.gemv_max;
-    const bool hg = cnt > 0 && !hm;
-    const uint64_t mg = __ballot(hg);
-    const uint64_t mm = __ballot(hm);
-    if (hg || hm) {
-      WorkEntry we;
-      we.e = e;
-      we.p0 = base_e[e];
-      we.Te = cnt;
-#pragma unroll
-      for (int j = 0; j < kGemvMaxTokens; ++j) we.tok[j] = j < cnt ? routes_src[we.p0 + j] / P.top_k : 0;
-#pragma unroll
-      for (int j = 0; j < 8 - 3 - kGemvMaxTokens; ++j) we.pad[j] = 0;
-      if (hg) {
-        P.gemv_list[ng + __popcll(mg & lt)] = we;
-      } else {
-        P.mfma_list[nm + __popcll(mm & lt)] = we;
-      }
-    }
-    ng += __popcll(mg);
-    nm += __popcll(mm);
-  }
-  if (lane == 0) {
-    P.plan->n_gemv = ng;
-    P.plan->n_mfma = nm;
-  }
-}
-
-// Bucketing of 64 < R <= kChunkedRoutes routes by one wave: the stable
-// counting sort of the general path without its workgroup barriers.  Pass 1
-// walks the routes in 64-route chunks, in route order: the lanes of a chunk
-// that go to one expert find each other with one ballot per expert-id bit,
-// rank after the expert's running count (ranks follow route order, so the
-// sort is stable) and the group's lowest lane advances the count.  The
-// counts are scanned into offsets and pass bases; pass 2 places every route
-// at its expert's offset plus its rank.  LDS: cnt [E_l] (zeroed by the
-// caller), rank_s and routes_s [R], base_e [E_l + 1], pass_base [E_l].
-constexpr int kChunkedRoutes = 512;
-
-__device__ __forceinline__ void bucket_chunks(const PlanArgs& P, const int32_t* ids, int R, int lane, int* cnt, int* rank_s,
-                              int32_t* routes_s, int* base_e, int* pass_base, int* pass_base2) {
-  const int E_l = P.E_local;
-  constexpr int bits = kExpertIdBits;
-  const uint64_t lt = (1ull << lane) - 1ull;
-  for (int c = 0; c < R; c += 64) {
-    const int r = c + lane;
-    const bool in = r < R;
-    const int e = in ? ids[r] - P.offset : -1;
-    const bool loc = in && static_cast<unsigned>(e) < static_cast<unsigned>(E_l);
-    const uint64_t m = same_expert_lanes(loc, e, bits);
-    if (loc) rank_s[r] = cnt[e] + __popcll(m & lt);
-    __builtin_amdgcn_wave_barrier();
-    if (loc && (m & lt) == 0) cnt[e] += __popcll(m);
-    __builtin_amdgcn_wave_barrier();
-    if (in && !loc) P.pos[r] = -1;
-  }
-  // counts -> offsets (and pass bases): 8 experts per lane, DPP wave scans
-  constexpr int per = kMaxLocalExperts / 64;
-  int cc[per];
-  int local = 0, nz = 0;
-#pragma unroll
-  for (int i = 0; i < per; ++i) {
-    const int e = lane * per + i;
-    cc[i] = e < E_l ? cnt[e] : 0;
-    local += cc[i];
-    nz += cc[i] > 0;
-  }
-  int total, n_touched;
-  int run = wave_exclusive_scan_dpp(local, total);
-  (void)wave_exclusive_scan_dpp(nz, n_touched);
-#pragma unroll
-  for (int i = 0; i < per; ++i) {
-    const int e = lane * per + i;
-    if (e < E_l) {
-      P.counts[e] = cc[i];
-      P.offsets[e] = run;
-      base_e[e] = run;
-    }
-    run += cc[i];
-  }
-  if (lane == 0) {
-    P.offsets[E_l] = total;
-    base_e[E_l] = total;
-    P.plan->n_touched = n_touched;
-    P.plan->R_local = total;
-    P.plan->key = P.key;
-  }
-  // first pass of each expert in each pass list (exclusive scan of its pass counts)
-  auto pass_bases = [&](int sh, int* base, int32_t* count) {
-    const int tp1 = (1 << sh) - 1;
-    int np = 0;
-#pragma unroll
-    for (int i = 0; i < per; ++i) np += (cc[i] + tp1) >> sh;
-    int np_total;
-    int prun = wave_exclusive_scan_dpp(np, np_total);
-#pragma unroll
-    for (int i = 0; i < per; ++i) {
-      const int e = lane * per + i;
-      if (e < E_l) base[e] = prun;
-      prun += (cc[i] + tp1) >> sh;
-    }
-    if (lane == 0) *count = np_total;
-  };
-  if (P.passes != nullptr) pass_bases(P.pass_shift, pass_base, &P.plan->n_passes);
-  if (P.passes2 != nullptr) pass_bases(P.pass_shift2, pass_base2, &P.plan->n_passes2);
-  __builtin_amdgcn_wave_barrier();
-  for (int c = 0; c < R; c += 64) {
-    const int r = c + lane;
-    const bool in = r < R;
-    const int e = in ? ids[r] - P.offset : -1;
-    const bool loc = in && static_cast<unsigned>(e) < static_cast<unsigned>(E_l);
-    if (loc) {
-      const int j = rank_s[r];
-      const int p = base_e[e] + j;
-      P.routes[p] = r;
-      routes_s[p] = r;
-      P.pos[r] = p;
-      if (P.passes != nullptr) place_in_pass(P.passes, P.pass_shift, pass_base[e], e, j, p, r, base_e);
-      if (P.passes2 != nullptr) place_in_pass(P.passes2, P.pass_shift2, pass_base2[e], e, j, p, r, base_e);
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
-  if (P.lists) build_lists(P, base_e, routes_s, lane);
-  if (P.routes_out != nullptr) {
-    for (int i = lane; i < R; i += 64) P.routes_out[i] = i < total ? routes_s[i] : -1;
-  }
-}
-
-}  // namespace
-
 // One wave per token, for calls too large to route inside the plan kernel.
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                          int scoring, int32_t* __restrict__ ids,
@@ -262,7 +88,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs P) {
     // up to kChunkedRoutes routes: one wave, no further workgroup barrier
     static_assert(3 * kChunkedRoutes <= kMaxLocalExperts * kPlanWaves, "LDS of the chunked path");
     if (wave == 0)
-      bucket_chunks(P, fused ? ids_s : P.ids_in, R, lane, hist, hist + kMaxLocalExperts,
+      bucket_chunks<true>(P, fused ? ids_s : P.ids_in, R, lane, hist, hist + kMaxLocalExperts,
                     hist + kMaxLocalExperts + kChunkedRoutes, base_e, pass_base, pass_base2);
     return;
   }

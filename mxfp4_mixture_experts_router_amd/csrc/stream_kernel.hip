@@ -141,9 +141,12 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
   int N, n_my, e_idx, e_pass;
   uint4 ent = make_uint4(0u, 0u, 0u, 0u);
   if constexpr (kSelf) {
-    // the call's routing and pass list, in the staging buffers (unused until
-    // the first step is staged): ids [kSelfRoutes] | two sort scratches of
-    // 128 ints | pass count | pass list [kSelfRoutes] at byte 2048
+    // the call's routing and pass list, in the staging buffers and strips
+    // (unused until the first item is entered): ids [kSelfRoutes] | two sort
+    // scratches of 128 ints | pass count | pass list [kSelfRoutes] at byte
+    // 2048 | above 64 routes, the chunked bucketing's arrays from
+    // kSelfLdsBase (the host sizes the launch's LDS for them; the pass list
+    // ends below the item table, which is filled only after the last barrier)
     const PlanArgs& Q = A.self;
     int* ids_l = reinterpret_cast<int*>(lds);
     int* sort0 = ids_l + kSelfRoutes;
@@ -165,11 +168,30 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
       }
     }
     __syncthreads();
-    if (vw == 0) {
-      const SmallBuckets b = sort_small(ids_l, R, Q.E_local, Q.offset, lane, sort0);
-      small_pass_list(b, ptab, Q.pass_shift, lane, np_l);
-    } else if (vw == 1 && bid == 0) {
-      bucket_one_wave(Q, ids_l, R, lane, sort1);
+    if (R <= 64) {
+      if (vw == 0) {
+        const SmallBuckets b = sort_small(ids_l, R, Q.E_local, Q.offset, lane, sort0);
+        small_pass_list(b, ptab, Q.pass_shift, lane, np_l);
+      } else if (vw == 1 && bid == 0) {
+        bucket_one_wave(Q, ids_l, R, lane, sort1);
+      }
+    } else if (vw == 0 || (vw == 1 && bid == 0)) {
+      // the plan kernel's chunked bucketing: the pass list into LDS, and in
+      // workgroup 0 a second wave writes the whole plan
+      const int E_l = Q.E_local;
+      int* cnt = reinterpret_cast<int*>(lds + kSelfLdsBase) + (vw == 0 ? 0 : self_bucket_ints(E_l, R));
+      int* rank_s = cnt + E_l;
+      int* routes_s = rank_s + R;
+      int* base_e = routes_s + R;
+      int* pass_base = base_e + E_l + 1;
+      int* pass_base2 = pass_base + E_l;
+      for (int e = lane; e < E_l; e += 64) cnt[e] = 0;
+      __builtin_amdgcn_wave_barrier();
+      if (vw == 0)
+        bucket_chunks<false>(Q, ids_l, R, lane, cnt, rank_s, routes_s, base_e, pass_base, pass_base2, ptab,
+                             Q.pass_shift, np_l);
+      else
+        bucket_chunks<true>(Q, ids_l, R, lane, cnt, rank_s, routes_s, base_e, pass_base, pass_base2);
     }
     __syncthreads();
     N = min(max(*np_l, 0), A.max_passes) * tiles;

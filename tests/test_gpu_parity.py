@@ -476,8 +476,9 @@ def test_steps_compose_to_decode():
     assert np.array_equal(bf16_bits_np(out1), bf16_bits_np(out2))
 
 
-# Calls of at most 64 routes and 16 tokens whose two projections both run in
-# the stream regime skip the plan kernel: the gate/up launch of
+# Calls of at most 128 routes and 32 tokens (more than 16 only with top_k <=
+# 16 and at most 256 experts) whose two projections both run in the stream
+# regime skip the plan kernel: the gate/up launch of
 # moe_mxfp4_decode routes and buckets the call in every workgroup and its
 # workgroup 0 writes the plan.  The layer output is bit-identical to the
 # three steps (plan kernel, gate/up, down) and the plan left in the
@@ -497,7 +498,8 @@ def _self_planned(cfg, T):
     dsplit = split
     if 0 < split < 4 and T <= 32 and R <= 2 * cfg.E_global and _stream_fits(cfg.I, 4):
         dsplit = 4
-    return _stream_fits(cfg.K, split) and _stream_fits(cfg.I, dsplit) and T <= 16 and R <= 64
+    return (_stream_fits(cfg.K, split) and _stream_fits(cfg.I, dsplit) and T <= 32 and R <= 128
+            and (T <= 16 or (cfg.top_k <= 16 and cfg.E_global <= 256)))
 
 
 SELF_PLAN_CFGS = {
@@ -506,12 +508,18 @@ SELF_PLAN_CFGS = {
     "top8-sigmoid": dict(K=2048, I=1024, E_global=256, E_local=32, expert_offset=96, top_k=8, scoring="sigmoid",
                          scale_lo=115, scale_hi=127),
     "all-experts": dict(K=1024, I=2048, E_global=24, E_local=24, top_k=4, bias=True),
+    # 384 experts: above 256 a token's top-k takes a whole wave, also at T > 4
+    "wide-e": dict(K=1024, I=1024, E_global=384, E_local=48, expert_offset=96, top_k=8, scoring="sigmoid"),
 }
 SELF_PLAN_CASES = [("top4", 1, "random"), ("top4", 1, "all-local"), ("top4", 4, "random"), ("top4", 4, "all-local"),
                    ("top4", 8, "all-local"), ("top4", 16, "random"), ("top4", 16, "all-local"),
                    ("top4", 5, "ties"), ("top8-sigmoid", 2, "all-local"), ("top8-sigmoid", 8, "random"),
                    ("top8-sigmoid", 8, "all-local"), ("all-experts", 16, "random"), ("all-experts", 3, "ids"),
-                   ("top4", 12, "ids")]
+                   ("top4", 12, "ids"), ("wide-e", 8, "random"), ("wide-e", 8, "all-local"),
+                   # 65 - 128 routes: the chunked bucketing inside the gate/up launch
+                   ("top4", 20, "random"), ("top4", 32, "random"), ("top4", 32, "all-local"), ("top4", 32, "ties"),
+                   ("top4", 28, "ids"), ("top8-sigmoid", 16, "random"), ("top8-sigmoid", 16, "all-local"),
+                   ("all-experts", 32, "random")]
 
 
 @pytest.mark.parametrize("name,T,variant", SELF_PLAN_CASES)
