@@ -510,6 +510,8 @@ SELF_PLAN_CFGS = {
     "all-experts": dict(K=1024, I=2048, E_global=24, E_local=24, top_k=4, bias=True),
     # 384 experts: above 256 a token's top-k takes a whole wave, also at T > 4
     "wide-e": dict(K=1024, I=1024, E_global=384, E_local=48, expert_offset=96, top_k=8, scoring="sigmoid"),
+    # 512 local experts: the largest chunked-bucketing arrays in the launch's LDS
+    "e512": dict(K=512, I=512, E_global=512, E_local=512, top_k=8, scoring="sigmoid"),
 }
 SELF_PLAN_CASES = [("top4", 1, "random"), ("top4", 1, "all-local"), ("top4", 4, "random"), ("top4", 4, "all-local"),
                    ("top4", 8, "all-local"), ("top4", 16, "random"), ("top4", 16, "all-local"),
@@ -519,7 +521,7 @@ SELF_PLAN_CASES = [("top4", 1, "random"), ("top4", 1, "all-local"), ("top4", 4, 
                    # 65 - 128 routes: the chunked bucketing inside the gate/up launch
                    ("top4", 20, "random"), ("top4", 32, "random"), ("top4", 32, "all-local"), ("top4", 32, "ties"),
                    ("top4", 28, "ids"), ("top8-sigmoid", 16, "random"), ("top8-sigmoid", 16, "all-local"),
-                   ("all-experts", 32, "random")]
+                   ("all-experts", 32, "random"), ("e512", 16, "random")]
 
 
 @pytest.mark.parametrize("name,T,variant", SELF_PLAN_CASES)
