@@ -586,13 +586,16 @@ hipError_t enqueue_stream_self(const moe_mxfp4_desc& d, int split, const moe::St
 
 // Calls whose gate/up launch can make the plan itself: both projections in
 // the stream regime (no GEMV / MFMA lists), at most kSelfRoutes routes (one
-// wave buckets them) and kSelfTokens tokens, more than 16 of them only where
-// four tokens share a wave's top-k (top_k <= 16, E_global <= 256).
+// wave buckets them) and kSelfTokens tokens.  Every workgroup routes the
+// whole call, so above 16 tokens it pays only where a top-k is cheap: with
+// at most 64 experts (the gpt-oss-20b shape at T = 32: 97.5 -> 95.9 us); with
+// 128 (gpt-oss-120b, T = 32) the prologue took 8.5 us, as long as the plan
+// launch it replaces.
 bool self_plan_ok(const moe_mxfp4_desc& d) {
   const int split = stream_split(d);
   const int64_t R = static_cast<int64_t>(d.T) * d.top_k;
   return split > 0 && stream_fits(d.K, split) && stream_fits(d.I, down_split(d)) && d.T <= moe::kSelfTokens &&
-         R <= moe::kSelfRoutes && (d.T <= 16 || (d.top_k <= 16 && d.E_global <= 256));
+         R <= moe::kSelfRoutes && (d.T <= 16 || (d.top_k <= 16 && d.E_global <= 64));
 }
 
 // LDS of the self-planning prologue (the kernel's layout).

@@ -477,7 +477,7 @@ def test_steps_compose_to_decode():
 
 
 # Calls of at most 128 routes and 32 tokens (more than 16 only with top_k <=
-# 16 and at most 256 experts) whose two projections both run in the stream
+# 16 and at most 64 experts) whose two projections both run in the stream
 # regime skip the plan kernel: the gate/up launch of
 # moe_mxfp4_decode routes and buckets the call in every workgroup and its
 # workgroup 0 writes the plan.  The layer output is bit-identical to the
@@ -499,7 +499,7 @@ def _self_planned(cfg, T):
     if 0 < split < 4 and T <= 32 and R <= 2 * cfg.E_global and _stream_fits(cfg.I, 4):
         dsplit = 4
     return (_stream_fits(cfg.K, split) and _stream_fits(cfg.I, dsplit) and T <= 32 and R <= 128
-            and (T <= 16 or (cfg.top_k <= 16 and cfg.E_global <= 256)))
+            and (T <= 16 or (cfg.top_k <= 16 and cfg.E_global <= 64)))
 
 
 SELF_PLAN_CFGS = {
@@ -512,6 +512,8 @@ SELF_PLAN_CFGS = {
     "wide-e": dict(K=1024, I=1024, E_global=384, E_local=48, expert_offset=96, top_k=8, scoring="sigmoid"),
     # 512 local experts: the largest chunked-bucketing arrays in the launch's LDS
     "e512": dict(K=512, I=512, E_global=512, E_local=512, top_k=8, scoring="sigmoid"),
+    "top4-e64": dict(K=2048, I=2048, E_global=64, E_local=16, expert_offset=40, top_k=4, activation="swiglu_oai",
+                     bias=True, scale_lo=115, scale_hi=127),
 }
 SELF_PLAN_CASES = [("top4", 1, "random"), ("top4", 1, "all-local"), ("top4", 4, "random"), ("top4", 4, "all-local"),
                    ("top4", 8, "all-local"), ("top4", 16, "random"), ("top4", 16, "all-local"),
@@ -519,8 +521,9 @@ SELF_PLAN_CASES = [("top4", 1, "random"), ("top4", 1, "all-local"), ("top4", 4, 
                    ("top8-sigmoid", 8, "all-local"), ("all-experts", 16, "random"), ("all-experts", 3, "ids"),
                    ("top4", 12, "ids"), ("wide-e", 8, "random"), ("wide-e", 8, "all-local"),
                    # 65 - 128 routes: the chunked bucketing inside the gate/up launch
-                   ("top4", 20, "random"), ("top4", 32, "random"), ("top4", 32, "all-local"), ("top4", 32, "ties"),
-                   ("top4", 28, "ids"), ("top8-sigmoid", 16, "random"), ("top8-sigmoid", 16, "all-local"),
+                   ("top4-e64", 20, "random"), ("top4-e64", 32, "random"), ("top4-e64", 32, "all-local"),
+                   ("top4-e64", 32, "ties"), ("top4-e64", 28, "ids"), ("top8-sigmoid", 16, "random"),
+                   ("top8-sigmoid", 16, "all-local"),
                    ("all-experts", 32, "random"), ("e512", 16, "random")]
 
 
