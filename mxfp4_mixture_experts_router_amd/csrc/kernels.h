@@ -197,6 +197,13 @@ __global__ void gemv_kernel(ExpertArgs A);
 // kBf16W reads the bf16-unpacked weights (prefill) instead of decoding MXFP4.
 template <bool kGateUp, int kGroups, bool kBf16W, bool kPair>
 __global__ void mfma_kernel(ExpertArgs A);
+// The down projection of the MFMA regime with four 16-row weight sets per
+// wave (256 rows per workgroup), up to 64 routes per pass, the intermediate
+// rows staged by direct buffer->LDS loads: same list, same results as
+// mfma_kernel<false, ...>; for I a multiple of 128 and K of 256.
+constexpr int kD4ScaleSlots = 3;                // per-wave LDS ring of step scales
+constexpr int kD4LdsBytes = 3 * 64 * 256 + 4 * kD4ScaleSlots * 256;
+__global__ void down4_kernel(ExpertArgs A);
 
 // Scaled-FP4 form of the MFMA regime.  Activations are first split, row by
 // row, into two E4M3 parts with one E8M0 scale each (hi = the row rounded to

@@ -150,6 +150,19 @@ int tokens_bound(const moe_mxfp4_desc& d) {
 // kernel and the launches below apply the same rule.
 bool mfma_enabled(const moe_mxfp4_desc& d) { return d.T > moe::kGemvMaxTokens; }
 
+// The GEMV list (experts with at most kGemvMaxTokens routes) is left out,
+// and every touched expert goes to the MFMA list, when uniform routing
+// expects at least kMfmaOnlyRoutes routes per expert (T * top_k / E_global):
+// then an expert with one or two routes is rare (E_local * e^-16 * 145 <
+// 0.01 at 16 per expert and 512 experts), the MFMA kernels serve it as a
+// pass of one 16-route group, and the call skips two GEMV launches that
+// would find an empty list (~5 us each at the wide-K shape, T = 2048).
+constexpr int kMfmaOnlyRoutes = 16;
+bool gemv_list_used(const moe_mxfp4_desc& d) {
+  return !mfma_enabled(d) ||
+         static_cast<int64_t>(d.T) * d.top_k < static_cast<int64_t>(kMfmaOnlyRoutes) * d.E_global;
+}
+
 // Stream regime: the persistent stream kernel, whose waves split the
 // reduction kSplit ways with 16/kSplit routes per pass.  It serves every call
 // with T <= kStreamMaxTokens, and larger calls while the routes per local
@@ -264,7 +277,7 @@ moe::PlanArgs plan_args(const moe_mxfp4_desc& d, void* ws) {
   P.offset = d.expert_offset;
   P.scoring = d.scoring;
   P.mfma_enabled = mfma_enabled(d) ? 1 : 0;
-  P.gemv_max = moe::kGemvMaxTokens;
+  P.gemv_max = gemv_list_used(d) ? moe::kGemvMaxTokens : 0;
   P.lists = 1;
   P.ids_ws = at<int32_t>(ws, L.ids);
   P.weights_ws = at<float>(ws, L.weights);
@@ -378,9 +391,15 @@ hipError_t enqueue_mfma_fp4(const moe_mxfp4_desc& d, bool gate_up, moe::ExpertAr
   return launch(moe::mfma_fp4_kernel<false, 4, false>, g, dim3(256), lds1, s, M);
 }
 
+// The four-set down kernel takes a down projection whose reduction is a
+// multiple of 128 values and whose rows fill its 256-row tiles; mfma_kernel
+// the others (and every gate/up projection).
+bool down4_fits(const moe_mxfp4_desc& d) { return d.I % 128 == 0 && d.K % 256 == 0; }
+
 // Both regimes of one projection.  Grids are host-side upper bounds: at most
 // min(E_local, T*top_k) experts are touched, and at most T*top_k / (G+1) of
-// them have more than G = kGemvMaxTokens routes; workgroups past the lists exit.
+// them have more than G = kGemvMaxTokens routes (all of them are in the MFMA
+// list when the GEMV list is left out); workgroups past the lists exit.
 // With T <= G every expert is in the GEMV list (the GEMV kernel loops over
 // token pairs if repeated ids give an expert more routes); otherwise experts
 // with more than G routes are in the MFMA list, whose token groups per pass
@@ -391,7 +410,7 @@ hipError_t enqueue_expert_pair(const moe_mxfp4_desc& d, bool gate_up, moe::Exper
   const int rows = A.rows, red = A.red;
   const int lanes = red > 4096 ? 32 : 16;
   const int rows_per_wg = 256 / lanes;
-  {
+  if (gemv_list_used(d)) {
     moe::ExpertArgs G = A;
     G.list = at<moe::WorkEntry>(ws, L.gemv_list);
     G.list_cap = d.E_local;
@@ -427,7 +446,8 @@ hipError_t enqueue_expert_pair(const moe_mxfp4_desc& d, bool gate_up, moe::Exper
     }
   }
   const int64_t R = static_cast<int64_t>(d.T) * d.top_k;
-  const int64_t mfma_experts = std::min<int64_t>(d.E_local, R / (moe::kGemvMaxTokens + 1));
+  const int64_t mfma_experts =
+      std::min<int64_t>(d.E_local, gemv_list_used(d) ? R / (moe::kGemvMaxTokens + 1) : R);
   if (mfma_experts > 0 && mfma_enabled(d)) {
     moe::ExpertArgs M = A;
     M.list = at<moe::WorkEntry>(ws, L.mfma_list);
@@ -443,6 +463,9 @@ hipError_t enqueue_expert_pair(const moe_mxfp4_desc& d, bool gate_up, moe::Exper
                         static_cast<size_t>(moe::kMfmaRows) * (red / 32);
     const int64_t slots = (mfma_experts + 7) / 8 * 8;
     if (d.mma == MOE_MMA_SCALED_FP4) return enqueue_mfma_fp4(d, gate_up, M, L, ws, groups, lds, lds1, slots, s);
+    if (!gate_up && down4_fits(d))
+      return launch(moe::down4_kernel, dim3(static_cast<unsigned>(slots * (rows / 256))), dim3(256), moe::kD4LdsBytes,
+                    s, M);
     if (gate_up) {
       const dim3 g(static_cast<unsigned>(slots * ((rows + moe::kMfmaRows - 1) / moe::kMfmaRows)));
       if (groups == 1) return launch(moe::mfma_kernel<true, 1, false, false>, g, dim3(256), lds, s, M);

@@ -944,7 +944,8 @@ def test_layer_duplicate_ids_more_routes_than_tokens():
 # Routes per expert for the list path (T > 64, or a reduction too short for
 # the stream kernel): passes of every column-group count in one launch.
 GROUP_COUNT_CASES = [
-    # T = 100, 4 groups of 16 tokens per pass: 2 routes (GEMV), 18, 40, 55, 75
+    # T = 100, 4 groups of 16 tokens per pass: 2 routes (in the MFMA list too:
+    # 25 routes per expert expected leave the GEMV list out), 18, 40, 55, 75
     # (a full 64-route pass, then 11) and 10 give passes of 2, 3, 4 and 1
     # groups; I = 384 and K = 512 leave ragged row tiles in both projections
     (100, 512, 384, [2, 18, 40, 55, 75, 10, 0, 0]),
