@@ -385,12 +385,14 @@ int moe_mxfp4_dequant(const uint8_t* packed, const uint8_t* scales, int64_t rows
  * Copy of the plan a moe_mxfp4_plan (or a layer call) left in `workspace`
  * (test hook: the routing and bucketing the layer kernels actually used):
  * ids int32 [T, top_k] and weights fp32 [T, top_k] (logits mode: the
- * router's choice, made inside the plan kernel for T <= 64; ids mode: the
- * caller's), counts int32 [E_local], offsets int32 [E_local + 1] and routes
- * int32 [T*top_k] (local route indices grouped by local expert, -1 past the
- * local routes), as moe_mxfp4_route and moe_mxfp4_bucket define them.  Any
- * output may be NULL (not written).  Same descriptor as the call that
- * planned; enqueued on `stream` after it.
+ * router's choice, made inside the gate/up launch for the small calls
+ * that plan there, inside the plan kernel for other calls of T <= 64 with
+ * E_global <= 256, and by the one-wave-per-token router for the rest; ids
+ * mode: the caller's), counts int32 [E_local], offsets int32 [E_local + 1]
+ * and routes int32 [T*top_k] (local route indices grouped by local expert,
+ * -1 past the local routes), as moe_mxfp4_route and moe_mxfp4_bucket define
+ * them.  Any output may be NULL (not written).  Same descriptor as the call
+ * that planned; enqueued on `stream` after it.
  */
 int moe_mxfp4_plan_read(const moe_mxfp4_desc* desc, const void* workspace, size_t workspace_bytes,
                         int32_t* topk_ids, float* topk_weights, int32_t* counts, int32_t* offsets,

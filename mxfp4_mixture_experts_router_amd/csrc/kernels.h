@@ -15,7 +15,7 @@ constexpr int kMaxTopK = 64;
 constexpr int kPlanWaves = 16;                          // waves of the planning workgroup
 constexpr int kMaxLocalExperts = 512;
 constexpr int kMaxDim = 8192;                           // K and I
-constexpr int kFusedRouteTokens = 64;                   // T up to this: routing runs inside the plan kernel
+constexpr int kFusedRouteTokens = 64;                   // T up to this (and E_global <= 256): routing runs inside the plan kernel
 
 // Regime per touched expert, decided on the device from its route count:
 // up to kGemvMaxTokens routes -> VALU GEMV (gemv_kernel); more -> bf16 MFMA

@@ -317,10 +317,19 @@ moe::PlanArgs full_plan_args(const moe_mxfp4_desc& d, void* ws, bool prefill) {
   return P;
 }
 
+// Router logits of calls up to kFusedRouteTokens tokens are routed inside
+// the plan kernel, on its one CU, where a token's top-k takes one 16-lane row
+// or one wave; with more than kFusedRouteMaxExperts experts, the
+// one-wave-per-token kernel spreads the tokens over the chip first, which
+// measured faster despite its launch (wide-K slice, 384 experts, top-8: T =
+// 32 / 64 from 137.7 / 206.0 to 128.6 / 182.5 us per call; with 256 experts
+// the two were equal).
+constexpr int kFusedRouteMaxExperts = 256;
+
 hipError_t enqueue_plan(const moe_mxfp4_desc& d, const float* logits, const int32_t* ids, const float* wts, void* ws,
                         hipStream_t s, bool prefill = false) {
   moe::PlanArgs P = full_plan_args(d, ws, prefill);
-  if (logits != nullptr && d.T <= moe::kFusedRouteTokens) {
+  if (logits != nullptr && d.T <= moe::kFusedRouteTokens && d.E_global <= kFusedRouteMaxExperts) {
     P.logits = logits;
   } else if (logits != nullptr) {
     MOE_TRY(launch(moe::route_topk_kernel, dim3((d.T + 3) / 4), dim3(256), 0, s, logits, d.T, d.E_global, d.top_k,
