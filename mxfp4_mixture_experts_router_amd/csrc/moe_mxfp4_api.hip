@@ -189,9 +189,21 @@ bool stream_regime(const moe_mxfp4_desc& d) {
 int steps_per_slice(int red, int split) { return ((red / 32 + 3) / 4 + split - 1) / split; }
 bool stream_fits(int red, int split) { return split > 0 && steps_per_slice(red, split) >= moe::kStreamRing; }
 
+// Wide reductions (K >= kWideSplitK) at T <= 32 with at most 2 routes per
+// expert expected split gate/up 4 ways too: a row tile's 128-value steps
+// are long enough to cut in four, and the shorter items end the launch with
+// a shorter tail (wide-K slice T = 16 / 32: 95.0 / 129.4 -> 92.0 / 122.3 us
+// per call; GLM-5.x slice T = 8 / 32: 48.1 / 104.4 -> 47.0 / 95.6 us).  At
+// K = 2880 splitting gate/up above 8 tokens measured slower, and above 32
+// tokens the 4-way split measured slower at wide K as well.
+constexpr int kWideSplitK = 4096;
+
 int stream_split(const moe_mxfp4_desc& d) {
   if (!stream_regime(d)) return 0;
   int split = d.T <= 4 ? 4 : (d.T <= 8 ? 2 : 1);
+  if (d.K >= kWideSplitK && d.T <= 32 &&
+      static_cast<int64_t>(d.T) * d.top_k <= 2 * static_cast<int64_t>(d.E_global))
+    split = 4;
   while (split > 1 && !(stream_fits(d.K, split) && stream_fits(d.I, split))) split /= 2;
   return split;
 }
