@@ -82,6 +82,7 @@ __device__ __forceinline__ uint4 as_uint4(const __attribute__((ext_vector_type(4
 }
 
 constexpr uint32_t kOob = 0x80000000u;  // buffer offset past every range: the load returns zeros
+constexpr int kNonTemporal = 2;         // cache-policy operand of a buffer load: the "nt" bit
 
 // Wave priority (0..3) from the items a workgroup still has to finish.  At
 // equal priority a CU issues for its oldest waves first, so the workgroups
@@ -308,14 +309,16 @@ __global__ __launch_bounds__(256, 2) void stream_kernel(StreamArgs A) {
   uint4 rw0[kR], rw1[kR], rx[kR];
   auto load_step = [&](int slot) {
     // weights of step (li, ls) for this lane; out-of-range blocks and steps
-    // past this workgroup's items read zeros
+    // past this workgroup's items read zeros.  Every weight byte is read
+    // once per launch, so the loads are non-temporal (aux bit 1, "nt"):
+    // gpt-oss-120b T = 32 gate/up 125 -> 112.5 us, down 69 -> 62 us.
     const int b = (kp * NCp + ls) * 4 + q;
     const bool ok = li < n_my && b < RB;
     const uint32_t o0 = ok ? l_wo + bstride * b : kOob;
-    rw0[slot] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(wrs, o0, 0, 0));
+    rw0[slot] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(wrs, o0, 0, kNonTemporal));
     if (kNW == 2) {
       const uint32_t o1 = ok ? l_wo1 + bstride * b : kOob;
-      rw1[slot] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(wrs, o1, 0, 0));
+      rw1[slot] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(wrs, o1, 0, kNonTemporal));
     }
     // activation piece of the staging thread
     const int xb = (spart * NCp + ls) * 4 + (piece >> 2);
