@@ -210,18 +210,20 @@ int stream_split(const moe_mxfp4_desc& d) {
 
 // The down projection's split.  Its items are (pass, rows) with the whole
 // reduction per workgroup when unsplit, so at decode (few routes per expert,
-// T <= 32) its 4-way split keeps more, shorter items in flight and ends the
-// launch with a shorter tail; passes then hold 4 routes, and an expert with
-// more local routes than that is read once per pass.  So it is taken only
-// when uniform routing expects at most 2 routes per expert (T * top_k <=
-// 2 * E_global): the gpt-oss-120b shape at T = 32 (1 route per expert)
-// gains ~1%, the gpt-oss-20b shape at T = 32 (4 per expert) lost 7% with
-// it.  The plan then writes a second pass list cut at 4 routes.
+// T <= 32) a 4-way (up to 8 tokens) or 2-way split keeps more, shorter items
+// in flight and ends the launch with a shorter tail; passes then hold 4 or 8
+// routes, and an expert with more local routes than that is read once per
+// pass.  So it is taken only when uniform routing expects at most 2 routes
+// per expert (T * top_k <= 2 * E_global): the gpt-oss-120b shape at T = 32
+// (1 route per expert) gains ~1% with split 4 and ~0.6% more with split 2
+// (down 62.3 -> 61.4 us), the gpt-oss-20b shape at T = 32 (4 per expert)
+// lost 7% with split 4.  The plan then writes a second pass list cut at
+// the down split's route count.
 int down_split(const moe_mxfp4_desc& d) {
   const int split = stream_split(d);
   const int64_t R = static_cast<int64_t>(d.T) * d.top_k;
   if (split > 0 && split < 4 && d.T <= 32 && R <= 2 * static_cast<int64_t>(d.E_global) && stream_fits(d.I, 4))
-    return 4;
+    return d.T > 8 ? 2 : 4;
   return split;
 }
 int pass_shift_of(int split) { return split == 4 ? 2 : (split == 2 ? 3 : 4); }  // kStreamPassTokens / split routes
