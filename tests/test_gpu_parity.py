@@ -605,18 +605,23 @@ LAYER_CASES = [
                                    activation="swiglu_oai"), 200, 1.0),
     ("stream-regime-large-T-sigmoid", dict(K=1024, I=512, E_global=32, E_local=32, top_k=4, scoring="sigmoid"),
      128, 1.0),
-    # T <= 32 with the down projection split 4 ways (its own pass list, 4
-    # routes per pass) under a gate/up split of 1, which needs T * top_k <=
+    # 8 < T <= 32 with the down projection split 2 ways (its own pass list,
+    # 8 routes per pass) under a gate/up split of 1, which needs T * top_k <=
     # 2 * E_global; logits boosted on the slice make every route local, so
     # each expert's routes span several down passes.  768 routes take the
-    # plan's general bucketing path (24 routes per expert, 6 down passes)
-    ("stream-down-split4-general-plan", dict(K=512, I=2048, E_global=384, E_local=32, top_k=24, bias=True), 32,
+    # plan's general bucketing path (24 routes per expert, 3 down passes)
+    ("stream-down-split2-general-plan", dict(K=512, I=2048, E_global=384, E_local=32, top_k=24, bias=True), 32,
      1.0, 30.0),
     # the same split pair with the one-wave (64 routes) and chunked (256 routes) plans
-    ("stream-down-split4-one-wave-plan", dict(K=1024, I=2048, E_global=32, E_local=8, expert_offset=8, top_k=4),
+    ("stream-down-split2-one-wave-plan", dict(K=1024, I=2048, E_global=32, E_local=8, expert_offset=8, top_k=4),
      16, 1.0, 30.0),
-    ("stream-down-split4-chunked-plan", dict(K=1024, I=2048, E_global=128, E_local=12, expert_offset=4, top_k=8,
+    ("stream-down-split2-chunked-plan", dict(K=1024, I=2048, E_global=128, E_local=12, expert_offset=4, top_k=8,
                                              scoring="sigmoid"), 32, 1.0, 30.0),
+    # 4 < T <= 8: the down projection split 4 ways (4 routes per pass) under a
+    # gate/up split of 2 (8 routes per pass); 8 local routes per expert, so
+    # every expert has two down passes and one gate/up pass
+    ("stream-down-split4-under-split2", dict(K=1024, I=2048, E_global=64, E_local=8, expert_offset=8, top_k=8,
+                                             scoring="sigmoid"), 8, 1.0, 30.0),
 ]
 
 
