@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["plan.hip", "expert_kernels.hip", "down4_kernel.hip", "scaled_kernels.hip", "stream_kernel.hip",
-           "moe_mxfp4_api.hip"]
+           "token_down_kernel.hip", "moe_mxfp4_api.hip"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 HIPCC_FLAGS = [

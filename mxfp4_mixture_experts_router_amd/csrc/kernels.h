@@ -242,6 +242,34 @@ constexpr int kStreamMaxItems = 32;  // items per workgroup (their entries live 
 // one token (grid: T x column blocks).
 template <int kCols>
 __global__ void combine_kernel(CombineArgs A);
+// One-token calls (T = 1, top_k <= kTokenRoutes) whose down projection runs
+// the stream kernel's 4-way split: the down projection of every local route
+// and the token sum in one launch of K / 16 workgroups (16 output rows each),
+// 16 waves = kTokenRoutes route slots x 4 reduction slices.  Same MFMA
+// sequence, slice order, bias add and combine arithmetic as
+// stream_kernel<false, 4, *> followed by combine_kernel, so the same bits.
+constexpr int kTokenRoutes = 4;
+struct TokenDownArgs {
+  const uint16_t* a;        // intermediate rows [R, I] bf16, row = plan position
+  uint32_t a_bytes;
+  const uint8_t* wp;        // w2 packed [E_l][K][I/2]
+  const uint8_t* ws;        // w2 scales [E_l][K][I/32]
+  const uint16_t* bias;     // b2 [E_l][K] bf16, or nullptr
+  const Plan* plan;
+  uint32_t key;             // the plan is used only when plan->key == key
+  const int32_t* ids;       // the plan's routing: global expert id of route j
+  const int32_t* pos;       // plan position of route j, -1 when not local
+  const float* weights;     // routing weight of route j
+  uint16_t* out;            // [1, K] bf16
+  int K, I, E_local, offset, top_k, tiled;
+  int steps;                // steps (128 reduction values) per slice: ceil(ceil(I / 128) / 4)
+};
+__global__ void token_down_kernel(TokenDownArgs A);
+// LDS of token_down_kernel: the kTokenRoutes intermediate rows, each padded to
+// 4 * steps * 256 bytes, then the 16 waves' 16 row sums.
+inline size_t token_down_lds_bytes(int steps) {
+  return static_cast<size_t>(kTokenRoutes) * 4 * steps * 256 + 16 * 16 * sizeof(float);
+}
 // Per-route output rows [R, K] fp32: rows of routes outside the slice become
 // zeros; with in_place == 0 the others are copied from o (plan order) to
 // their route's row.

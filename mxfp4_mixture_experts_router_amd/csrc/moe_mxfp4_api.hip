@@ -748,11 +748,45 @@ hipError_t launch_combine(const moe_mxfp4_desc& d, const moe::CombineArgs& C, hi
   return launch(moe::combine_kernel<4>, dim3(d.T, (d.K + 4095) / 4096), dim3(256), 0, s, C);
 }
 
+// One-token calls whose down projection would run the stream kernel's 4-way
+// split take token_down_kernel instead: the same bits in one launch, without
+// the per-route rows and the combine launch (gpt-oss-120b T = 1: ~3 us of a
+// ~24 us call).  Its LDS (the four padded intermediate rows) stays within
+// 64 KB: at most 15 steps per slice, I <= 7680.
+constexpr int kTokenDownMaxSteps = 15;
+int token_down_steps(const moe_mxfp4_desc& d) { return steps_per_slice(d.I, 4); }
+bool token_down_ok(const moe_mxfp4_desc& d) {
+  return d.T == 1 && d.top_k <= moe::kTokenRoutes && down_split(d) == 4 && stream_fits(d.I, 4) && d.K % 16 == 0 &&
+         token_down_steps(d) <= kTokenDownMaxSteps;
+}
+
 // The down projection, then either the per-token combine into out (bf16
 // [T, K]) or, with out_routes, the per-route rows (fp32 [T*top_k, K]).
 hipError_t enqueue_w2(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_t* w2p, const uint8_t* w2s,
                       const uint16_t* b2, uint16_t* out, float* out_routes, void* ws, hipStream_t s) {
   const Layout L = make_layout(d);
+  if (out_routes == nullptr && token_down_ok(d)) {
+    moe::TokenDownArgs D{};
+    D.a = a != nullptr ? a : at<uint16_t>(ws, L.a);
+    D.a_bytes = static_cast<uint32_t>(static_cast<size_t>(d.top_k) * d.I * 2);
+    D.wp = w2p;
+    D.ws = w2s;
+    D.bias = b2;
+    D.plan = at<Plan>(ws, L.plan);
+    D.key = plan_key(d, false);
+    D.ids = at<int32_t>(ws, L.ids);
+    D.pos = at<int32_t>(ws, L.pos);
+    D.weights = at<float>(ws, L.weights);
+    D.out = out;
+    D.K = d.K;
+    D.I = d.I;
+    D.E_local = d.E_local;
+    D.offset = d.expert_offset;
+    D.top_k = d.top_k;
+    D.tiled = d.weight_layout == MOE_LAYOUT_TILE16;
+    D.steps = token_down_steps(d);
+    return launch(moe::token_down_kernel, dim3(d.K / 16), dim3(1024), moe::token_down_lds_bytes(D.steps), s, D);
+  }
   moe::ExpertArgs A{};
   A.in = a != nullptr ? a : at<uint16_t>(ws, L.a);
   A.in_bytes = static_cast<uint32_t>(static_cast<size_t>(d.T) * d.top_k * d.I * 2);
