@@ -100,6 +100,14 @@ __global__ __launch_bounds__(1024) void token_down_kernel(TokenDownArgs A) {
     e = j == i ? ev[i] : e;
   }
 
+  // the sum's bias values (wave 0, lane m < 16 sums row n0 + m), requested
+  // before the rows and weights so that they are in when the sum starts
+  uint16_t bv[kTokenRoutes] = {0, 0, 0, 0};
+  if (wave == 0 && A.bias != nullptr) {
+#pragma unroll
+    for (int i = 0; i < kTokenRoutes; ++i) bv[i] = A.bias[static_cast<size_t>(ev[i]) * K + n0 + (lane & 15)];
+  }
+
   // this lane's weight row n0 + r of expert e; an empty range for a slot
   // without a local route
   const uint32_t row_bytes = static_cast<uint32_t>(I >> 1);
@@ -193,7 +201,7 @@ __global__ __launch_bounds__(1024) void token_down_kernel(TokenDownArgs A) {
       o += red[(4 * i + 1) * 16 + lane];
       o += red[(4 * i + 2) * 16 + lane];
       o += red[(4 * i + 3) * 16 + lane];
-      const float b = A.bias != nullptr ? bf16_bits_to_f32(A.bias[static_cast<size_t>(ev[i]) * K + n]) : 0.0f;
+      const float b = bf16_bits_to_f32(bv[i]);  // +0 without a bias
       o = o + b;
       y = __fadd_rn(y, __fmul_rn(wv[i], o));
     }
