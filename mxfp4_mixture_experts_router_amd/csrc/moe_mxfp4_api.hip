@@ -750,13 +750,13 @@ hipError_t launch_combine(const moe_mxfp4_desc& d, const moe::CombineArgs& C, hi
 
 // One-token calls whose down projection would run the stream kernel's 4-way
 // split take token_down_kernel instead: the same bits in one launch, without
-// the per-route rows and the combine launch (gpt-oss-120b T = 1: ~3 us of a
-// ~24 us call).  Its LDS (the four padded intermediate rows) stays within
+// the per-route rows and the combine launch (gpt-oss-120b T = 1: 24.3 ->
+// 23.0 us per call).  Its LDS (the four padded intermediate rows) stays within
 // 64 KB: at most 15 steps per slice, I <= 7680.
 constexpr int kTokenDownMaxSteps = 15;
 int token_down_steps(const moe_mxfp4_desc& d) { return steps_per_slice(d.I, 4); }
 bool token_down_ok(const moe_mxfp4_desc& d) {
-  return d.T == 1 && d.top_k <= moe::kTokenRoutes && down_split(d) == 4 && stream_fits(d.I, 4) && d.K % 16 == 0 &&
+  return d.T >= 1 && d.T <= moe::kTokenMaxTokens && d.top_k <= moe::kTokenRoutes && down_split(d) == 4 && stream_fits(d.I, 4) && d.K % 16 == 0 &&
          token_down_steps(d) <= kTokenDownMaxSteps;
 }
 
@@ -768,7 +768,7 @@ hipError_t enqueue_w2(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_t*
   if (out_routes == nullptr && token_down_ok(d)) {
     moe::TokenDownArgs D{};
     D.a = a != nullptr ? a : at<uint16_t>(ws, L.a);
-    D.a_bytes = static_cast<uint32_t>(static_cast<size_t>(d.top_k) * d.I * 2);
+    D.a_bytes = static_cast<uint32_t>(static_cast<size_t>(d.T) * d.top_k * d.I * 2);
     D.wp = w2p;
     D.ws = w2s;
     D.bias = b2;
@@ -778,6 +778,7 @@ hipError_t enqueue_w2(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_t*
     D.pos = at<int32_t>(ws, L.pos);
     D.weights = at<float>(ws, L.weights);
     D.out = out;
+    D.T = d.T;
     D.K = d.K;
     D.I = d.I;
     D.E_local = d.E_local;
@@ -785,7 +786,7 @@ hipError_t enqueue_w2(const moe_mxfp4_desc& d, const uint16_t* a, const uint8_t*
     D.top_k = d.top_k;
     D.tiled = d.weight_layout == MOE_LAYOUT_TILE16;
     D.steps = token_down_steps(d);
-    return launch(moe::token_down_kernel, dim3(d.K / 16), dim3(1024), moe::token_down_lds_bytes(D.steps), s, D);
+    return launch(moe::token_down_kernel, dim3(d.K / 16, d.T), dim3(1024), moe::token_down_lds_bytes(D.steps), s, D);
   }
   moe::ExpertArgs A{};
   A.in = a != nullptr ? a : at<uint16_t>(ws, L.a);

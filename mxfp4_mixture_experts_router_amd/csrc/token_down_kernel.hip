@@ -16,7 +16,9 @@
 // takes the per-route fp32 rows, their round trip through memory and the
 // combine launch off the smallest calls.
 //
-// Layout: K / 16 workgroups of 16 waves; every column of a wave's MFMAs
+// Layout: K / 16 workgroups of 16 waves per token (grid row = token; the
+// host launches it for one-token calls, where it measured faster than the
+// separate launches, and not above); every column of a wave's MFMAs
 // carries the same intermediate row (its route's), staged once in LDS with
 // each row padded to the four slices' steps (zeros past I).  A route slot
 // without a local route reads its weights through an empty buffer range
@@ -60,6 +62,8 @@ __global__ __launch_bounds__(1024) void token_down_kernel(TokenDownArgs A) {
   const int r = lane & 15, q = lane >> 4;
   const int j = wave >> 2, kp = wave & 3;  // route slot, reduction slice
   const int n0 = static_cast<int>(blockIdx.x) * 16;
+  const int t = static_cast<int>(blockIdx.y);  // token
+  const int k = A.top_k, R = A.T * A.top_k;
 
   // the token's route slots (plan position, expert id, weight) are requested
   // together with the plan's key, at indices valid for any plan, so that one
@@ -69,7 +73,7 @@ __global__ __launch_bounds__(1024) void token_down_kernel(TokenDownArgs A) {
   float w_[kTokenRoutes];
 #pragma unroll
   for (int i = 0; i < kTokenRoutes; ++i) {
-    const int ii = min(i, A.top_k - 1);
+    const int ii = t * k + min(i, k - 1);
     pr_[i] = A.pos[ii];
     id_[i] = A.ids[ii];
     w_[i] = A.weights[ii];
@@ -83,13 +87,13 @@ __global__ __launch_bounds__(1024) void token_down_kernel(TokenDownArgs A) {
   const int xrow_bytes = 4 * NCp * 256;  // one staged intermediate row
 
   // slot i: plan position (-1: not local), expert, weight; a position
-  // outside [0, top_k) counts as not local, as in the combine
+  // outside [0, T * top_k) counts as not local, as in the combine
   int pv[kTokenRoutes], ev[kTokenRoutes];
   float wv[kTokenRoutes];
 #pragma unroll
   for (int i = 0; i < kTokenRoutes; ++i) {
-    const bool in = i < A.top_k;
-    pv[i] = (in && pr_[i] >= 0 && pr_[i] < A.top_k) ? pr_[i] : -1;
+    const bool in = i < k;
+    pv[i] = (in && pr_[i] >= 0 && pr_[i] < R) ? pr_[i] : -1;
     ev[i] = in ? min(max(id_[i] - A.offset, 0), A.E_local - 1) : 0;
     wv[i] = in ? w_[i] : 0.0f;
   }
@@ -205,7 +209,7 @@ __global__ __launch_bounds__(1024) void token_down_kernel(TokenDownArgs A) {
       o = o + b;
       y = __fadd_rn(y, __fmul_rn(wv[i], o));
     }
-    A.out[n] = f32_to_bf16_rne(y);
+    A.out[static_cast<size_t>(t) * K + n] = f32_to_bf16_rne(y);
   }
 }
 

@@ -777,63 +777,74 @@ def test_route_outputs_match_oracle(case):
     assert oracle.rel_l2(y, ysum) <= 3e-3, name
 
 
-# One-token calls with top_k <= 4 take one launch for the down projection and
-# the token sum (token_down_kernel).  Against the per-route rows of the same
-# call (the stream kernel's 4-way split) summed here with the combine's fp32
-# arithmetic (route order, product then sum, one rounding each, bf16 at the
-# end): the same bits; and against the oracle within the bar.
+# One-token calls with top_k <= 4 take one launch for the down projection
+# and the token sum (token_down_kernel); calls of 2 - 4 tokens run the stream
+# kernel and the combine.  Either way, against the per-route rows of the same
+# call (the stream kernel's 4-way split, routes of one expert side by side in
+# its MFMA columns) summed here with the combine's fp32 arithmetic (route
+# order, product then sum, one rounding each, bf16 at the end): the same
+# bits; and against the oracle within the bar.
 TOKEN_CASES = [
     ("gpt-oss-slice", dict(K=2880, I=2880, E_global=16, E_local=6, expert_offset=4, top_k=4,
-                           activation="swiglu_oai", bias=True, scale_lo=115, scale_hi=127), "tile16", "logits", 0.0),
+                           activation="swiglu_oai", bias=True, scale_lo=115, scale_hi=127), 1, "tile16", "logits", 0.0),
     ("gpt-oss-all-local", dict(K=2880, I=2880, E_global=8, E_local=8, top_k=4, activation="swiglu_oai", bias=True,
-                               scale_lo=115, scale_hi=127), "rows", "logits", 0.0),
-    ("top2-short-K", dict(K=1056, I=2048, E_global=8, E_local=8, top_k=2), "tile16", "logits", 0.0),
-    ("top3-ragged-I", dict(K=1024, I=2080, E_global=12, E_local=3, expert_offset=5, top_k=3, bias=True), "rows",
+                               scale_lo=115, scale_hi=127), 1, "rows", "logits", 0.0),
+    ("gpt-oss-4-tokens-shared-experts", dict(K=2880, I=2880, E_global=8, E_local=8, top_k=4,
+                                             activation="swiglu_oai", bias=True, scale_lo=115, scale_hi=127), 4,
+     "tile16", "logits", 0.0),
+    ("top2-short-K", dict(K=1056, I=2048, E_global=8, E_local=8, top_k=2), 3, "tile16", "logits", 0.0),
+    ("top3-ragged-I", dict(K=1024, I=2080, E_global=12, E_local=3, expert_offset=5, top_k=3, bias=True), 2, "rows",
      "logits", 30.0),
-    ("ids-padding-foreign", dict(K=2048, I=2048, E_global=16, E_local=4, expert_offset=6, top_k=4, bias=True),
+    ("ids-padding-foreign", dict(K=2048, I=2048, E_global=16, E_local=4, expert_offset=6, top_k=4, bias=True), 4,
      "tile16", "ids", 0.0),
-    ("ids-no-local-route", dict(K=2048, I=2048, E_global=16, E_local=2, expert_offset=14, top_k=4), "rows", "ids",
+    ("ids-no-local-route", dict(K=2048, I=2048, E_global=16, E_local=2, expert_offset=14, top_k=4), 1, "rows", "ids",
      0.0),
 ]
 
 
 @pytest.mark.parametrize("case", range(len(TOKEN_CASES)))
-def test_single_token_call_bit_identical_to_route_rows(case):
+def test_few_token_call_bit_identical_to_route_rows(case):
     t = torch()
-    name, kw, layout, mode, boost = TOKEN_CASES[case]
+    name, kw, T, layout, mode, boost = TOKEN_CASES[case]
     cfg = _cfg(**kw)
     w = make_weights(cfg)
     layer = DeviceLayer(w, layout=layout)
-    d = desc_for(cfg, 1, weight_layout=layout)
+    d = desc_for(cfg, T, weight_layout=layout)
     k = cfg.top_k
     if mode == "logits":
-        inp = make_inputs(cfg, 1, t_index=case, all_local_boost=boost)
+        inp = make_inputs(cfg, T, t_index=case, all_local_boost=boost)
         route = dict(router_logits=dev_f32(inp.logits))
     else:
-        inp = make_topk_inputs(cfg, 1, seed=40 + case, pad_fraction=0.25)
+        inp = make_topk_inputs(cfg, T, seed=40 + case, pad_fraction=0.25)
         if name == "ids-no-local-route":
             inp.topk_ids[:] = np.array([0, 3, -1, 7], np.int32)   # all outside experts 14..15
         route = dict(topk_ids=dev_i32(inp.topk_ids), topk_weights=dev_f32(inp.topk_weights))
     x = dev_bf16(inp.x)
-    y = t.full((1, cfg.K), float("nan"), dtype=t.bfloat16, device="cuda")
+    y = t.full((T, cfg.K), float("nan"), dtype=t.bfloat16, device="cuda")
     moe.moe_mxfp4_decode(d, x, layer.w13p, layer.w13s, layer.w2p, layer.w2s, y, w13_bias=layer.b13,
                          w2_bias=layer.b2, **route)
-    rows = t.full((k, cfg.K), float("nan"), dtype=t.float32, device="cuda")
+    rows = t.full((T * k, cfg.K), float("nan"), dtype=t.float32, device="cuda")
     moe.moe_mxfp4_decode_routes(d, x, layer.w13p, layer.w13s, layer.w2p, layer.w2s, rows, w13_bias=layer.b13,
                                 w2_bias=layer.b2, **route)
     ws = moe.moe_mxfp4_plan(d, **route)
-    plan = _plan_read(cfg, 1, d, ws)
+    plan = _plan_read(cfg, T, d, ws)
     t.cuda.synchronize()
-    local = sorted(int(r) for r in plan["routes"] if r >= 0)
+    local = set(int(r) for r in plan["routes"] if r >= 0)
     o = rows.cpu().numpy()
-    acc = np.zeros(cfg.K, np.float32)
-    for j in local:
-        acc = (acc + (np.float32(plan["w"][0, j]) * o[j]).astype(np.float32)).astype(np.float32)
+    acc = np.zeros((T, cfg.K), np.float32)
+    for tt in range(T):
+        for j in range(k):
+            if tt * k + j in local:
+                prod = (np.float32(plan["w"][tt, j]) * o[tt * k + j]).astype(np.float32)
+                acc[tt] = (acc[tt] + prod).astype(np.float32)
     want = bf16_bits_np(t.from_numpy(acc).to(t.bfloat16))
-    got = bf16_bits_np(y)[0]
-    assert np.array_equal(got, want), f"{name}: {np.count_nonzero(got != want)} of {cfg.K} outputs differ"
+    got = bf16_bits_np(y)
+    assert np.array_equal(got, want), f"{name}: {np.count_nonzero(got != want)} of {got.size} outputs differ"
     if name == "ids-no-local-route":
         assert not local and not np.any(got)
+    if name.startswith("gpt-oss-4-tokens"):
+        experts = plan["ids"][plan["ids"] >= 0].ravel()
+        assert len(set(experts.tolist())) < experts.size, "some expert should serve several routes"
     ref = oracle.moe_forward_cfg(cfg, w, inp)
     _assert_close(bf16_to_np(y), ref["y"], name)
 
